@@ -1,0 +1,92 @@
+/*
+ * oracle.h -- plain CPU oracle of the packed lightning-indexer step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this library: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no header, helper, table or constant with
+ * the GPU library; the two only agree on the argument layout, which is the
+ * problem statement of the pages (queries, K planes, scale plane, slot/page
+ * table, per-row lengths, packed_queries, local_blocks, topk).
+ *
+ * Sources it follows (the pages, by title and section):
+ *  - "[AMD] MiniMax-M3 indexer CP: packed scoring for EAGLE verify rows"
+ *    (sglang PR 42614), Modifications item 1 and Accuracy Tests: tile row i is
+ *    (draft row i / gqa, head i % gqa); each row masks with its own length and
+ *    gets its own forced init/local blocks; K is addressed through the request
+ *    slot table; a slot past the request table (graph padding) reads no K;
+ *    selection is exact.
+ *  - sglang PR 45451 ("packed decode score kernel"), Modifications: each row
+ *    keeps its own length mask and the block score is the max score.
+ *  - ROCm/ATOM PR 2745 (NVFP4 index cache), Summary and Validation: per key a
+ *    64 B e2m1 payload (two codes a byte, even element in the low nibble) and
+ *    8 B of E4M3 scales, one per 16 elements, unit outer scale; the store uses
+ *    scale = e4m3(amax / 6) and codes rounded half-to-even, saturating at 6.
+ *
+ * All arithmetic is plain loops.  Token scores are accumulated in double; the
+ * block max is rounded once to float, and selection compares those floats.
+ */
+#ifndef SAL_ORACLE_H
+#define SAL_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ORACLE_K_BF16 = 0,     /* K stored as bf16, 256 B per token             */
+  ORACLE_K_FP8_E4M3 = 1, /* K stored as OCP e4m3fn, 128 B per token        */
+  ORACLE_K_NVFP4 = 2     /* 64 B e2m1 payload + 8 B E4M3 scales per token  */
+};
+
+/* Same field order and meaning as the GPU library's parameter block. */
+typedef struct oracle_params {
+  int32_t k_format;
+  int32_t n_req;          /* requests, graph pads included                      */
+  int32_t n_slot_rows;    /* rows of block_table                                 */
+  int32_t packed_queries; /* P: draft rows per request                          */
+  int32_t gqa;            /* H: index heads                                      */
+  int32_t head_dim;       /* D: 128                                              */
+  int32_t block_size;     /* tokens per block and per page: 128                  */
+  int32_t max_blocks;     /* columns of block_table and of block_scores          */
+  int32_t topk;
+  int32_t init_blocks;
+  int32_t local_blocks;
+  int32_t reserved;
+  int64_t n_pages;        /* pages in the K pool                                 */
+  const void*    q;        /* bf16 [n_req*P][H][D]                               */
+  const void*    k;        /* [n_pages*block_size][bytes per token]              */
+  const uint8_t* k_scale;  /* NVFP4: [n_pages*block_size][D/16]; else unused      */
+  const int32_t* req_slot; /* [n_req]                                            */
+  const int32_t* block_table; /* [n_slot_rows][max_blocks]                       */
+  const int32_t* row_len;  /* [n_req*P]                                          */
+  float*   block_scores;   /* [n_req*P][H][max_blocks]                           */
+  int32_t* topk_ids;       /* [n_req*P][H][topk]                                 */
+  float*   topk_scores;    /* [n_req*P][H][topk]                                 */
+} oracle_params;
+
+/* Block max of every (row, head, block); -inf past the row's own block count,
+ * NaN for a visible block whose page id is outside [0, n_pages). */
+int oracle_score_packed(const oracle_params* p);
+/* Forced top-k over block_scores; ids ascending, padded with -1 / -inf. */
+int oracle_block_topk(const oracle_params* p);
+/* oracle_score_packed followed by oracle_block_topk. */
+int oracle_step(const oracle_params* p);
+
+/* NVFP4 store: quantize bf16 staging rows into payload/scale planes at
+ * slot_mapping[t]; a negative slot or one >= n_slots is skipped. */
+int oracle_fp4_store(const void* staging_bf16, int64_t n_tokens,
+                     int64_t staging_row_stride, const int64_t* slot_mapping,
+                     uint8_t* payload, uint8_t* scales, int64_t n_slots);
+
+/* The oracle's own format steps, exported so the tests can pin them. */
+double  oracle_fp8_value(uint8_t code);          /* OCP e4m3fn -> value          */
+double  oracle_e2m1_value(uint8_t code);         /* 4-bit e2m1 code -> value     */
+uint8_t oracle_e4m3_encode(float t);             /* t >= 0: RNE, satfinite 448    */
+uint8_t oracle_e2m1_encode(float x, float s);    /* code of x / s, sign kept      */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,235 @@
+"""Benchmark of the packed indexer step (score + block top-k) on one MI355X.
+
+One step is one call of the hot path over one batch: the NVFP4 store (only
+for the NVFP4 workload), the packed block scoring and the forced top-k, for
+every request of one layer.  By default the workload is 32 requests x 4 draft
+rows x 4 index heads, fp8 e4m3 keys, contexts U[491520, 524285], 3 graph-pad
+requests (about 2.08 GB of K per step, eight times the 256 MB Infinity Cache,
+so back-to-back steps stream K from HBM).
+
+Prints one JSON line: the metric (us per index step), the dominant kernel's
+roofline against the 8 TB/s HBM peak (algorithmic bytes over its mean duration,
+from HIP events on its launch stream inside the timed region), and the CPU
+oracle timed on the host as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "index step µs (score+top-k) and achieved HBM GB/s vs peak, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse() -> argparse.Namespace:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload index 0..4 (default 3)")
+    ap.add_argument("--local-blocks", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=None,
+                    help="requests in the CPU-oracle sample (default: all real requests)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "sparse_attention_lightning_amd" / "csrc").glob("*")):
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    f = ROOT / "profiles" / f"{kernel}_{workload}_traffic.md"
+    if not f.exists():
+        return None
+    text = f.read_text()
+    m_src = re.search(r"source digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != digest:
+        return None
+    return float(m_b.group(1))
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU: the indexer step has no multi-GPU path in this build "
+              "(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_attention_lightning_amd import idx as I
+    from sparse_attention_lightning_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    w = W.config(args.config, device=dev, local_blocks=args.local_blocks)
+    rows, K, MB = w.rows, w.topk, w.max_blocks
+    outs = {"block_scores": torch.empty((rows, MB), dtype=torch.float32, device=dev),
+            "topk_ids": torch.empty((rows, K), dtype=torch.int32, device=dev),
+            "topk_scores": torch.empty((rows, K), dtype=torch.float32, device=dev)}
+    fp4 = w.k_format == W.K_NVFP4
+    if fp4:
+        I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale)
+    p = I.make_params(k_format=w.k_format, q=w.q, k=w.k, k_scale=w.k_scale, req_slot=w.req_slot,
+                      block_table=w.block_table, row_len=w.row_len, packed_queries=w.packed_queries,
+                      gqa=w.gqa, topk=K, init_blocks=w.init_blocks, local_blocks=w.local_blocks,
+                      max_blocks=MB, n_slot_rows=w.n_slot_rows, n_pages=w.n_pages, **outs)
+
+    # algorithmic bytes (token-exact K of each real request's longest row)
+    P, H = w.packed_queries, w.gqa
+    tokens = w.k_tokens()
+    k_bytes = tokens * W.BYTES_PER_TOKEN[w.k_format]
+    real_rows = w.n_real * P * H
+    nbg = w.pool_pages_used()
+    score_bytes = k_bytes + real_rows * 256 + nbg * 4 + (w.n_req * P + w.n_req) * 4
+    out_bytes = rows * K * 8
+    step_bytes = score_bytes + out_bytes
+    store_bytes = tokens * (256 + 72 + 8) if fp4 else 0   # staging in, payload+scales out, slot
+
+    # cold L2/MALL between steps only for workloads the 256 MB cache could hold
+    flush = None
+    if k_bytes < (1 << 30):
+        flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev=None):
+        if fp4:
+            if ev is not None:
+                ev[0].record(stream)
+            I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        I.idx_score_packed(p, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        I.idx_block_topk(p, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.fill_(1)
+        one_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(s)
+        one_step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    store_ms = [e[0].elapsed_time(e[1]) for e in evs] if fp4 else [0.0] * args.steps
+    score_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    topk_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [a + b + c for a, b, c in zip(store_ms, score_ms, topk_ms)]
+    ms_per_step = wall * 1e3 / args.steps if flush is None else float(np.mean(step_ms))
+    score_mean_s = float(np.mean(score_ms)) / 1e3
+    achieved = score_bytes / score_mean_s / 1e9
+    digest = source_digest()
+    traffic = traffic_from_profiles("score_kernel_fp8", W.CONFIG_NAMES[args.config], digest)
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {W.K_BF16: "bf16", W.K_FP8_E4M3: "fp8_e4m3->bf16", W.K_NVFP4: "nvfp4->f16"}[w.k_format],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "requests": w.n_real, "graph_pads": w.n_req - w.n_real,
+            "packed_queries": P, "gqa": H, "head_dim": 128, "block": 128,
+            "k_format": W.FORMAT_NAMES[w.k_format], "q": "bf16",
+            "context_tokens": [int(w.req_len.min()), int(w.req_len.max() + P - 1)],
+            "topk": K, "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
+            "k_bytes_per_step": k_bytes, "parallelism": "single GPU",
+            "cache": "flushed between steps" if flush is not None else "K is 8x the 256 MB MALL",
+        },
+        "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "kernels_us": {"score": round(score_mean_s * 1e6, 2),
+                       "topk": round(float(np.mean(topk_ms)) * 1e3, 2),
+                       **({"fp4_store": round(float(np.mean(store_ms)) * 1e3, 2)} if fp4 else {})},
+        "roofline": {
+            "kernel": "score_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": score_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if fp4:
+        line["store_GBps"] = round(store_bytes / (float(np.mean(store_ms)) / 1e3) / 1e9, 1)
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(w, n_sample) -> dict:
+    """The oracle, untuned, on the host cores: the step over the first
+    ``n_sample`` real requests (default all), scaled to one full step."""
+    import numpy as np
+
+    from oracle.binding import Oracle
+    from sparse_attention_lightning_amd import workloads as W
+
+    o = Oracle()
+    P, H = w.packed_queries, w.gqa
+    n = w.n_real if n_sample is None else min(n_sample, w.n_real)
+    sel = np.arange(n)
+    if w.k_format == W.K_NVFP4:
+        a = w.oracle_args(w.k.cpu().numpy(), w.k_scale.cpu().numpy())
+    else:
+        a = w.oracle_args()
+    q = a["q"].reshape(a["n_req"], P * H, 128)[sel].reshape(-1, H, 128)
+    sub = dict(a, n_req=n, q=np.ascontiguousarray(q), req_slot=np.ascontiguousarray(a["req_slot"][sel]),
+               row_len=np.ascontiguousarray(a["row_len"].reshape(a["n_req"], P)[sel].reshape(-1)))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        o.step(**sub)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    lmax = w.group_len()[: w.n_real].astype(np.int64)
+    frac = lmax[:n].sum() / lmax.sum()
+    return {"value": round(t / frac * 1e6, 1), "unit": "us", "cores": o.threads(), "kind": "oracle",
+            "sample": f"score+top-k of the first {n} of {w.n_real} requests "
+                      f"({int(lmax[:n].sum())} request-tokens), median of 3, scaled by token count"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,162 @@
+/*
+ * idx.h -- C-ABI of the MI355X (gfx950) packed lightning-indexer step.
+ *
+ * The step scores, for every request, its packed query rows (draft row x
+ * index head) against the request's paged index-K cache, reduces each
+ * 128-token block to its max score under each row's own length, and selects
+ * the top-k blocks per (row, head) with the init and local-window blocks
+ * always selected.  Sources (by page title and section):
+ *
+ *  [P1] sglang PR 45451, "packed decode score kernel", Modifications: a
+ *       request's rows share one 16-row dot tile so each K tile loads once;
+ *       each row keeps its own length mask; the packed form applies when
+ *       packed_queries x gqa <= 16.
+ *  [P2] sglang PR 42614, "[AMD] MiniMax-M3 indexer CP: packed scoring for
+ *       EAGLE verify rows", Modifications item 1: tile row i is (draft row
+ *       i / gqa, head i % gqa); K is read up to the group's longest row while
+ *       masks and forced init/local blocks use each row's own length; a slot
+ *       past the request table (graph padding) reads no K.  Accuracy Tests:
+ *       selection is exact; K is addressed through a permuted, gapped slot
+ *       table.
+ *  [P3] ROCm/ATOM PR 2745, "NVFP4 index cache", Summary: per key (D = 128)
+ *       a 64 B e2m1 payload, two codes a byte with the even element in the
+ *       low nibble, and 8 B of E4M3 scales, one per 16 elements, unit outer
+ *       scale; the store quantizes with scale = e4m3(amax / 6) and codes
+ *       rounded half-to-even, saturating at 6.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no memory and keeps no state between calls, except a
+ *    thread-local copy of the last error message.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  A call checks its
+ *    arguments on the host, enqueues its kernels on `stream` and returns
+ *    without synchronising.  0 = enqueued; a negative IDX_E_* code = refused,
+ *    nothing enqueued (IDX_E_LAUNCH: the runtime rejected a launch).
+ *  - Sizes that live in device memory (row lengths, page ids, slots) cannot be
+ *    checked on the host; the kernels clamp or reject them as stated below and
+ *    never access memory outside the extents passed in.
+ *  - Calls on one stream run in order; the library adds no synchronisation
+ *    between streams.
+ */
+#ifndef SAL_IDX_H
+#define SAL_IDX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  IDX_OK = 0,
+  IDX_E_NULL = -1,   /* a required pointer is NULL                                  */
+  IDX_E_FORMAT = -2, /* unknown k_format                                            */
+  IDX_E_SHAPE = -3,  /* head_dim / block_size != 128, or a count out of range        */
+  IDX_E_PACK = -4,   /* packed_queries * gqa > 16: the rows do not fit one tile [P1] */
+  IDX_E_TOPK = -5,   /* topk < 1, init/local < 0, or topk < init_blocks + local_blocks */
+  IDX_E_LAUNCH = -6, /* the HIP runtime rejected a kernel launch                      */
+  IDX_E_ALIGN = -7   /* q, k, k_scale or staging not 16-byte aligned                  */
+};
+
+enum {
+  IDX_K_BF16 = 0,     /* K row: 128 bf16 (256 B)                                        */
+  IDX_K_FP8_E4M3 = 1, /* K row: 128 OCP e4m3fn bytes (128 B), unit scale               */
+  IDX_K_NVFP4 = 2     /* K row: 64 B e2m1 payload; scale row: 8 E4M3 bytes [P3]         */
+};
+
+/* Largest max_blocks: 1,048,576-token contexts, the context length the
+ * pages serve with (sglang PR 45451, Reproduce: --context-length). */
+#define IDX_MAX_BLOCKS 8192
+
+/*
+ * Parameters of one indexer step (one layer, all requests of the batch).
+ *
+ * Shapes, with P = packed_queries, H = gqa, R = n_req (graph pads included),
+ * MB = max_blocks, D = head_dim = 128, B = block_size = 128:
+ *   q            bf16  [R*P][H][D]   row-major; tile row i of request r is
+ *                                    q[(r*P + i/H)*H + i%H], i.e. the R*P*H
+ *                                    rows in order [P2].
+ *   k            bf16 or fp8: [n_pages*B][D] elements; NVFP4: [n_pages*B][64]
+ *                bytes.  Token t of page p is row p*B + t.  Page = block.
+ *   k_scale      NVFP4 only: uint8 [n_pages*B][D/16] E4M3 scales; else ignored.
+ *   req_slot     int32 [R]: the request's row in block_table.  A slot < 0 or
+ *                >= n_slot_rows marks a graph pad: no K is read and its
+ *                outputs are sentinels [P2].
+ *   block_table  int32 [n_slot_rows][MB]: page id of each 128-token block.
+ *                A page id outside [0, n_pages) is not read; every row that
+ *                sees that block gets a NaN block score.
+ *   row_len      int32 [R*P]: tokens visible to each draft row.  Negative
+ *                values count as 0, values above MB*B as MB*B.
+ *   block_scores fp32 [R*P][H][MB]: for block b of a row with nb =
+ *                ceil(row_len/B) blocks, the max over that block's visible
+ *                tokens of the raw dot q.k (fp32 accumulation); -inf for
+ *                b >= nb and for graph pads.
+ *   topk_ids     int32 [R*P][H][topk]: selected block ids, ascending, padded
+ *                with -1.  If nb <= topk every block is selected; otherwise
+ *                blocks [0, init_blocks) and [nb - local_blocks, nb) are
+ *                always selected and the rest go by score, higher first, ties
+ *                to the lower id, NaN below every number.
+ *   topk_scores  fp32 [R*P][H][topk]: block_scores of each selected id, -inf
+ *                padding.
+ */
+typedef struct idx_params {
+  int32_t k_format;       /* IDX_K_*                                        */
+  int32_t n_req;          /* requests in the launch, graph pads included     */
+  int32_t n_slot_rows;    /* rows of block_table (the request table)         */
+  int32_t packed_queries; /* draft rows per request, >= 1                    */
+  int32_t gqa;            /* index heads, >= 1; packed_queries*gqa <= 16     */
+  int32_t head_dim;       /* must be 128                                     */
+  int32_t block_size;     /* must be 128                                     */
+  int32_t max_blocks;     /* columns of block_table / block_scores, 0..IDX_MAX_BLOCKS */
+  int32_t topk;           /* >= 1                                            */
+  int32_t init_blocks;    /* forced leading blocks, >= 0                     */
+  int32_t local_blocks;   /* forced trailing blocks, >= 0                    */
+  int32_t reserved;       /* must be 0                                       */
+  int64_t n_pages;        /* pages in the K pool, >= 0                       */
+  const void* q;
+  const void* k;
+  const uint8_t* k_scale;
+  const int32_t* req_slot;
+  const int32_t* block_table;
+  const int32_t* row_len;
+  float* block_scores;
+  int32_t* topk_ids;
+  float* topk_scores;
+} idx_params;
+
+/*
+ * NVFP4 store [P3]: quantize bf16 staging keys into the paged payload and
+ * scale planes.  For token t < n_tokens, row t of `staging_bf16` (128 bf16,
+ * rows `staging_row_stride` elements apart, stride >= 128) goes to slot
+ * s = slot_mapping[t] (slot = page*128 + offset): payload[s][0..63] and
+ * scales[s][0..7].  Per 16-element group: scale byte = E4M3 nearest to
+ * amax/6 (fp32 quotient, ties to even, clamped at 448); code = e2m1 nearest
+ * to x/scale, ties to the even code, saturating at 6, with x's sign bit
+ * (scale 0 gives magnitude 0).  A slot < 0 or >= n_slots is skipped; other
+ * slots are left untouched.  NaN/Inf inputs give unspecified bytes.
+ * Pointers: staging_bf16 and payload 16-byte aligned.
+ */
+int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_row_stride,
+                  const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,
+                  int64_t n_slots, void* stream);
+
+/* Block scores of every (row, head, block) [P1, P2]: reads q, k, k_scale,
+ * req_slot, block_table, row_len; writes block_scores (all R*P*H*MB entries).
+ * topk_ids / topk_scores may be NULL. */
+int idx_score_packed(const idx_params* p, void* stream);
+
+/* Forced top-k [P2] over an existing block_scores: reads req_slot, row_len,
+ * block_scores; writes topk_ids and topk_scores.  q, k, k_scale and
+ * block_table may be NULL. */
+int idx_block_topk(const idx_params* p, void* stream);
+
+/* idx_score_packed then idx_block_topk on the same stream. */
+int idx_step(const idx_params* p, void* stream);
+
+/* Message describing the last refusal on the calling thread ("" if none). */
+const char* idx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -50,6 +50,8 @@ def load(path: Path | str | None = None) -> C.CDLL:
     lib.oracle_fp4_store.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_int64]
     lib.oracle_fp4_store.restype = C.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = C.c_int
     lib.oracle_fp8_value.argtypes = [C.c_uint8]
     lib.oracle_fp8_value.restype = C.c_double
     lib.oracle_e2m1_value.argtypes = [C.c_uint8]
@@ -81,6 +83,9 @@ class Oracle:
 
     def __init__(self, path: Path | str | None = None):
         self.lib = load(path)
+
+    def threads(self) -> int:
+        return self.lib.oracle_threads()
 
     # -- number formats --------------------------------------------------
     def fp8_value(self, code: int) -> float:

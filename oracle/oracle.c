@@ -15,6 +15,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
@@ -390,4 +393,12 @@ int oracle_block_topk(const oracle_params* p) {
 int oracle_step(const oracle_params* p) {
   int rc = oracle_score_packed(p);
   return rc ? rc : oracle_block_topk(p);
+}
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

@@ -80,6 +80,9 @@ int oracle_fp4_store(const void* staging_bf16, int64_t n_tokens,
                      int64_t staging_row_stride, const int64_t* slot_mapping,
                      uint8_t* payload, uint8_t* scales, int64_t n_slots);
 
+/* OpenMP threads the oracle's parallel loops use. */
+int oracle_threads(void);
+
 /* The oracle's own format steps, exported so the tests can pin them. */
 double  oracle_fp8_value(uint8_t code);          /* OCP e4m3fn -> value          */
 double  oracle_e2m1_value(uint8_t code);         /* 4-bit e2m1 code -> value     */

@@ -1,0 +1,151 @@
+// api.hip -- the C-ABI entry points declared in include/idx.h.
+//
+// Every entry point checks its arguments on the host before touching the HIP
+// runtime, so a refused call enqueues nothing and needs no device.
+#include <cstdarg>
+#include <cstdio>
+
+#include "device.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum Need { kScore = 1, kTopk = 2 };
+
+int check(const idx_params* p, int need) {
+  if (!p) return fail(IDX_E_NULL, "params is NULL");
+  if (p->k_format < IDX_K_BF16 || p->k_format > IDX_K_NVFP4)
+    return fail(IDX_E_FORMAT, "unknown k_format %d", p->k_format);
+  if (p->head_dim != 128 || p->block_size != 128)
+    return fail(IDX_E_SHAPE, "head_dim and block_size must be 128 (got %d, %d)", p->head_dim,
+                p->block_size);
+  if (p->packed_queries < 1 || p->gqa < 1)
+    return fail(IDX_E_SHAPE, "packed_queries and gqa must be >= 1 (got %d, %d)",
+                p->packed_queries, p->gqa);
+  if ((int64_t)p->packed_queries * p->gqa > 16)
+    return fail(IDX_E_PACK, "packed_queries * gqa = %lld exceeds the 16-row tile",
+                (long long)p->packed_queries * p->gqa);
+  if (p->n_req < 0 || p->n_slot_rows < 0 || p->n_pages < 0)
+    return fail(IDX_E_SHAPE, "negative count (n_req %d, n_slot_rows %d, n_pages %lld)",
+                p->n_req, p->n_slot_rows, (long long)p->n_pages);
+  if (p->max_blocks < 0 || p->max_blocks > IDX_MAX_BLOCKS)
+    return fail(IDX_E_SHAPE, "max_blocks %d outside [0, %d]", p->max_blocks, IDX_MAX_BLOCKS);
+  if (p->reserved != 0) return fail(IDX_E_SHAPE, "reserved field must be 0");
+  if (p->n_pages > (int64_t)1 << 40) return fail(IDX_E_SHAPE, "n_pages %lld too large", (long long)p->n_pages);
+  if (p->topk < 1 || p->init_blocks < 0 || p->local_blocks < 0 ||
+      (int64_t)p->topk < (int64_t)p->init_blocks + p->local_blocks)
+    return fail(IDX_E_TOPK, "need topk >= 1, init/local >= 0, topk >= init + local (got %d, %d, %d)",
+                p->topk, p->init_blocks, p->local_blocks);
+  if (!p->req_slot || !p->row_len) return fail(IDX_E_NULL, "req_slot and row_len are required");
+  if (!p->block_scores) return fail(IDX_E_NULL, "block_scores is required");
+  if (need & kScore) {
+    if (!p->q || !p->k || !p->block_table)
+      return fail(IDX_E_NULL, "q, k and block_table are required for scoring");
+    if (p->k_format == IDX_K_NVFP4 && !p->k_scale)
+      return fail(IDX_E_NULL, "k_scale is required for NVFP4 keys");
+    if (!aligned16(p->q) || !aligned16(p->k))
+      return fail(IDX_E_ALIGN, "q and k must be 16-byte aligned");
+    if (p->k_format == IDX_K_NVFP4 && (reinterpret_cast<uintptr_t>(p->k_scale) & 1u))
+      return fail(IDX_E_ALIGN, "k_scale must be 2-byte aligned");
+  }
+  if (need & kTopk) {
+    if (!p->topk_ids || !p->topk_scores)
+      return fail(IDX_E_NULL, "topk_ids and topk_scores are required for selection");
+  }
+  return IDX_OK;
+}
+
+idx::StepArgs args_of(const idx_params* p) {
+  idx::StepArgs a{};
+  a.q = p->q;
+  a.k = p->k;
+  a.k_scale = p->k_scale;
+  a.req_slot = p->req_slot;
+  a.block_table = p->block_table;
+  a.row_len = p->row_len;
+  a.block_scores = p->block_scores;
+  a.topk_ids = p->topk_ids;
+  a.topk_scores = p->topk_scores;
+  a.n_pages = p->n_pages;
+  a.k_format = p->k_format;
+  a.n_req = p->n_req;
+  a.n_slot_rows = p->n_slot_rows;
+  a.P = p->packed_queries;
+  a.H = p->gqa;
+  a.max_blocks = p->max_blocks;
+  a.topk = p->topk;
+  a.init_blocks = p->init_blocks;
+  a.local_blocks = p->local_blocks;
+  return a;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(IDX_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* idx_last_error(void) { return g_err; }
+
+int idx_score_packed(const idx_params* p, void* stream) {
+  const int rc = check(p, kScore);
+  if (rc) return rc;
+  return launched(idx::launch_score(args_of(p), (hipStream_t)stream), "score");
+}
+
+int idx_block_topk(const idx_params* p, void* stream) {
+  const int rc = check(p, kTopk);
+  if (rc) return rc;
+  return launched(idx::launch_topk(args_of(p), (hipStream_t)stream), "top-k");
+}
+
+int idx_step(const idx_params* p, void* stream) {
+  const int rc = check(p, kScore | kTopk);
+  if (rc) return rc;
+  const idx::StepArgs a = args_of(p);
+  const int r1 = launched(idx::launch_score(a, (hipStream_t)stream), "score");
+  if (r1) return r1;
+  return launched(idx::launch_topk(a, (hipStream_t)stream), "top-k");
+}
+
+int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_row_stride,
+                  const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales, int64_t n_slots,
+                  void* stream) {
+  if (n_tokens < 0 || n_slots < 0)
+    return fail(IDX_E_SHAPE, "negative count (n_tokens %lld, n_slots %lld)", (long long)n_tokens,
+                (long long)n_slots);
+  if (staging_row_stride < 128 || (staging_row_stride & 7))
+    return fail(IDX_E_SHAPE, "staging_row_stride %lld must be >= 128 and a multiple of 8",
+                (long long)staging_row_stride);
+  if (n_tokens > ((int64_t)1 << 40) || n_slots > ((int64_t)1 << 40))
+    return fail(IDX_E_SHAPE, "n_tokens / n_slots too large");
+  if (n_tokens == 0) {
+    g_err[0] = '\0';
+    return IDX_OK;
+  }
+  if (!staging_bf16 || !slot_mapping || !payload || !scales)
+    return fail(IDX_E_NULL, "staging, slot_mapping, payload and scales are required");
+  if (!aligned16(staging_bf16) || !aligned16(payload))
+    return fail(IDX_E_ALIGN, "staging and payload must be 16-byte aligned");
+  return launched(idx::launch_fp4_store(static_cast<const uint16_t*>(staging_bf16), n_tokens,
+                                        staging_row_stride, slot_mapping, payload, scales, n_slots,
+                                        (hipStream_t)stream),
+                  "fp4 store");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// device.h -- internal types and helpers of the gfx950 indexer kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "idx.h"
+
+namespace idx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 128;   // tokens per block = tokens per page
+constexpr int kTileRows = 16; // rows of the packed query tile
+
+// Everything the kernels need, by value (one parameter block per launch).
+struct StepArgs {
+  const void* q;
+  const void* k;
+  const uint8_t* k_scale;
+  const int32_t* req_slot;
+  const int32_t* block_table;
+  const int32_t* row_len;
+  float* block_scores;
+  int32_t* topk_ids;
+  float* topk_scores;
+  int64_t n_pages;
+  int32_t k_format;
+  int32_t n_req, n_slot_rows, P, H, max_blocks, topk, init_blocks, local_blocks;
+  int32_t n_chunks;  // score kernel: workgroups per request
+};
+
+hipError_t launch_score(const StepArgs& a, hipStream_t stream);
+hipError_t launch_topk(const StepArgs& a, hipStream_t stream);
+hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t stride,
+                            const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,
+                            int64_t n_slots, hipStream_t stream);
+
+__device__ __forceinline__ int clamp_len(int32_t len, int max_blocks) {
+  const int cap = max_blocks * kBlock;
+  return len < 0 ? 0 : (len > cap ? cap : len);
+}
+
+__device__ __forceinline__ int blocks_of(int len) { return (len + kBlock - 1) / kBlock; }
+
+// Lane permutation within DPP rows (16 lanes); CTRL is the DPP control word.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_mov<0x128>(x));  // row_ror:8
+  return x;
+}
+
+}  // namespace idx

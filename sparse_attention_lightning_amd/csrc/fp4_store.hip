@@ -1,0 +1,91 @@
+// fp4_store.hip -- NVFP4 index-key store for gfx950.
+//
+// ROCm/ATOM PR 2745, Summary ("Store" and the per-key layout): per 16-element
+// group, scale = e4m3(amax / 6) and codes rounded half-to-even, saturating at
+// 6; two codes a byte, the even element in the low nibble; 64 B payload and
+// 8 B scales per key, written at the key's slot.
+//
+// Eight threads per key, one per 16-element group.  amax / 6 is an IEEE fp32
+// division; its E4M3 rounding (nearest, ties to even, clamped at 448) is done
+// on the bits.  Codes come from exact comparisons of |x| with the e2m1
+// midpoints times the scale (each product is exact in fp32), which is the
+// half-to-even rounding of x / scale without a division.  A code keeps the
+// sign bit of x; a zero scale gives magnitude 0.
+#include "device.h"
+
+namespace idx {
+
+constexpr int kStoreThreads = 256;
+
+__device__ __forceinline__ uint32_t e4m3_rne_satfinite(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;  // clamp (NaN too: unspecified)
+  if (t < 0x1p-6f) return (uint32_t)__builtin_rintf(t * 512.0f);  // subnormal step 2^-9
+  uint32_t u = __float_as_uint(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round to 3 mantissa bits, ties to even
+  const uint32_t e = (u >> 23) - 127u + 7u;
+  return (e << 3) | ((u >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = b >> 3, m = b & 7u;
+  return (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+__global__ __launch_bounds__(kStoreThreads) void fp4_store_kernel(
+    const uint16_t* __restrict__ staging, int64_t n_tokens, int64_t stride,
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ payload,
+    uint8_t* __restrict__ scales, int64_t n_slots) {
+  const int64_t n_items = n_tokens * 8;
+  for (int64_t item = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x; item < n_items;
+       item += (int64_t)gridDim.x * kStoreThreads) {
+    const int64_t t = item >> 3;
+    const int grp = (int)(item & 7);
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= n_slots) continue;
+    const uint4* src = reinterpret_cast<const uint4*>(staging + t * stride + 16 * grp);
+    const uint4 w0 = src[0], w1 = src[1];
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float x[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[2 * j] = __uint_as_float(wd[j] << 16);
+      x[2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
+    }
+    const uint32_t sb = e4m3_rne_satfinite(amax / 6.0f);
+    const float s = e4m3_value(sb);
+    // midpoints of the e2m1 grid 0 .5 1 1.5 2 3 4 6, times s (exact)
+    const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
+    const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float a = fabsf(x[j]);
+      // ties: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+      const uint32_t b2 = a >= m3;
+      const uint32_t b1 = a >= (b2 ? m5 : m1);
+      const float t3 = b2 ? (b1 ? m6 : m4) : (b1 ? m2 : m0);
+      const uint32_t b0 = a > t3;
+      uint32_t mag = (b2 << 2) | (b1 << 1) | b0;
+      mag = (s > 0.0f) ? mag : 0u;
+      const uint32_t code = mag | ((__float_as_uint(x[j]) >> 28) & 8u);
+      packed[j >> 3] |= code << (4 * (j & 7));
+    }
+    *reinterpret_cast<uint2*>(payload + slot * 64 + 8 * grp) = make_uint2(packed[0], packed[1]);
+    scales[slot * 8 + grp] = (uint8_t)sb;
+  }
+}
+
+hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t stride,
+                            const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,
+                            int64_t n_slots, hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  const int64_t want = (n_tokens * 8 + kStoreThreads - 1) / kStoreThreads;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(fp4_store_kernel, dim3(grid), dim3(kStoreThreads), 0, stream, staging,
+                     n_tokens, stride, slot_mapping, payload, scales, n_slots);
+  return hipGetLastError();
+}
+
+}  // namespace idx

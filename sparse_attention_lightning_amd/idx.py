@@ -1,0 +1,204 @@
+"""Python binding of the C-ABI in ``include/idx.h`` (argument marshalling only).
+
+The functions carry the C names.  They take torch tensors that already live on
+the GPU, check dtype, device and layout (refusing, for example, int64 slot
+tables or non-contiguous planes), pass raw device pointers and the current HIP
+stream to ``libidx.so``, and raise :class:`IdxError` with the library's message
+when it refuses a call.  Every step of the computation runs in the library's
+HIP kernels; if the library is missing this module raises instead of falling
+back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libidx.so"
+
+IDX_OK, IDX_E_NULL, IDX_E_FORMAT, IDX_E_SHAPE, IDX_E_PACK = 0, -1, -2, -3, -4
+IDX_E_TOPK, IDX_E_LAUNCH, IDX_E_ALIGN = -5, -6, -7
+IDX_K_BF16, IDX_K_FP8_E4M3, IDX_K_NVFP4 = 0, 1, 2
+IDX_MAX_BLOCKS = 8192
+EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error")
+
+
+class IdxError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class IdxParams(C.Structure):
+    """Mirror of ``idx_params``."""
+    _fields_ = [
+        ("k_format", C.c_int32), ("n_req", C.c_int32), ("n_slot_rows", C.c_int32),
+        ("packed_queries", C.c_int32), ("gqa", C.c_int32), ("head_dim", C.c_int32),
+        ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
+        ("init_blocks", C.c_int32), ("local_blocks", C.c_int32), ("reserved", C.c_int32),
+        ("n_pages", C.c_int64),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("k_scale", C.c_void_p),
+        ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
+        ("block_scores", C.c_void_p), ("topk_ids", C.c_void_p), ("topk_scores", C.c_void_p),
+    ]
+
+
+_lib: C.CDLL | None = None
+
+
+def load(path: Path | str | None = None) -> C.CDLL:
+    """Load ``libidx.so``; raise if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"HIP library {p} is missing: build it with __graft_entry__.build()")
+    lib = C.CDLL(str(p))
+    for name in ("idx_score_packed", "idx_block_topk", "idx_step"):
+        fn = getattr(lib, name)
+        fn.argtypes = [C.POINTER(IdxParams), C.c_void_p]
+        fn.restype = C.c_int
+    lib.idx_fp4_store.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_int64, C.c_void_p]
+    lib.idx_fp4_store.restype = C.c_int
+    lib.idx_last_error.argtypes = []
+    lib.idx_last_error.restype = C.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(rc: int, lib: C.CDLL) -> None:
+    if rc != IDX_OK:
+        raise IdxError(rc, lib.idx_last_error().decode())
+
+
+def _dev(t: torch.Tensor | None, name: str, dtypes, optional: bool = False) -> int | None:
+    if t is None:
+        if optional:
+            return None
+        raise TypeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {[str(d) for d in dtypes]}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_K_DTYPES = {
+    IDX_K_BF16: (torch.bfloat16,),
+    IDX_K_FP8_E4M3: (torch.float8_e4m3fn, torch.uint8),
+    IDX_K_NVFP4: (torch.uint8,),
+}
+_ROW_BYTES = {IDX_K_BF16: 256, IDX_K_FP8_E4M3: 128, IDX_K_NVFP4: 64}
+
+
+def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
+                k_scale: torch.Tensor | None, req_slot: torch.Tensor,
+                block_table: torch.Tensor | None, row_len: torch.Tensor,
+                block_scores: torch.Tensor, topk_ids: torch.Tensor | None,
+                topk_scores: torch.Tensor | None, packed_queries: int, gqa: int, topk: int,
+                init_blocks: int, local_blocks: int, max_blocks: int | None = None,
+                n_slot_rows: int | None = None, n_pages: int | None = None) -> IdxParams:
+    """Build the parameter block from tensors (sizes read from their shapes
+    unless given).  The returned object keeps the tensors alive."""
+    if k_format not in _K_DTYPES:
+        raise ValueError(f"unknown k_format {k_format}")
+    p = IdxParams()
+    p.k_format = k_format
+    p.packed_queries = packed_queries
+    p.gqa = gqa
+    p.head_dim = 128
+    p.block_size = 128
+    p.topk = topk
+    p.init_blocks = init_blocks
+    p.local_blocks = local_blocks
+    p.q = _dev(q, "q", (torch.bfloat16,), optional=True)
+    p.k = _dev(k, "k", _K_DTYPES[k_format], optional=True)
+    p.k_scale = _dev(k_scale, "k_scale", (torch.uint8,), optional=True)
+    p.req_slot = _dev(req_slot, "req_slot", (torch.int32,))
+    p.block_table = _dev(block_table, "block_table", (torch.int32,), optional=True)
+    p.row_len = _dev(row_len, "row_len", (torch.int32,))
+    p.block_scores = _dev(block_scores, "block_scores", (torch.float32,))
+    p.topk_ids = _dev(topk_ids, "topk_ids", (torch.int32,), optional=True)
+    p.topk_scores = _dev(topk_scores, "topk_scores", (torch.float32,), optional=True)
+    p.n_req = req_slot.numel()
+    if max_blocks is None:
+        max_blocks = block_table.shape[-1] if block_table is not None else (
+            block_scores.numel() // max(1, p.n_req * packed_queries * gqa))
+    p.max_blocks = max_blocks
+    if n_slot_rows is None:
+        n_slot_rows = block_table.shape[0] if block_table is not None else 0
+    p.n_slot_rows = n_slot_rows
+    if n_pages is None:
+        n_pages = (k.numel() * k.element_size()) // (128 * _ROW_BYTES[k_format]) if k is not None else 0
+    p.n_pages = n_pages
+    rows = p.n_req * packed_queries * gqa
+    if row_len.numel() != p.n_req * packed_queries:
+        raise ValueError("row_len must have n_req * packed_queries entries")
+    if block_scores.numel() < rows * max_blocks:
+        raise ValueError("block_scores is smaller than n_req * P * H * max_blocks")
+    if q is not None and q.numel() < rows * 128:
+        raise ValueError("q is smaller than n_req * P * H * 128")
+    if block_table is not None and block_table.numel() < n_slot_rows * max_blocks:
+        raise ValueError("block_table is smaller than n_slot_rows * max_blocks")
+    if k is not None and k.numel() * k.element_size() < n_pages * 128 * _ROW_BYTES[k_format]:
+        raise ValueError("k is smaller than n_pages pages")
+    if k_format == IDX_K_NVFP4 and k_scale is not None and k_scale.numel() < n_pages * 128 * 8:
+        raise ValueError("k_scale is smaller than n_pages pages")
+    for t, n in ((topk_ids, "topk_ids"), (topk_scores, "topk_scores")):
+        if t is not None and t.numel() < rows * topk:
+            raise ValueError(f"{n} is smaller than n_req * P * H * topk")
+    p._keep = (q, k, k_scale, req_slot, block_table, row_len, block_scores, topk_ids, topk_scores)
+    return p
+
+
+def idx_score_packed(p: IdxParams, stream=None) -> None:
+    lib = load()
+    _check(lib.idx_score_packed(C.byref(p), _stream(stream)), lib)
+
+
+def idx_block_topk(p: IdxParams, stream=None) -> None:
+    lib = load()
+    _check(lib.idx_block_topk(C.byref(p), _stream(stream)), lib)
+
+
+def idx_step(p: IdxParams, stream=None) -> None:
+    lib = load()
+    _check(lib.idx_step(C.byref(p), _stream(stream)), lib)
+
+
+def idx_fp4_store(staging: torch.Tensor, slot_mapping: torch.Tensor, payload: torch.Tensor,
+                  scales: torch.Tensor, stream=None) -> None:
+    """Quantize ``staging`` (bf16 [n_tokens, >=128], row stride from the
+    tensor) into ``payload`` (uint8 [n_slots, 64]) and ``scales`` (uint8
+    [n_slots, 8]) at ``slot_mapping`` (int64 [n_tokens])."""
+    lib = load()
+    if staging.dim() != 2 or staging.shape[1] < 128 or staging.stride(1) != 1:
+        raise ValueError("staging must be [n_tokens, >=128] with unit element stride")
+    if staging.device.type != "cuda" or staging.dtype != torch.bfloat16:
+        raise TypeError("staging must be a bf16 GPU tensor")
+    _dev(slot_mapping, "slot_mapping", (torch.int64,))
+    _dev(payload, "payload", (torch.uint8,))
+    _dev(scales, "scales", (torch.uint8,))
+    n_slots = payload.shape[0]
+    if payload.shape != (n_slots, 64) or scales.shape != (n_slots, 8):
+        raise ValueError("payload must be [n_slots, 64] and scales [n_slots, 8]")
+    if slot_mapping.numel() != staging.shape[0]:
+        raise ValueError("slot_mapping needs one entry per staging row")
+    rc = lib.idx_fp4_store(staging.data_ptr(), staging.shape[0], staging.stride(0),
+                           slot_mapping.data_ptr(), payload.data_ptr(), scales.data_ptr(),
+                           n_slots, _stream(stream))
+    _check(rc, lib)

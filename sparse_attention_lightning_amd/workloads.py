@@ -119,9 +119,12 @@ class Workload:
 
 def _slot_table(rng: np.random.Generator, R: int, P: int) -> tuple[int, np.ndarray]:
     """Permuted, gapped request slots: no request's slot equals its group index
-    r or any of its row indices r*P + j."""
+    r or any of its row indices r*P + j.  The table has 2R + 5 rows, grown by P
+    until every request has at least R free candidates."""
     n_slot_rows = 2 * R + 5
-    while True:
+    while n_slot_rows - (P + 1) < R:
+        n_slot_rows += P
+    for _ in range(100000):
         slots = rng.permutation(n_slot_rows)[:R]
         bad = False
         for r, s in enumerate(slots):
@@ -130,6 +133,7 @@ def _slot_table(rng: np.random.Generator, R: int, P: int) -> tuple[int, np.ndarr
                 break
         if not bad:
             return n_slot_rows, slots.astype(np.int32)
+    raise RuntimeError("no slot permutation satisfies the constraints")
 
 
 def _randn_into(dst: torch.Tensor, gen: torch.Generator, chunk_rows: int = 1 << 17) -> None:

@@ -1,0 +1,130 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/idx.h declares, and refuses bad arguments with the documented codes
+before touching the HIP runtime."""
+from __future__ import annotations
+
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+from sparse_attention_lightning_amd import idx as I
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not I.LIB_PATH.exists():
+        pytest.fail("libidx.so is not built (run __graft_entry__.build())")
+    return I.load()
+
+
+def declared_functions() -> list[str]:
+    text = (ROOT / "include" / "idx.h").read_text()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(idx_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(I.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def good_params() -> I.IdxParams:
+    """Valid-looking parameters with dummy, never dereferenced pointers."""
+    p = I.IdxParams()
+    p.k_format, p.n_req, p.n_slot_rows = I.IDX_K_FP8_E4M3, 2, 4
+    p.packed_queries, p.gqa, p.head_dim, p.block_size = 4, 4, 128, 128
+    p.max_blocks, p.topk, p.init_blocks, p.local_blocks, p.n_pages = 16, 8, 1, 2, 64
+    for i, f in enumerate(["q", "k", "k_scale", "req_slot", "block_table", "row_len",
+                           "block_scores", "topk_ids", "topk_scores"]):
+        setattr(p, f, 0x100000 * (i + 1))
+    return p
+
+
+REFUSALS = [
+    ("k_format", 3, I.IDX_E_FORMAT),
+    ("k_format", -1, I.IDX_E_FORMAT),
+    ("head_dim", 64, I.IDX_E_SHAPE),
+    ("block_size", 64, I.IDX_E_SHAPE),
+    ("packed_queries", 0, I.IDX_E_SHAPE),
+    ("gqa", 17, I.IDX_E_PACK),
+    ("packed_queries", 5, I.IDX_E_PACK),
+    ("n_req", -1, I.IDX_E_SHAPE),
+    ("n_pages", -2, I.IDX_E_SHAPE),
+    ("max_blocks", I.IDX_MAX_BLOCKS + 1, I.IDX_E_SHAPE),
+    ("max_blocks", -1, I.IDX_E_SHAPE),
+    ("reserved", 1, I.IDX_E_SHAPE),
+    ("topk", 0, I.IDX_E_TOPK),
+    ("topk", 2, I.IDX_E_TOPK),          # < init + local
+    ("local_blocks", -1, I.IDX_E_TOPK),
+    ("init_blocks", -2, I.IDX_E_TOPK),
+    ("q", None, I.IDX_E_NULL),
+    ("k", None, I.IDX_E_NULL),
+    ("req_slot", None, I.IDX_E_NULL),
+    ("row_len", None, I.IDX_E_NULL),
+    ("block_table", None, I.IDX_E_NULL),
+    ("block_scores", None, I.IDX_E_NULL),
+    ("topk_ids", None, I.IDX_E_NULL),
+    ("topk_scores", None, I.IDX_E_NULL),
+    ("q", 0x100008, I.IDX_E_ALIGN),
+    ("k", 0x100004, I.IDX_E_ALIGN),
+]
+
+
+@pytest.mark.parametrize("field,value,code", REFUSALS, ids=[f"{f}={v}" for f, v, _ in REFUSALS])
+def test_step_refusals(lib, field, value, code):
+    p = good_params()
+    setattr(p, field, value)
+    assert lib.idx_step(C.byref(p), None) == code
+    assert lib.idx_last_error().decode() != ""
+
+
+def test_null_params(lib):
+    assert lib.idx_step(None, None) == I.IDX_E_NULL
+    assert lib.idx_score_packed(None, None) == I.IDX_E_NULL
+    assert lib.idx_block_topk(None, None) == I.IDX_E_NULL
+
+
+def test_entry_specific_requirements(lib):
+    p = good_params()
+    p.k_format = I.IDX_K_NVFP4
+    p.k_scale = None
+    assert lib.idx_score_packed(C.byref(p), None) == I.IDX_E_NULL   # scoring needs scales
+    p = good_params()
+    p.topk_ids = None
+    assert lib.idx_block_topk(C.byref(p), None) == I.IDX_E_NULL    # selection needs outputs
+    p = good_params()
+    p.k_format = I.IDX_K_NVFP4
+    p.k_scale = 0x100001
+    assert lib.idx_score_packed(C.byref(p), None) == I.IDX_E_ALIGN
+
+
+FP4_REFUSALS = [
+    dict(stride=100, code=I.IDX_E_SHAPE),
+    dict(stride=130, code=I.IDX_E_SHAPE),
+    dict(n_tokens=-1, code=I.IDX_E_SHAPE),
+    dict(n_slots=-1, code=I.IDX_E_SHAPE),
+    dict(payload=None, code=I.IDX_E_NULL),
+    dict(slot_mapping=None, code=I.IDX_E_NULL),
+    dict(staging=0x200008, code=I.IDX_E_ALIGN),
+]
+
+
+@pytest.mark.parametrize("case", FP4_REFUSALS, ids=lambda c: ",".join(f"{k}" for k in c if k != "code"))
+def test_fp4_store_refusals(lib, case):
+    a = dict(staging=0x200000, n_tokens=10, stride=128, slot_mapping=0x300000, payload=0x400000,
+             scales=0x500000, n_slots=10)
+    a.update({k: v for k, v in case.items() if k != "code"})
+    rc = lib.idx_fp4_store(a["staging"], a["n_tokens"], a["stride"], a["slot_mapping"],
+                           a["payload"], a["scales"], a["n_slots"], None)
+    assert rc == case["code"]
+
+
+def test_fp4_store_empty_is_ok(lib):
+    assert lib.idx_fp4_store(None, 0, 128, None, None, None, 0, None) == I.IDX_OK

@@ -1,0 +1,365 @@
+"""HIP path vs the CPU oracle on an MI355X (through the C-ABI).
+
+Small cases are compared in full; the five workloads run at full size in the
+launch configuration the benchmark times, compared on sampled requests (the
+oracle computes them one by one) and on properties that hold at any size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import harness as Hn
+import pins
+from sparse_attention_lightning_amd import idx as I
+from sparse_attention_lightning_amd import workloads as W
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not Hn.gpu_ok(), reason="needs an MI355X (gfx950)")]
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# small shapes, full comparison
+# ---------------------------------------------------------------------------
+SHAPES = [  # (P, H, lens of the requests, topk, init, local, pads)
+    (4, 2, [1000, 1500], 4, 1, 1, 0),                  # the tiny workload's shape
+    (4, 4, [0, 1, 127, 128, 300, 1022, 3000], 5, 1, 2, 2),
+    (1, 1, [5, 129, 2000], 3, 1, 1, 1),
+    (2, 8, [640, 700], 6, 2, 0, 0),
+    (1, 16, [4095, 77], 8, 0, 3, 1),
+    (16, 1, [513, 2049], 7, 1, 2, 0),
+    (3, 5, [260, 1031, 30], 4, 1, 3, 1),
+]
+
+
+@pytest.mark.parametrize("fmt", [W.K_BF16, W.K_FP8_E4M3, W.K_NVFP4], ids=["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_small_shapes(oracle, fmt, shape):
+    P, H, lens, topk, init, local, pads = SHAPES[shape]
+    say("small", fmt, SHAPES[shape])
+    w = W.make(name="small", R=len(lens), P=P, H=H, k_format=fmt, req_len=lens, topk=topk,
+               init_blocks=init, local_blocks=local, seed=100 + shape, pads=pads,
+               pad_len=4096, device="cuda")
+    if fmt == W.K_NVFP4:
+        Hn.gpu_fp4_store(w)
+        payload, scales = Hn.oracle_pool(oracle, w)
+        assert np.array_equal(w.k.cpu().numpy(), payload), "fp4 payload bytes differ"
+        assert np.array_equal(w.k_scale.cpu().numpy(), scales), "fp4 scale bytes differ"
+        a = w.oracle_args(payload, scales)
+    else:
+        a = w.oracle_args()
+    g = Hn.gpu_step(w)
+    o = oracle.step(**a)
+    Hn.assert_parity(g, o, a)
+
+
+def test_tiny_workload(oracle):
+    say("tiny workload, full comparison")
+    w = W.config(0, device="cuda")
+    a = w.oracle_args()
+    g, o = Hn.gpu_step(w), oracle.step(**a)
+    Hn.assert_parity(g, o, a)
+    assert np.array_equal(g["topk_ids"], o["topk_ids"])
+
+
+def test_invalid_page_ids(oracle):
+    """Page ids outside the pool are not read; the rows that see the block
+    get NaN, and selection ranks NaN below every number."""
+    say("invalid page ids")
+    w = W.make(name="badpage", R=3, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[900, 1500, 400],
+               topk=4, init_blocks=1, local_blocks=1, seed=7, device="cuda")
+    bt = w.block_table
+    s0, s1 = int(w.req_slot[0]), int(w.req_slot[1])
+    bt[s0, 2] = w.n_pages + 5
+    bt[s1, 0] = -3
+    bt[s1, 11] = 1 << 30
+    a = w.oracle_args()
+    g, o = Hn.gpu_step(w), oracle.step(**a)
+    Hn.assert_parity(g, o, a)
+    assert np.isnan(g["block_scores"][:16, 2]).all() and np.isnan(g["block_scores"][16:32, 0]).all()
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 store
+# ---------------------------------------------------------------------------
+def test_fp4_store_exhaustive_rounding(oracle):
+    """Every bf16 x with |x| <= 6 s at every positive finite E4M3 scale s
+    (4.2M values) stored by the GPU and by the oracle: identical bytes."""
+    say("fp4 store exhaustive rounding set")
+    fp8 = pins.fp8_values_torch()
+    pos = np.arange(0, 0x7F80, dtype=np.uint32)
+    posv = (pos << 16).view(np.float32)
+    groups = []
+    for sb in range(1, 0x7F):
+        s = float(fp8[sb])
+        lead = pins.bf16_bits([6 * s])[0]
+        sel = pos[posv <= 6 * s].astype(np.uint16)
+        xs = np.concatenate([sel, sel | 0x8000])
+        xs = np.concatenate([xs, np.zeros((-len(xs)) % 15, np.uint16)]).reshape(-1, 15)
+        groups.append(np.concatenate([np.full((len(xs), 1), lead, np.uint16), xs], axis=1))
+    # also every amax (scale rounding), one group each
+    amax = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    g2 = np.zeros((len(amax), 16), np.uint16)
+    g2[:, 0] = amax
+    groups.append(g2)
+    groups = np.concatenate(groups)
+    groups = np.concatenate([groups, np.zeros(((-len(groups)) % 8, 16), np.uint16)])
+    st = groups.reshape(-1, 128)
+    n = st.shape[0]
+    perm = np.random.default_rng(3).permutation(n).astype(np.int64)   # scattered slots
+    pay_o = np.full((n, 64), 0x5A, np.uint8)
+    sc_o = np.full((n, 8), 0x5A, np.uint8)
+    oracle.fp4_store(st, perm, pay_o, sc_o)
+    stg = torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).cuda()
+    pay_g = torch.full((n, 64), 0x5A, dtype=torch.uint8, device="cuda")
+    sc_g = torch.full((n, 8), 0x5A, dtype=torch.uint8, device="cuda")
+    I.idx_fp4_store(stg, torch.from_numpy(perm).cuda(), pay_g, sc_g)
+    torch.cuda.synchronize()
+    assert np.array_equal(sc_g.cpu().numpy(), sc_o), "scale bytes differ"
+    assert np.array_equal(pay_g.cpu().numpy(), pay_o), "payload bytes differ"
+
+
+def test_fp4_store_skips_and_strides(oracle):
+    """Negative and out-of-range slots are skipped (their bytes keep the
+    fill); a staging row stride larger than 128 is honoured."""
+    say("fp4 store skip/stride")
+    n, n_slots = 3000, 2500
+    rng = np.random.default_rng(5)
+    big = torch.randn(n, 200, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    st = big[:, :128]
+    slots = np.concatenate([rng.permutation(n_slots).astype(np.int64), np.full(n - n_slots, -1)])
+    slots[rng.random(n) < 0.05] = -9
+    slots[rng.random(n) < 0.05] = n_slots + 17
+    pay_o = np.full((n_slots, 64), 0x33, np.uint8)
+    sc_o = np.full((n_slots, 8), 0x33, np.uint8)
+    st_np = np.ascontiguousarray(st.view(torch.int16).numpy().view(np.uint16))
+    oracle.fp4_store(st_np, slots, pay_o, sc_o)
+    pay_g = torch.full((n_slots, 64), 0x33, dtype=torch.uint8, device="cuda")
+    sc_g = torch.full((n_slots, 8), 0x33, dtype=torch.uint8, device="cuda")
+    big_g = big.cuda()
+    I.idx_fp4_store(big_g[:, :128], torch.from_numpy(slots).cuda(), pay_g, sc_g)
+    torch.cuda.synchronize()
+    assert np.array_equal(pay_g.cpu().numpy(), pay_o) and np.array_equal(sc_g.cpu().numpy(), sc_o)
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+def test_packed_equals_per_row():
+    """Each (draft row, head) run as its own request gives bit-identical
+    block scores and ids (sglang PR 45451: packed max scores equal the
+    per-row kernel's)."""
+    for fmt in (W.K_BF16, W.K_FP8_E4M3):
+        say("packed == per-row", fmt)
+        w = W.make(name="pk", R=4, P=4, H=4, k_format=fmt, req_len=[0, 300, 1022, 3000], topk=5,
+                   init_blocks=1, local_blocks=2, seed=61, pads=1, pad_len=2000, device="cuda")
+        g = Hn.gpu_step(w)
+        R, P, H = w.n_req, 4, 4
+        per = W.Workload(**{**w.__dict__})
+        per.n_req, per.packed_queries, per.gqa = R * P * H, 1, 1
+        per.q = w.q.reshape(R * P * H, 1, 128).contiguous()
+        per.req_slot = w.req_slot.repeat_interleave(P * H).contiguous()
+        per.row_len = w.row_len.repeat_interleave(H).contiguous()
+        gp = Hn.gpu_step(per)
+        for key in g:
+            assert np.array_equal(g[key], gp[key], equal_nan=True), f"packed != per-row ({key})"
+
+
+def test_batch_invariance():
+    """A probe request's outputs do not depend on the other requests of the
+    launch (alone, with others, with pads) (ATOM PR 2485, Why / Test)."""
+    say("batch invariance")
+    base = W.make(name="bi", R=6, P=4, H=4, k_format=W.K_FP8_E4M3,
+                  req_len=[2000, 50, 7000, 333, 4100, 1], topk=6, init_blocks=1, local_blocks=2,
+                  seed=71, pads=2, pad_len=3000, device="cuda")
+    full = Hn.gpu_step(base)
+    rows = 16
+    for probe in (0, 2, 4):
+        for others in ([], [1], [3, 5], [1, 3, 5, 6, 7]):
+            sel = [probe] + others
+            sub = W.Workload(**{**base.__dict__})
+            idx_t = torch.as_tensor(sel, device="cuda")
+            sub.n_req = len(sel)
+            sub.q = base.q.reshape(base.n_req, rows, 128)[idx_t].reshape(-1, 4, 128).contiguous()
+            sub.req_slot = base.req_slot[idx_t].contiguous()
+            sub.row_len = base.row_len.reshape(base.n_req, 4)[idx_t].reshape(-1).contiguous()
+            g = Hn.gpu_step(sub)
+            for key in full:
+                assert np.array_equal(g[key][:rows], full[key][probe * rows:(probe + 1) * rows],
+                                      equal_nan=True), (probe, others, key)
+
+
+def test_masked_keys_never_seen():
+    """Poisoning keys past the shortest row changes nothing for that row."""
+    say("masking")
+    w = W.make(name="mask", R=4, P=4, H=4, k_format=W.K_BF16, req_len=[0, 300, 1022, 3000],
+               topk=5, init_blocks=1, local_blocks=2, seed=81, device="cuda")
+    base = Hn.gpu_step(w)
+    bt = w.block_table.cpu().numpy()
+    slots = w.req_slot.cpu().numpy()
+    for r, L in enumerate(w.req_len):
+        for pos in range(int(L), int(L) + 3):
+            page = int(bt[slots[r], pos // 128])
+            w.k[page * 128 + pos % 128] = 8192.0
+    res = Hn.gpu_step(w)
+    for r in range(4):
+        o0 = r * 16
+        for key in res:
+            assert np.array_equal(res[key][o0:o0 + 4], base[key][o0:o0 + 4], equal_nan=True)
+
+
+def test_exact_tie_lower_id():
+    """Bit-identical pages tie exactly; with one free slot the lower id wins."""
+    say("exact tie")
+    w = W.make(name="tie", R=2, P=4, H=4, k_format=W.K_BF16, req_len=[2000, 2500], topk=4,
+               init_blocks=1, local_blocks=2, seed=41, device="cuda")
+    b1, b2 = 3, 9
+    s0 = int(w.req_slot[0])
+    p1, p2 = int(w.block_table[s0, b1]), int(w.block_table[s0, b2])
+    kv = w.k.view(w.n_pages, 128, 128)
+    kv[p1] *= 8
+    kv[p2] = kv[p1]
+    g = Hn.gpu_step(w)
+    for i in range(16):
+        assert g["block_scores"][i, b1] == g["block_scores"][i, b2]
+        ids = set(g["topk_ids"][i].tolist())
+        assert b1 in ids and b2 not in ids
+
+
+def test_topk_synthetic_scores_exact(oracle):
+    """Selection alone on the same fp32 scores (many exact ties, NaN, -0):
+    ids and scores identical to the oracle's."""
+    rng = np.random.default_rng(9)
+    for MB, topk, init, local in [(40, 8, 1, 2), (300, 64, 1, 2), (1000, 64, 0, 0), (8192, 64, 3, 5),
+                                  (700, 1, 1, 0), (50, 50, 2, 2)]:
+        say("topk synthetic", MB, topk, init, local)
+        R = 48
+        nb = rng.integers(0, MB + 1, size=R)
+        nb[:3] = [MB, topk, topk + 1]
+        vals = np.array([-1.0, 0.0, -0.0, 0.5, 1.0, 2.0, np.nan, -np.inf], np.float32)
+        bs = rng.choice(vals, size=(R, MB), p=[.2, .1, .1, .2, .2, .14, .03, .03]).astype(np.float32)
+        bs[R // 2:] = rng.standard_normal((R - R // 2, MB)).astype(np.float32)
+        a = pins.topk_args(nb, MB, topk, init, local, rng)
+        o = oracle.block_topk(bs, **a)
+        dev = "cuda"
+        outs = {"block_scores": torch.from_numpy(bs).to(dev),
+                "topk_ids": torch.full((R, topk), -7, dtype=torch.int32, device=dev),
+                "topk_scores": torch.full((R, topk), 7.0, dtype=torch.float32, device=dev)}
+        p = I.make_params(k_format=W.K_BF16, q=None, k=None, k_scale=None,
+                          req_slot=torch.from_numpy(a["req_slot"]).to(dev), block_table=None,
+                          row_len=torch.from_numpy(a["row_len"]).to(dev), packed_queries=1, gqa=1,
+                          topk=topk, init_blocks=init, local_blocks=local, max_blocks=MB,
+                          n_slot_rows=R, n_pages=0, **outs)
+        I.idx_block_topk(p)
+        torch.cuda.synchronize()
+        assert np.array_equal(outs["topk_ids"].cpu().numpy(), o["topk_ids"])
+        assert np.array_equal(outs["topk_scores"].cpu().numpy(), o["topk_scores"], equal_nan=True)
+
+
+def test_fp4_equals_bf16_of_dequant():
+    """NVFP4 scoring equals bf16 scoring fed the dequantized keys (ATOM PR
+    2745, Validation): ids identical, scores within fp32 summation noise."""
+    say("nvfp4 == bf16 of dequant")
+    w = W.make(name="x", R=4, P=4, H=4, k_format=W.K_NVFP4, req_len=[0, 300, 1022, 3000], topk=5,
+               init_blocks=1, local_blocks=2, seed=14, device="cuda")
+    vals = pins.exact_fp4_staging(w, seed=14)   # exactly representable keys
+    Hn.gpu_fp4_store(w)
+    g4 = Hn.gpu_step(w)
+    pool = np.full((w.n_pages * 128, 128), 8192.0)
+    pool[w.slot_mapping.cpu().numpy()] = vals
+    w16 = W.Workload(**{**w.__dict__})
+    w16.k_format = W.K_BF16
+    w16.k = torch.from_numpy(pins.bf16_bits(pool).view(np.int16)).view(torch.bfloat16).cuda()
+    w16.k_scale = None
+    g16 = Hn.gpu_step(w16)
+    assert np.array_equal(g4["topk_ids"], g16["topk_ids"])
+    a, b = g4["block_scores"], g16["block_scores"]
+    f = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), f)
+    assert np.max(np.abs(a[f] - b[f]) / np.maximum(np.abs(b[f]), 1)) <= 1e-5
+
+
+def test_repeat_launches_identical():
+    """Repeated launches give bit-identical outputs (the graph-replay
+    analogue of sglang PR 45451's tests)."""
+    say("determinism")
+    w = W.make(name="det", R=5, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[100, 900, 4000, 1, 2222],
+               topk=8, init_blocks=1, local_blocks=2, seed=91, device="cuda")
+    first = Hn.gpu_step(w)
+    outs = Hn.gpu_outputs(w)
+    p = Hn.gpu_params(w, outs)
+    for _ in range(50):
+        I.idx_step(p)
+    torch.cuda.synchronize()
+    for key in first:
+        assert np.array_equal(outs[key].cpu().numpy(), first[key], equal_nan=True)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+def _full(oracle, idx, sample, local_blocks=None):
+    say("workload", W.CONFIG_NAMES[idx], "local", local_blocks, "sample", sample)
+    w = W.config(idx, device="cuda", local_blocks=local_blocks)
+    P, H = w.packed_queries, w.gqa
+    if w.k_format == W.K_NVFP4:
+        Hn.gpu_fp4_store(w)
+        # oracle store of the sampled requests' keys only
+        starts = np.concatenate([[0], np.cumsum(w.req_len + P - 1)])
+        toks = np.concatenate([np.arange(starts[r], starts[r + 1]) for r in sample if r < w.n_real])
+        payload, scales = Hn.oracle_pool(oracle, w, toks)
+        slots = w.slot_mapping.cpu().numpy()[toks]
+        assert np.array_equal(w.k.cpu().numpy()[slots], payload[slots]), "fp4 payload differs"
+        assert np.array_equal(w.k_scale.cpu().numpy()[slots], scales[slots]), "fp4 scales differ"
+        a = w.oracle_args(payload, scales)
+    else:
+        a = w.oracle_args()
+    g = Hn.gpu_step(w)
+    sub = Hn.subset_args(a, sample, P, H)
+    o = oracle.step(**sub)
+    rows = Hn.rows_of(sample, P * H)
+    gs = {k: v[rows] for k, v in g.items()}
+    relaxed = Hn.assert_parity(gs, o, sub)
+    # properties at full size: every row's selection is valid
+    nbs = Hn.row_blocks(a)
+    ids = g["topk_ids"]
+    for r in range(ids.shape[0]):
+        nb = int(nbs[r])
+        sel = ids[r][ids[r] >= 0]
+        assert np.all(np.diff(sel) > 0)
+        if nb <= w.topk:
+            assert np.array_equal(sel, np.arange(nb))
+        else:
+            assert len(sel) == w.topk and Hn._forced(nb, w.init_blocks, w.local_blocks) <= set(sel.tolist())
+    assert np.isneginf(g["block_scores"][nbs == 0]).all()
+    return g, relaxed
+
+
+def test_workload_1_bf16_131k(oracle):
+    _full(oracle, 1, sample=[0, 5, 15])
+
+
+@pytest.mark.parametrize("local", [2, 0])
+def test_workload_2_fp8_straddle(oracle, local):
+    g, _ = _full(oracle, 2, sample=[0, 1, 2, 3, 9], local_blocks=local)
+    # the straddling requests: rows end at 32767..32770 -> 256/256/257/257 blocks
+    for r in range(4):
+        for j, nb in enumerate([256, 256, 257, 257]):
+            for h in range(4):
+                row = g["block_scores"][r * 16 + j * 4 + h]
+                assert np.isfinite(row[:nb]).all() and np.isneginf(row[nb:]).all()
+
+
+def test_workload_3_fp8_524k_pads(oracle):
+    g, _ = _full(oracle, 3, sample=[0, 17, 31, 32, 33, 34])
+    pads = g["topk_ids"][32 * 16:]
+    assert (pads == -1).all() and np.isneginf(g["block_scores"][32 * 16:]).all()
+
+
+def test_workload_4_nvfp4_150k(oracle):
+    _full(oracle, 4, sample=[0, 33, 63])

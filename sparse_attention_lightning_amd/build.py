@@ -20,10 +20,16 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(out: Path | str | None = None, verbose: bool = False) -> Path:
+def build(out: Path | str | None = None, verbose: bool = False, extra_flags=(),
+          csrc: Path | str | None = None) -> Path:
+    """Compile the library to ``out``.  ``extra_flags`` (e.g. -D overrides of
+    the score kernel's tuning knobs) and another source directory are for
+    experiments; the default build uses neither."""
     out = Path(out) if out is not None else LIB
+    src = Path(csrc) if csrc is not None else CSRC
     tmp = out.with_name(out.name + f".tmp{os.getpid()}")
-    cmd = ["hipcc", *HIPCC_FLAGS, *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
+    flags = [f if f != f"-I{CSRC}" else f"-I{src}" for f in HIPCC_FLAGS]
+    cmd = ["hipcc", *flags, *extra_flags, *[str(src / s) for s in SOURCES], "-o", str(tmp)]
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)

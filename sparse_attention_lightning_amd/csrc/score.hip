@@ -32,16 +32,32 @@
 
 namespace idx {
 
-constexpr int kWaves = 4;
+// Tuning knobs (compile-time; none of them changes what is computed).
+#ifndef IDX_SCORE_WAVES
+#define IDX_SCORE_WAVES 4        // waves per workgroup
+#endif
+#ifndef IDX_SCORE_PAGES_PER_WAVE
+#define IDX_SCORE_PAGES_PER_WAVE 8
+#endif
+#ifndef IDX_SCORE_RING
+#define IDX_SCORE_RING 0         // half-page buffers per wave (0: per-format default)
+#endif
+#ifndef IDX_SCORE_NT
+#define IDX_SCORE_NT 0           // 1: non-temporal K loads
+#endif
+constexpr int kWaves = IDX_SCORE_WAVES;
 constexpr int kThreads = kWaves * 64;
-constexpr int kPagesPerWave = 8;
+constexpr int kPagesPerWave = IDX_SCORE_PAGES_PER_WAVE;
 constexpr int kChunkPages = kWaves * kPagesPerWave;
+
 
 template <int FMT>
 struct Fmt;
 
 template <>
 struct Fmt<IDX_K_BF16> {
+  // half pages in flight per wave (registers bound it: a bf16 half is 16 KB a wave)
+  static constexpr int kRing = IDX_SCORE_RING ? IDX_SCORE_RING : 2;
   static constexpr int kRowBytes = 256;
   static constexpr int kLoads = 4;  // 16-byte loads per lane per tile
   typedef bf16x8 Op;
@@ -51,6 +67,8 @@ struct Fmt<IDX_K_BF16> {
 
 template <>
 struct Fmt<IDX_K_FP8_E4M3> {
+  // half pages in flight per wave (registers bound it: a bf16 half is 16 KB a wave)
+  static constexpr int kRing = IDX_SCORE_RING ? IDX_SCORE_RING : 3;
   static constexpr int kRowBytes = 128;
   static constexpr int kLoads = 2;
   typedef bf16x8 Op;
@@ -60,6 +78,8 @@ struct Fmt<IDX_K_FP8_E4M3> {
 
 template <>
 struct Fmt<IDX_K_NVFP4> {
+  // half pages in flight per wave (registers bound it: a bf16 half is 16 KB a wave)
+  static constexpr int kRing = IDX_SCORE_RING ? IDX_SCORE_RING : 4;
   static constexpr int kRowBytes = 64;
   static constexpr int kLoads = 1;
   typedef f16x8 Op;
@@ -70,7 +90,7 @@ struct Fmt<IDX_K_NVFP4> {
 // Registers holding one lane's share of a 64-token half page.
 template <int FMT>
 struct Half {
-  uint4 v[4][Fmt<FMT>::kLoads];
+  u32x4 v[4][Fmt<FMT>::kLoads];
   uint32_t sc[4];  // NVFP4: this lane's two scale bytes of each tile
 };
 
@@ -90,8 +110,10 @@ __device__ __forceinline__ void load_half(Half<FMT>& h, const uint8_t* __restric
   for (int t = 0; t < 4; ++t) {
     const uint8_t* row = k + (tok0 + 16 * t) * Fmt<FMT>::kRowBytes;
 #pragma unroll
-    for (int i = 0; i < Fmt<FMT>::kLoads; ++i)
-      h.v[t][i] = *reinterpret_cast<const uint4*>(row + Fmt<FMT>::off(i, g));
+    for (int i = 0; i < Fmt<FMT>::kLoads; ++i) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(row + Fmt<FMT>::off(i, g));
+      h.v[t][i] = IDX_SCORE_NT ? __builtin_nontemporal_load(src) : *src;
+    }
     if constexpr (FMT == IDX_K_NVFP4)
       h.sc[t] = *reinterpret_cast<const uint16_t*>(ks + (tok0 + 16 * t) * 8 + 2 * g);
   }
@@ -104,7 +126,7 @@ __device__ __forceinline__ typename Fmt<FMT>::Op operand(const Half<FMT>& h, int
   if constexpr (FMT == IDX_K_BF16) {
     return __builtin_bit_cast(bf16x8, h.v[t][s]);
   } else if constexpr (FMT == IDX_K_FP8_E4M3) {
-    const uint4 w = h.v[t][s >> 1];
+    const u32x4 w = h.v[t][s >> 1];
     const uint32_t lo = (s & 1) ? w.z : w.x, hi = (s & 1) ? w.w : w.y;
     bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
     bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
@@ -115,7 +137,7 @@ __device__ __forceinline__ typename Fmt<FMT>::Op operand(const Half<FMT>& h, int
     o[4] = c[0]; o[5] = c[1]; o[6] = d[0]; o[7] = d[1];
     return o;
   } else {
-    const uint4 w4 = h.v[t][0];
+    const u32x4 w4 = h.v[t][0];
     const uint32_t w = (s == 0) ? w4.x : (s == 1) ? w4.y : (s == 2) ? w4.z : w4.w;
     const float sc = scale[s >> 1];
     const f16x2 m = mant[s >> 1];
@@ -257,25 +279,43 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
       ok[i] = pid[i] >= 0 && pid[i] < a.n_pages;
     }
 
-    Half<FMT> h0, h1;
-    if (ok[0]) load_half<FMT>(h0, kp, ks, pid[0], 0, n, g);
+    // Units are half pages: unit u is half u % 2 of the wave's page u / 2.
+    // A ring of kRing buffers keeps kRing - 1 units in flight ahead of the
+    // one the matrix cores work on.
+    const int n_units = 2 * (b_load_end - b_begin);
+    constexpr int kRing = Fmt<FMT>::kRing;
+    static_assert(kRing >= 2 && kRing <= 4, "ring of 2..4 half pages");
+    Half<FMT> ring[kRing];
 #pragma unroll
-    for (int i = 0; i < kPagesPerWave; ++i) {
-      const int b = b_begin + i;
-      if (b >= b_load_end) break;
-      if (ok[i]) load_half<FMT>(h1, kp, ks, pid[i], 1, n, g);
-      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      const bool full = (b + 1) * kBlock <= lmin;
-      score_half<FMT>(h0, qf, full, b * kBlock + n, len, mx);
-      if (i + 1 < kPagesPerWave && b + 1 < b_load_end && ok[i + 1])
-        load_half<FMT>(h0, kp, ks, pid[i + 1], 0, n, g);
-      score_half<FMT>(h1, qf, full, b * kBlock + 64 + n, len, mx);
+    for (int u = 0; u < kRing - 1; ++u)
+      if (u < n_units && ok[u >> 1]) load_half<FMT>(ring[u], kp, ks, pid[u >> 1], u & 1, n, g);
+    float mx[4];
+    // constant trip count with uniform guards (no break), so the loop unrolls
+    // and every ring / page index is static
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mx[j] = row16_max(mx[j]);
-      float v = (n == 0) ? mx[0] : (n == 1) ? mx[1] : (n == 2) ? mx[2] : mx[3];
-      if constexpr (FMT == IDX_K_NVFP4) v = ldexpf(v, -sigma);
-      if (!ok[i]) v = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
-      if (writer) wptr[b] = v;
+    for (int u = 0; u < 2 * kPagesPerWave; ++u) {
+      if (u < n_units) {
+        const int ahead = u + kRing - 1;
+        if (ahead < 2 * kPagesPerWave && ahead < n_units && ok[ahead >> 1])
+          load_half<FMT>(ring[ahead % kRing], kp, ks, pid[ahead >> 1], ahead & 1, n, g);
+        const int i = u >> 1;
+        const int b = b_begin + i;
+        if ((u & 1) == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx[j] = -INFINITY;
+        }
+        const bool full = (b + 1) * kBlock <= lmin;
+        score_half<FMT>(ring[u % kRing], qf, full, b * kBlock + 64 * (u & 1) + n, len, mx);
+        if (u & 1) {
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = row16_max(mx[j]);
+          float o = (n == 0) ? v[0] : (n == 1) ? v[1] : (n == 2) ? v[2] : v[3];
+          if constexpr (FMT == IDX_K_NVFP4) o = ldexpf(o, -sigma);
+          if (!ok[i]) o = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
+          if (writer) wptr[b] = o;
+        }
+      }
     }
   }
   // blocks past the group's longest row (and every block of a graph pad)

@@ -42,6 +42,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=None,
                     help="requests in the CPU-oracle sample (default: all real requests)")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MiB",
+                    help="first run a plain device copy of this many MiB three times (a kernel of "
+                         "known traffic, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -69,8 +72,9 @@ def traffic_from_profiles(kernel: str, workload: str, digest: str):
 def main() -> int:
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU: the indexer step has no multi-GPU path in this build "
-              "(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py runs on one GPU: the indexer step has no multi-GPU path in this build; "
+              "requests shard across GPUs with no exchange, so one GPU's share is this same step "
+              "on fewer requests", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -81,6 +85,13 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.calibration_copy:
+        src = torch.ones(args.calibration_copy << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = W.config(args.config, device=dev, local_blocks=args.local_blocks)
     rows, K, MB = w.rows, w.topk, w.max_blocks
     outs = {"block_scores": torch.empty((rows, MB), dtype=torch.float32, device=dev),

@@ -67,6 +67,8 @@ enum {
 /* Largest max_blocks: 1,048,576-token contexts, the context length the
  * pages serve with (sglang PR 45451, Reproduce: --context-length). */
 #define IDX_MAX_BLOCKS 8192
+/* Largest n_req (graph pads included) one call accepts. */
+#define IDX_MAX_REQ 8192
 
 /*
  * Parameters of one indexer step (one layer, all requests of the batch).
@@ -101,7 +103,7 @@ enum {
  */
 typedef struct idx_params {
   int32_t k_format;       /* IDX_K_*                                        */
-  int32_t n_req;          /* requests in the launch, graph pads included     */
+  int32_t n_req;          /* requests in the launch, graph pads included, <= IDX_MAX_REQ */
   int32_t n_slot_rows;    /* rows of block_table (the request table)         */
   int32_t packed_queries; /* draft rows per request, >= 1                    */
   int32_t gqa;            /* index heads, >= 1; packed_queries*gqa <= 16     */

@@ -39,6 +39,8 @@ int check(const idx_params* p, int need) {
   if (p->n_req < 0 || p->n_slot_rows < 0 || p->n_pages < 0)
     return fail(IDX_E_SHAPE, "negative count (n_req %d, n_slot_rows %d, n_pages %lld)",
                 p->n_req, p->n_slot_rows, (long long)p->n_pages);
+  if (p->n_req > IDX_MAX_REQ)
+    return fail(IDX_E_SHAPE, "n_req %d exceeds %d", p->n_req, IDX_MAX_REQ);
   if (p->max_blocks < 0 || p->max_blocks > IDX_MAX_BLOCKS)
     return fail(IDX_E_SHAPE, "max_blocks %d outside [0, %d]", p->max_blocks, IDX_MAX_BLOCKS);
   if (p->reserved != 0) return fail(IDX_E_SHAPE, "reserved field must be 0");

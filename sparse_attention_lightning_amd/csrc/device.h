@@ -33,7 +33,6 @@ struct StepArgs {
   int64_t n_pages;
   int32_t k_format;
   int32_t n_req, n_slot_rows, P, H, max_blocks, topk, init_blocks, local_blocks;
-  int32_t n_chunks;  // score kernel: workgroups per request
 };
 
 hipError_t launch_score(const StepArgs& a, hipStream_t stream);
@@ -63,6 +62,32 @@ __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp_mov<0x124>(x));  // row_ror:4
   x = fmaxf(x, dpp_mov<0x128>(x));  // row_ror:8
   return x;
+}
+
+// Exclusive prefix sum over a workgroup of THREADS threads (all must call);
+// *total receives the full sum.  wave_tot: THREADS / 64 words of LDS.
+template <int THREADS>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
+                                                         uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < THREADS / 64; ++w) {
+    const uint32_t t = wave_tot[w];
+    before += (w < wave) ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
 }
 
 }  // namespace idx

@@ -30,30 +30,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the full sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
-                                                         uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
-    const uint32_t t = wave_tot[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* wave_tot) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d));
@@ -114,7 +90,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     nforced += (j < cnt && forced) ? 1u : 0u;
   }
   uint32_t total;
-  block_exclusive_scan(nforced, wave_tot, &total);
+  block_exclusive_scan<kTopkThreads>(nforced, wave_tot, &total);
   const uint32_t F = total;
   kmin = block_min_u32(kmin, wave_tot);
   kmax = ~block_min_u32(~kmax, wave_tot);
@@ -142,7 +118,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
       // thread t looks at digit 255 - t: counts of larger digits come first
       const uint32_t h = hist[255 - tid];
       uint32_t tot;
-      const uint32_t above = block_exclusive_scan(h, wave_tot, &tot);
+      const uint32_t above = block_exclusive_scan<kTopkThreads>(h, wave_tot, &tot);
       if (above < want && want <= above + h) {
         pick_digit = 255u - (uint32_t)tid;
         pick_above = above;
@@ -172,7 +148,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
       eq += (!forced && want > 0 && kt == T) ? 1u : 0u;
     }
   }
-  const uint32_t ex = block_exclusive_scan((sure << 16) | eq, wave_tot, &total);
+  const uint32_t ex = block_exclusive_scan<kTopkThreads>((sure << 16) | eq, wave_tot, &total);
   uint32_t eq_rank = ex & 0xFFFFu;
   uint32_t pos = (ex >> 16) + min(eq_rank, want);
 #pragma unroll

@@ -7,20 +7,24 @@
 // highest block scores, ties to the lower block id.  Selection is exact.
 //
 // One workgroup of 256 threads per (row, head).  Thread t owns the contiguous
-// blocks [t*C, t*C + C), C = ceil(nb / 256) <= 32, and keeps their scores and
-// 32-bit order keys in registers (all loads issued at once).  The key's
-// unsigned order is the selection order: NaN below every number, -0 equal to
-// +0.  A radix select over the non-forced keys finds the k-th largest key T,
-// k = topk - |forced|: it starts at the highest bit where the row's keys
-// differ, takes up to 8 bits a pass with an LDS histogram, and stops early
-// once the chosen bin holds exactly the keys still needed.  One packed scan of
+// blocks [t*C, t*C + C), C = ceil(max_blocks / 256) <= 32 (rounded up to a
+// multiple of 4 when rows are 16-byte aligned), and loads their scores into
+// registers first thing; the row's slot and length are fetched before them
+// and the score loads do not wait for them.  Keys are 32-bit integers whose unsigned order is the selection
+// order: NaN below every number, -0 equal to +0.  A radix select over the
+// non-forced keys finds the k-th largest key T, k = topk - |forced|: it starts
+// at the highest bit where the row's keys differ, takes up to 8 bits a pass
+// (per-wave LDS histograms, summed per bin), and stops early once the chosen
+// bin holds exactly the keys still needed.  One packed scan of
 // (taken-for-sure, equal-to-T) counts then gives every thread its output
-// position, so ids leave in ascending order without a sort.
+// position, so ids leave in ascending order without a sort.  Scans and
+// reductions inside a wave use DPP; waves meet through LDS.
 #include "device.h"
 
 namespace idx {
 
 constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kPerThread = IDX_MAX_BLOCKS / kTopkThreads;  // 32
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -30,35 +34,82 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* wave_tot) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d));
-  if ((threadIdx.x & 63) == 0) wave_tot[threadIdx.x >> 6] = v;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave (row_shr within rows of
+// 16 lanes, then row_bcast:15 / row_bcast:31 across rows).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  x += dpp_u32<0x111>(x);        // row_shr:1
+  x += dpp_u32<0x112>(x);        // row_shr:2
+  x += dpp_u32<0x114>(x);        // row_shr:4
+  x += dpp_u32<0x118>(x);        // row_shr:8
+  x += dpp_u32<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_u32<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup; *total gets the sum of all.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_sum(v);
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  uint32_t m = wave_tot[0];
+  uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 1; w < kTopkThreads / 64; ++w) m = min(m, wave_tot[w]);
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t t = wave_tot[w];
+    before += (w < wave) ? t : 0u;
+    all += t;
+  }
   __syncthreads();
-  return m;
+  *total = all;
+  return before + incl - v;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_tot[kTopkThreads / 64];
+  __shared__ uint32_t hist[kTopkWaves][256];
+  __shared__ uint32_t red[3][kTopkWaves];
+  __shared__ uint32_t wave_tot[kTopkWaves];
   __shared__ uint32_t pick_digit, pick_above, pick_count;
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rows = a.P * a.H;
   const int o = blockIdx.x;
   const int r = o / rows, i = o - r * rows;
   const int K = a.topk, MB = a.max_blocks;
-  int32_t* ids = a.topk_ids + (int64_t)o * K;
-  float* sc = a.topk_scores + (int64_t)o * K;
   const float* bs = a.block_scores + (int64_t)o * MB;
 
+  // the row's slot and length first: these two scalar loads must not queue
+  // behind the burst of score loads below
   const int slot = a.req_slot[r];
+  const int len_raw = a.row_len[r * a.P + i / a.H];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // this thread's scores (they do not wait for the length); 16-byte loads
+  // when every thread's range starts 16-byte aligned
+  const int C = (MB % 4 == 0) ? ((MB / 4 + kTopkThreads - 1) / kTopkThreads) * 4
+                              : (MB + kTopkThreads - 1) / kTopkThreads;
+  const int b0 = tid * C;
+  float sv[kPerThread];
+  if (MB % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < kPerThread / 4; ++q) {
+      f32x4 v = (4 * q < C && b0 + 4 * q < MB) ? *reinterpret_cast<const f32x4*>(bs + b0 + 4 * q)
+                                               : f32x4{0.f, 0.f, 0.f, 0.f};
+      sv[4 * q] = v[0]; sv[4 * q + 1] = v[1]; sv[4 * q + 2] = v[2]; sv[4 * q + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
+  }
+
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
-  const int nb = pad ? 0 : blocks_of(clamp_len(a.row_len[r * a.P + i / a.H], MB));
+  const int nb = pad ? 0 : blocks_of(clamp_len(len_raw, MB));
+  int32_t* ids = a.topk_ids + (int64_t)o * K;
+  float* sc = a.topk_scores + (int64_t)o * K;
 
   if (nb <= K) {
     for (int t = tid; t < K; t += kTopkThreads) {
@@ -68,15 +119,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     return;
   }
 
-  // this thread's blocks and keys
-  const int C = (nb + kTopkThreads - 1) / kTopkThreads;
-  const int b0 = tid * C;
   const int cnt = max(0, min(C, nb - b0));
   const int init = a.init_blocks, local_from = nb - a.local_blocks;
-  float sv[kPerThread];
   uint32_t key[kPerThread];
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) sv[j] = (j < cnt) ? bs[b0 + j] : 0.0f;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nforced = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
@@ -89,11 +134,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     }
     nforced += (j < cnt && forced) ? 1u : 0u;
   }
-  uint32_t total;
-  block_exclusive_scan<kTopkThreads>(nforced, wave_tot, &total);
-  const uint32_t F = total;
-  kmin = block_min_u32(kmin, wave_tot);
-  kmax = ~block_min_u32(~kmax, wave_tot);
+  // one combined reduction: min, max, forced count
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+    nforced += (uint32_t)__shfl_xor((int)nforced, d);
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+    red[2][wave] = nforced;
+  }
+  __syncthreads();
+  uint32_t F = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+    F += red[2][w];
+  }
 
   // radix select of the want-th largest non-forced key
   uint32_t want = (uint32_t)K - F;  // the free slots (F <= init + local <= K)
@@ -104,21 +164,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     while (hi >= 0) {
       const int lo = max(hi - 7, 0);
       const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-      hist[tid] = 0;
-      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[wave][lane + 64 * q] = 0;
+      // this wave's histogram: cleared and filled by the same wave, in order
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
         const int b = b0 + j;
         const bool forced = b < init || b >= local_from;
         const uint32_t k = key[j];
         const bool match = (hi == 31) || ((k >> (hi + 1)) == (prefix >> (hi + 1)));
-        if (j < cnt && !forced && match) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+        if (j < cnt && !forced && match) atomicAdd(&hist[wave][(k >> lo) & dmask], 1u);
       }
       __syncthreads();
       // thread t looks at digit 255 - t: counts of larger digits come first
-      const uint32_t h = hist[255 - tid];
+      uint32_t h = 0;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) h += hist[w][255 - tid];
       uint32_t tot;
-      const uint32_t above = block_exclusive_scan<kTopkThreads>(h, wave_tot, &tot);
+      const uint32_t above = block_scan(h, wave_tot, &tot);
       if (above < want && want <= above + h) {
         pick_digit = 255u - (uint32_t)tid;
         pick_above = above;
@@ -129,7 +192,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
       want -= pick_above;
       tshift = (uint32_t)lo;
       const bool done = (pick_count == want);  // the whole bin is taken
-      __syncthreads();
       if (done) break;
       hi = lo - 1;
     }
@@ -148,7 +210,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
       eq += (!forced && want > 0 && kt == T) ? 1u : 0u;
     }
   }
-  const uint32_t ex = block_exclusive_scan<kTopkThreads>((sure << 16) | eq, wave_tot, &total);
+  uint32_t total;
+  const uint32_t ex = block_scan((sure << 16) | eq, wave_tot, &total);
   uint32_t eq_rank = ex & 0xFFFFu;
   uint32_t pos = (ex >> 16) + min(eq_rank, want);
 #pragma unroll

@@ -161,7 +161,8 @@ def main() -> int:
     score_mean_s = float(np.mean(score_ms)) / 1e3
     achieved = score_bytes / score_mean_s / 1e9
     digest = source_digest()
-    traffic = traffic_from_profiles("score_kernel_fp8", W.CONFIG_NAMES[args.config], digest)
+    fmt_name = {W.K_BF16: "bf16", W.K_FP8_E4M3: "fp8", W.K_NVFP4: "nvfp4"}[w.k_format]
+    traffic = traffic_from_profiles(f"score_kernel_{fmt_name}", W.CONFIG_NAMES[args.config], digest)
 
     line = {
         "metric": METRIC,

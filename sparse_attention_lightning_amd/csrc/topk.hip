@@ -7,7 +7,7 @@
 // highest block scores, ties to the lower block id.  Selection is exact.
 //
 // One workgroup of 256 threads per (row, head).  Thread t owns the contiguous
-// blocks [t*C, t*C + C), C = ceil(max_blocks / 256) <= 32 (rounded up to a
+// blocks [t*C, t*C + C), C = ceil(max_blocks / 256) <= 16 or 32 (rounded up to a
 // multiple of 4 when rows are 16-byte aligned), and loads their scores into
 // registers first thing; the row's slot and length are fetched before them
 // and the score loads do not wait for them.  Keys are 32-bit integers whose unsigned order is the selection
@@ -25,7 +25,6 @@ namespace idx {
 
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kPerThread = IDX_MAX_BLOCKS / kTopkThreads;  // 32
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) return 0u;  // NaN
@@ -51,7 +50,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
   return x;
 }
 
-// Exclusive prefix sum over the workgroup; *total gets the sum of all.
+// Exclusive prefix sum over the workgroup; *total gets the sum of all.  One
+// barrier: the caller must not reuse `wave_tot` before another barrier.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_inclusive_sum(v);
@@ -64,15 +64,19 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot, u
     before += (w < wave) ? t : 0u;
     all += t;
   }
-  __syncthreads();
   *total = all;
   return before + incl - v;
 }
 
+// PER: blocks per thread (16 covers max_blocks <= 4096, 32 the full limit).
+template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
-  __shared__ uint32_t hist[kTopkWaves][256];
+  constexpr int kPerThread = PER;
+  constexpr int kBins = 4096, kBinsPerThread = kBins / kTopkThreads;  // 16
+  __shared__ u32x4 hist4[kBins / 4];
+  uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
   __shared__ uint32_t red[3][kTopkWaves];
-  __shared__ uint32_t wave_tot[kTopkWaves];
+  __shared__ uint32_t wave_tot[2][kTopkWaves];
   __shared__ uint32_t pick_digit, pick_above, pick_count;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -106,6 +110,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     for (int j = 0; j < kPerThread; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
   }
 
+  // this thread's 16 bins, highest digits first: bins [kBins - 16(t+1), kBins - 16 t)
+  const int bin0 = kBins - kBinsPerThread * (tid + 1);
+#pragma unroll
+  for (int q = 0; q < kBinsPerThread / 4; ++q) hist4[bin0 / 4 + q] = u32x4{0u, 0u, 0u, 0u};
+
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
   const int nb = pad ? 0 : blocks_of(clamp_len(len_raw, MB));
   int32_t* ids = a.topk_ids + (int64_t)o * K;
@@ -121,16 +130,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
 
   const int cnt = max(0, min(C, nb - b0));
   const int init = a.init_blocks, local_from = nb - a.local_blocks;
-  uint32_t key[kPerThread];
+  // keys are recomputed from the scores where needed (fewer live registers)
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nforced = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int b = b0 + j;
     const bool forced = b < init || b >= local_from;
-    key[j] = order_key(sv[j]);
+    const uint32_t k = order_key(sv[j]);
     if (j < cnt && !forced) {
-      kmin = min(kmin, key[j]);
-      kmax = max(kmax, key[j]);
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
     }
     nforced += (j < cnt && forced) ? 1u : 0u;
   }
@@ -162,37 +171,45 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     int hi = 31 - __builtin_clz(kmin ^ kmax);
     prefix = (hi == 31) ? 0u : (kmin >> (hi + 1)) << (hi + 1);
     while (hi >= 0) {
-      const int lo = max(hi - 7, 0);
+      const int lo = max(hi - 11, 0);
       const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[wave][lane + 64 * q] = 0;
-      // this wave's histogram: cleared and filled by the same wave, in order
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
         const int b = b0 + j;
         const bool forced = b < init || b >= local_from;
-        const uint32_t k = key[j];
+        const uint32_t k = order_key(sv[j]);
         const bool match = (hi == 31) || ((k >> (hi + 1)) == (prefix >> (hi + 1)));
-        if (j < cnt && !forced && match) atomicAdd(&hist[wave][(k >> lo) & dmask], 1u);
+        if (j < cnt && !forced && match) atomicAdd(&hist[(k >> lo) & dmask], 1u);
       }
       __syncthreads();
-      // thread t looks at digit 255 - t: counts of larger digits come first
-      uint32_t h = 0;
+      // sum and clear this thread's 16 bins (descending digits)
+      uint32_t local = 0;
 #pragma unroll
-      for (int w = 0; w < kTopkWaves; ++w) h += hist[w][255 - tid];
-      uint32_t tot;
-      const uint32_t above = block_scan(h, wave_tot, &tot);
-      if (above < want && want <= above + h) {
-        pick_digit = 255u - (uint32_t)tid;
-        pick_above = above;
-        pick_count = h;
+      for (int q = 0; q < kBinsPerThread / 4; ++q) {
+        const u32x4 v = hist4[bin0 / 4 + q];
+        local += v[0] + v[1] + v[2] + v[3];
       }
+      uint32_t tot;
+      uint32_t above = block_scan(local, wave_tot[0], &tot);
+      if (above < want && want <= above + local) {
+        // the cut is in this thread's bins: walk them from the highest digit
+        for (int q = kBinsPerThread - 1; q >= 0; --q) {
+          const uint32_t hq = hist[bin0 + q];
+          if (above < want && want <= above + hq) {
+            pick_digit = (uint32_t)(bin0 + q);
+            pick_above = above;
+            pick_count = hq;
+          }
+          above += hq;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kBinsPerThread / 4; ++q) hist4[bin0 / 4 + q] = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
       prefix |= pick_digit << lo;
       want -= pick_above;
       tshift = (uint32_t)lo;
-      const bool done = (pick_count == want);  // the whole bin is taken
-      if (done) break;
+      if (pick_count == want) break;  // the whole bin is taken
       hi = lo - 1;
     }
   }
@@ -204,21 +221,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   for (int j = 0; j < kPerThread; ++j) {
     const int b = b0 + j;
     const bool forced = b < init || b >= local_from;
-    const uint32_t kt = key[j] >> tshift;
+    const uint32_t kt = order_key(sv[j]) >> tshift;
     if (j < cnt) {
       sure += (forced || (want > 0 && kt > T)) ? 1u : 0u;
       eq += (!forced && want > 0 && kt == T) ? 1u : 0u;
     }
   }
   uint32_t total;
-  const uint32_t ex = block_scan((sure << 16) | eq, wave_tot, &total);
+  const uint32_t ex = block_scan((sure << 16) | eq, wave_tot[1], &total);
   uint32_t eq_rank = ex & 0xFFFFu;
   uint32_t pos = (ex >> 16) + min(eq_rank, want);
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int b = b0 + j;
     const bool forced = b < init || b >= local_from;
-    const uint32_t kt = key[j] >> tshift;
+    const uint32_t kt = order_key(sv[j]) >> tshift;
     if (j < cnt) {
       bool take = forced || (want > 0 && kt > T);
       if (!forced && want > 0 && kt == T) {
@@ -238,7 +255,11 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.n_req * a.P * a.H;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
+  static_assert(IDX_MAX_BLOCKS <= 32 * kTopkThreads, "32 blocks per thread cover the limit");
+  if (a.max_blocks <= 16 * kTopkThreads)
+    hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<32>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -7,27 +7,38 @@
 // request whose slot lies outside the request table is a graph pad: it reads
 // no K.
 //
-// Work split.  The grid is persistent (as many workgroups as fit on the chip
-// at once).  Every workgroup first computes, for all requests, the number of
-// blocks the group reads and their prefix sums (in LDS); the N pages of the
-// whole step, in (request, block) order, are then cut into equal contiguous
-// slices, one per wave.  A wave walks its slice as tasks of at most 64 pages
-// of one request, so it pays one start-up per task instead of one per few
-// pages, and all waves finish together.
+// Work split.  One workgroup of eight waves per CU stays resident for the
+// whole launch.  The pages of the step, in (request, block) order, are cut
+// into chunks that never cross a request: 32 pages, so that a row's scores of
+// a chunk fill one 128-byte line, except in the last twentieth of the step,
+// where chunks have 8 pages so that the launch ends evenly.  Workgroups take
+// chunks from a counter in the caller's scheduling state (the first two per
+// workgroup are fixed, so the launch does not open with every workgroup on
+// the counter), and waves take single pages from their workgroup's chunks
+// through LDS.  Both levels are dynamic because shares of the memory system
+// are not even: the two waves of a SIMD do not get equal shares of its
+// memory pipeline (the older runs about twice as fast) and CUs do not get
+// equal shares of HBM, so with fixed slices a launch lasts as long as its
+// slowest wave.  The workgroup that finishes last returns the counter to
+// zero for the next launch.
 //
-// Within a task, lane j holds the page id of the task's page j, and the wave
-// streams the task as 64-token halves through a ring of register buffers,
-// keeping RING - 1 halves in flight while the matrix cores work on one.
-// Loads go through per-page buffer descriptors: a page that must not be read
-// (out of range, or past the task) gets an empty descriptor and reads zeros
-// without touching memory, so the loads need no branches and the hardware
-// wait counters can keep the prefetches in flight.  Each half is four 16-token
-// tiles; per tile and per 32-element k-step one MFMA 16x16x32 computes 16 rows
-// x 16 tokens.  Lane l: n = l % 16 is the MFMA column (token) and the A-operand
-// row, g = l / 16 its k-group; the fp32 result holds rows 4g..4g+3 of token n.
-// The k positions a lane feeds are chosen per format so that each lane's loads
-// are 16-byte pieces of its own token's row, and Q is loaded with the same
-// d -> k assignment:
+// A chunk's LDS slot holds its page ids, the request's query tile and row
+// lengths (copied in by the wave that fetched the chunk, so a change of
+// request costs a wave LDS reads only) and the chunk's block scores; the
+// wave that completes the chunk's last page writes its rows out.
+//
+// Each wave streams its pages as 64-token halves through a ring of register
+// buffers, keeping RING - 1 halves in flight while the matrix cores work on
+// one.  Loads go through per-page buffer descriptors: a page that must not be
+// read (out of range, or no page at all) gets an empty descriptor and reads
+// zeros without touching memory, so the loads need no branches and the
+// hardware wait counters can keep the prefetches in flight.  Each half is
+// four 16-token tiles; per tile and per 32-element k-step one MFMA 16x16x32
+// computes 16 rows x 16 tokens.  Lane l: n = l % 16 is the MFMA column (token)
+// and the A-operand row, g = l / 16 its k-group; the fp32 result holds rows
+// 4g..4g+3 of token n.  The k positions a lane feeds are chosen per format so
+// that each lane's loads are 16-byte pieces of its own token's row, and Q is
+// read with the same d -> k assignment:
 //   bf16  row 256 B: step s takes d = 32 s + 8 g .. +8       (4 loads / tile)
 //   fp8   row 128 B: bytes [16g, +16) and [64 + 16g, +16);  (2 loads / tile)
 //         step s: d = 16 g + 8 s (s < 2), 64 + 16 g + 8 (s - 2)
@@ -40,20 +51,25 @@
 // bf16 queries are converted to f16 under a power-of-two scale 2^sigma that
 // puts the tile's largest magnitude in [2^14, 2^15); the fp32 block max is
 // scaled back by 2^-sigma, which is exact.
+#include <climits>
+#include <cstddef>
+
 #include "device.h"
 
 namespace idx {
 
 // Tuning knobs (compile-time; none of them changes what is computed).
 #ifndef IDX_SCORE_RING
-#define IDX_SCORE_RING 0         // half-page buffers per wave, even (0: per-format default)
+#define IDX_SCORE_RING 0         // half-page buffers per wave (0: per-format default)
 #endif
 #ifndef IDX_SCORE_NT
 #define IDX_SCORE_NT 0           // 1: non-temporal (streaming) K loads
 #endif
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTaskPages = 64;   // one page id per lane
+constexpr int kRoundPages = 1024;  // pages a workgroup stages at once
+constexpr int kRoundReqs = 8;      // requests a round may touch
+constexpr int kQStride = 136;      // 16-bit values per query row in LDS (272 B: rows change banks)
 
 template <int FMT>
 struct Fmt;
@@ -218,133 +234,245 @@ __device__ __forceinline__ void score_half(const Half<FMT>& h, const typename Fm
   }
 }
 
-// One task: pages [b_s, b_s + cnt) of request r (cnt <= 64), all P*H rows.
-// `stage` is this wave's LDS buffer of kTileRows x kTaskPages block scores:
-// the task's results are collected there and written out row by row, so
-// every row leaves as one contiguous run instead of one 4-byte store per page.
+
+// ---------------------------------------------------------------------------
+// Rounds.  A workgroup's range of the step's pages is handled in rounds of at
+// most kRoundPages pages touching at most kRoundReqs requests (one round at
+// the sizes served); a round's page ids, query tiles, row lengths and block
+// scores live in LDS.
+
+struct RoundReq {
+  int32_t r, p0, nbg, lmin;  // request, its first page in step order, its pages, shortest row
+  int32_t sigma, pad0, pad1, pad2;
+  int32_t len[kTileRows];    // each row's clamped length, 0 past the request's rows
+};
+
+struct RoundLds {
+  float stage[kTileRows][kRoundPages];            // block scores of the round
+  int32_t pid[kRoundPages];                       // page ids
+  uint8_t ridx[kRoundPages];                      // each page's request within the round
+  uint16_t q[kRoundReqs][kTileRows][kQStride];    // query tiles (bf16, or f16 scaled by 2^sigma)
+  RoundReq req[kRoundReqs];
+  uint32_t amax[kRoundReqs];                      // NVFP4: largest |q| of each tile (float bits)
+  uint32_t next;                                  // pages handed out
+};
+static_assert(offsetof(RoundLds, q) % 16 == 0 && offsetof(RoundLds, req) % 16 == 0, "16-byte LDS rows");
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Fill the round's LDS (all threads; one barrier inside).  Pages [lo, lo + np)
+// of the step belong to requests r0 .. r0 + nreq - 1.
 template <int FMT>
-__device__ __forceinline__ void score_task(const StepArgs& a, int r, int b_s, int cnt, int lane,
-                                           int n, int g, float* stage) {
-  typedef typename Fmt<FMT>::Op Op;
+__device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre, int r0, int nreq,
+                            uint32_t lo, int np, int tid) {
   const int P = a.P, H = a.H, rows = P * H, MB = a.max_blocks;
-  const int slot = a.req_slot[r];  // a task never belongs to a graph pad
-  const int32_t* bt = a.block_table + (int64_t)slot * MB + b_s;
-  const int pidv = (lane < cnt) ? bt[lane] : -1;  // lane j: page id of the task's page j
-
-  int lmin = MB * kBlock;
-  for (int j = 0; j < P; ++j) lmin = min(lmin, clamp_len(a.row_len[r * P + j], MB));
-  int len[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 4 * g + j;
-    len[j] = (row < rows) ? clamp_len(a.row_len[r * P + row / H], MB) : 0;
+  if (tid < nreq) {
+    const int r = r0 + tid;
+    RoundReq& rq = L.req[tid];
+    rq.r = r;
+    rq.p0 = (int)pre[r];
+    rq.nbg = (int)(pre[r + 1] - pre[r]);
+    int lm = INT_MAX;
+    for (int j = 0; j < P; ++j) lm = min(lm, clamp_len(a.row_len[r * P + j], MB));
+    rq.lmin = lm;
+    rq.sigma = 0;
+    L.amax[tid] = 0;
   }
-  const int wrow = 4 * g + n;  // lanes n < 4 hold row 4g + n
-  const bool writer = n < 4 && wrow < rows;
-  const int my_len = (n == 0) ? len[0] : (n == 1) ? len[1] : (n == 2) ? len[2] : len[3];
-
-  // Q fragments: A operand row n, k-group g
-  Op qf[4];
-  int sigma = 0;
-  const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)r * rows + n) * kHeadDim;
+  if (tid < nreq * kTileRows) {
+    const int j = tid / kTileRows, i = tid % kTileRows;
+    L.req[j].len[i] = (i < rows) ? clamp_len(a.row_len[(r0 + j) * P + i / H], MB) : 0;
+  }
+  for (int k = tid; k < np; k += kThreads) {
+    const uint32_t u = lo + (uint32_t)k;
+    int j = 0;
+    while (j + 1 < nreq && pre[r0 + j + 1] <= u) ++j;
+    const int r = r0 + j;
+    const int slot = a.req_slot[r];  // a request with pages is no graph pad
+    L.pid[k] = a.block_table[(int64_t)slot * MB + (int)(u - pre[r])];
+    L.ridx[k] = (uint8_t)j;
+  }
+  // query tiles: piece e = (request j, row, group of 8 values); 4 per thread
+  u32x4 pc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + kThreads * i, j = e >> 8, row = (e >> 4) & 15, col = (e & 15) * 8;
+    pc[i] = u32x4{0u, 0u, 0u, 0u};
+    if (j < nreq && row < rows)
+      pc[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                              ((int64_t)(r0 + j) * rows + row) * kHeadDim + col);
+  }
   if constexpr (FMT == IDX_K_NVFP4) {
-    bf16x8 qb[4];
-    float amax = 0.f;
+    __syncthreads();  // amax cleared
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qb[s] = (n < rows) ? *reinterpret_cast<const bf16x8*>(qrow + Fmt<FMT>::d0(s, g)) : bf16x8{};
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + kThreads * i, j = e >> 8;
+      float m = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qb[s][e]));
+      for (int w = 0; w < 4; ++w)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(pc[i][w] << 16)), fabsf(__uint_as_float(pc[i][w] & 0xFFFF0000u))));
+      if (j < nreq) atomicMax(&L.amax[j], __float_as_uint(m));  // non-negative floats order as integers
     }
-    amax = row16_max(amax);
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (amax > 0.f) {
-      int ex;
-      frexpf(amax, &ex);  // amax < 2^ex
-      sigma = 15 - ex;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + kThreads * i, j = e >> 8;
+      if (j >= nreq) continue;
+      const float amax = __uint_as_float(L.amax[j]);
+      int sigma = 0;
+      if (amax > 0.f) {
+        int ex;
+        frexpf(amax, &ex);  // amax < 2^ex
+        sigma = 15 - ex;
+      }
+      if ((e & 255) == 0) L.req[j].sigma = sigma;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const _Float16 lo16 = (_Float16)ldexpf(__uint_as_float(pc[i][w] << 16), sigma);
+        const _Float16 hi16 = (_Float16)ldexpf(__uint_as_float(pc[i][w] & 0xFFFF0000u), sigma);
+        pc[i][w] = (uint32_t)__builtin_bit_cast(uint16_t, lo16) | ((uint32_t)__builtin_bit_cast(uint16_t, hi16) << 16);
+      }
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = (_Float16)ldexpf((float)qb[s][e], sigma);
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qf[s] = (n < rows) ? *reinterpret_cast<const Op*>(qrow + Fmt<FMT>::d0(s, g)) : Op{};
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + kThreads * i, j = e >> 8, row = (e >> 4) & 15, col = (e & 15) * 8;
+    if (j < nreq) *reinterpret_cast<u32x4*>(&L.q[j][row][col]) = pc[i];
+  }
+  if (tid == 0) L.next = 0;
+}
 
+// One wave's part of a round: pages from the round's counter until none is
+// left.  Wave page p (two units) is described by lane p % 64 of vm_tag (round
+// page | request << 16, or -1) and vm_pid.
+template <int FMT>
+__device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uint32_t lo, int np, int lane,
+                                             int n, int g) {
+  typedef typename Fmt<FMT>::Op Op;
+  constexpr int kRing = Fmt<FMT>::kRing;
+  static_assert(kRing >= 2, "at least one half page in flight");
+  constexpr int kPageBytes = kBlock * Fmt<FMT>::kRowBytes;
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k);
   const uint8_t* ks = a.k_scale;
-  constexpr int kPageBytes = kBlock * Fmt<FMT>::kRowBytes;
-  constexpr int kRing = Fmt<FMT>::kRing;
-  static_assert(kRing == 2 || kRing == 4, "an even ring of 2 or 4 half pages");
-  const int n_units = 2 * cnt;  // unit u: half u % 2 of task page u / 2
+  const int rows = a.P * a.H;
+  const int wrow = 4 * g + n;  // lanes n < 4 hold row 4g + n
+  const bool writer = n < 4 && wrow < rows;
 
-  // issue the loads of unit ua (any ua: past the task it reads zeros)
-  auto issue = [&](Half<FMT>& h, int ua) {
-    const int j = ua >> 1;
-    const int pid = __builtin_amdgcn_readlane(pidv, min(j, kTaskPages - 1));
-    const bool ok = j < cnt && pid >= 0 && pid < a.n_pages;
+  int vm_tag = -1, vm_pid = -1;
+  bool done = false;
+  int last = -1;  // last wave page that holds a page
+
+  int cur = -1, p0 = 0, lmin = 0, sigma = 0, my_len = 0;
+  int len[4] = {0, 0, 0, 0};
+  Op qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s] = Op{};
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+
+  auto issue = [&](Half<FMT>& h, int V) {
+    const int p = V >> 1;
+    if ((V & 1) == 0) {
+      int tag = -1, pid = -1;
+      if (!done) {
+        uint32_t k = 0;
+        if (lane == 0) k = atomicAdd(&L.next, 1u);
+        k = uniform(k);
+        if (k < (uint32_t)np) {
+          pid = (int)uniform((uint32_t)L.pid[k]);
+          tag = (int)(k | ((uint32_t)L.ridx[k] << 16));
+          tag = (int)uniform((uint32_t)tag);
+          last = p;
+        } else {
+          done = true;
+        }
+      }
+      if (lane == (p & 63)) {
+        vm_tag = tag;
+        vm_pid = pid;
+      }
+    }
+    const int tag = __builtin_amdgcn_readlane(vm_tag, p & 63);
+    const int pid = __builtin_amdgcn_readlane(vm_pid, p & 63);
+    const bool ok = tag >= 0 && pid >= 0 && pid < a.n_pages;
     const __amdgpu_buffer_rsrc_t rk = page_rsrc(kp, pid, ok, kPageBytes);
     const __amdgpu_buffer_rsrc_t rs = (FMT == IDX_K_NVFP4) ? page_rsrc(ks, pid, ok, kBlock * 8) : rk;
-    load_half<FMT>(h, rk, rs, ua & 1, n, g);
+    load_half<FMT>(h, rk, rs, V & 1, n, g);
   };
 
+  auto compute = [&](const Half<FMT>& h, int U) {
+    const int p = U >> 1;
+    const int tag = __builtin_amdgcn_readlane(vm_tag, p & 63);
+    if (tag < 0) return;
+    const int k = tag & 0xFFFF, j = tag >> 16;
+    if ((U & 1) == 0) {
+      if (j != cur) {  // another request: its context from the round
+        cur = j;
+        const RoundReq& rq = L.req[j];
+        p0 = (int)uniform((uint32_t)rq.p0);
+        lmin = (int)uniform((uint32_t)rq.lmin);
+        sigma = (int)uniform((uint32_t)rq.sigma);
+        const u32x4 lv = *reinterpret_cast<const u32x4*>(&rq.len[4 * g]);
+        len[0] = (int)lv.x; len[1] = (int)lv.y; len[2] = (int)lv.z; len[3] = (int)lv.w;
+        my_len = (n == 0) ? len[0] : (n == 1) ? len[1] : (n == 2) ? len[2] : len[3];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          qf[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(&L.q[j][n][Fmt<FMT>::d0(s, g)]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx[e] = -INFINITY;
+    }
+    const int b = (int)(lo + (uint32_t)k) - p0;
+    const bool full = (b + 1) * kBlock <= lmin;
+    score_half<FMT>(h, qf, full, b * kBlock + 64 * (U & 1) + n, len, mx);
+    if (U & 1) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = row16_max(mx[e]);
+      float o = (n == 0) ? v[0] : (n == 1) ? v[1] : (n == 2) ? v[2] : v[3];
+      if constexpr (FMT == IDX_K_NVFP4) o = ldexpf(o, -sigma);
+      const int pid = __builtin_amdgcn_readlane(vm_pid, p & 63);
+      if (!(pid >= 0 && pid < a.n_pages)) o = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
+      if (writer) L.stage[wrow][k] = o;
+    }
+  };
+
+  // a trip covers an even number of units, so ring slots and halves are static
+  constexpr int kTrip = (kRing % 2) ? 2 * kRing : kRing;
   Half<FMT> ring[kRing];
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u) issue(ring[u], u);
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int u0 = 0; u0 < n_units; u0 += kRing) {
-    // kRing units per trip (even), so ring slots and halves are static
+  for (int U0 = 0;; U0 += kTrip) {
 #pragma unroll
-    for (int k = 0; k < kRing; ++k) {
-      const int u = u0 + k;
-      issue(ring[(k + kRing - 1) % kRing], u + kRing - 1);
-      const int j = u >> 1;
-      const int b = b_s + j;
-      if ((k & 1) == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx[e] = -INFINITY;
-      }
-      const bool full = (b + 1) * kBlock <= lmin;
-      score_half<FMT>(ring[k], qf, full, b * kBlock + 64 * (k & 1) + n, len, mx);
-      if (k & 1) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = row16_max(mx[e]);
-        float o = (n == 0) ? v[0] : (n == 1) ? v[1] : (n == 2) ? v[2] : v[3];
-        if constexpr (FMT == IDX_K_NVFP4) o = ldexpf(o, -sigma);
-        const int pid = __builtin_amdgcn_readlane(pidv, min(j, kTaskPages - 1));
-        if (!(pid >= 0 && pid < a.n_pages)) o = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
-        if (writer && j < cnt) stage[wrow * kTaskPages + j] = o;
-      }
+    for (int k = 0; k < kTrip; ++k) {
+      issue(ring[(k + kRing - 1) % kRing], U0 + k + kRing - 1);
+      compute(ring[k % kRing], U0 + k);
     }
+    if (done && 2 * (last + 1) <= U0 + kTrip) break;  // every held page is computed
   }
-  // write the task's scores: row i, blocks [b_s, b_s + cnt), one lane per block
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  float* out = a.block_scores + (int64_t)r * rows * MB + b_s;
+}
+
+// The round's block scores to their rows (all threads): runs of consecutive
+// blocks per row and request.
+__device__ __forceinline__ void write_round(const StepArgs& a, const RoundLds& L, uint32_t lo, int np, int tid) {
+  const int rows = a.P * a.H, MB = a.max_blocks;
   for (int i = 0; i < rows; ++i)
-    if (lane < cnt) out[(int64_t)i * MB + lane] = stage[i * kTaskPages + lane];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+    for (int k = tid; k < np; k += kThreads) {
+      const RoundReq& rq = L.req[L.ridx[k]];
+      const int b = (int)(lo + (uint32_t)k) - rq.p0;
+      a.block_scores[((int64_t)rq.r * rows + i) * MB + b] = L.stage[i][k];
+    }
 }
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   extern __shared__ uint32_t pre[];  // n_req + 1 prefix sums of per-request block counts
+  __shared__ RoundLds L;
   __shared__ uint32_t wave_tot[kWaves];
-  __shared__ float stage[kWaves][kTileRows * kTaskPages];
-  // Values that are uniform across a wave are passed through readfirstlane so
-  // the compiler keeps them (and the buffer descriptors built from them) in
-  // scalar registers.
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int P = a.P, rows = P * a.H, MB = a.max_blocks, R = a.n_req;
 
-  // 1. blocks each request's group reads (0 for graph pads), prefix sums
+  // 1. pages each request's group reads (0 for graph pads) and their prefix sums
   uint32_t carry = 0;
   for (int base = 0; base < R; base += kThreads) {
     const int r = base + tid;
@@ -364,62 +492,72 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   }
   if (tid == 0) pre[R] = carry;
   __syncthreads();
-  const uint32_t N = __builtin_amdgcn_readfirstlane(carry);
+  const uint32_t N = uniform(carry);
 
-  // 2. -inf past each group's extent, and everywhere for graph pads
-  for (int r = blockIdx.x; r < R; r += gridDim.x) {
-    const int nbg = (int)(__builtin_amdgcn_readfirstlane(pre[r + 1]) -
-                          __builtin_amdgcn_readfirstlane(pre[r]));
-    const int width = MB - nbg;
-    float* base = a.block_scores + (int64_t)r * rows * MB + nbg;
-    for (int e = tid; e < rows * width; e += kThreads) base[(int64_t)(e / width) * MB + e % width] = -INFINITY;
+  // 2. -inf past each group's extent, and everywhere for graph pads: one
+  // output row per workgroup in turn
+  for (int q = blockIdx.x; q < R * rows; q += gridDim.x) {
+    const int r = q / rows;
+    const int nbg = (int)(uniform(pre[r + 1]) - uniform(pre[r]));
+    float* out = a.block_scores + (int64_t)q * MB;
+    for (int c = nbg + tid; c < MB; c += kThreads) out[c] = -INFINITY;
   }
 
-  // 3. this wave's equal share of the N pages, as tasks of one request each
-  const int64_t nw = (int64_t)gridDim.x * kWaves;
-  const int64_t wid = (int64_t)blockIdx.x * kWaves + wave;
-  int64_t pos = wid * N / nw;
-  const int64_t end = (wid + 1) * N / nw;
+  // 3. this workgroup's equal share of the step's pages, in rounds
+  const uint32_t lo = (uint32_t)((uint64_t)blockIdx.x * N / gridDim.x);
+  const uint32_t hi = (uint32_t)((uint64_t)(blockIdx.x + 1) * N / gridDim.x);
   if (a.n_pages == 0) {
     // nothing can be read: every visible block is NaN
-    for (; pos < end; ++pos) {
-      int lo = 0, hi = R;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int64_t)__builtin_amdgcn_readfirstlane(pre[mid]) <= pos) lo = mid; else hi = mid;
+    for (uint32_t u = lo + tid; u < hi; u += kThreads) {
+      int rlo = 0, rhi = R;
+      while (rhi - rlo > 1) {
+        const int mid = (rlo + rhi) >> 1;
+        if (pre[mid] <= u) rlo = mid; else rhi = mid;
       }
-      const int b = (int)(pos - __builtin_amdgcn_readfirstlane(pre[lo]));
-      const int wrow = 4 * g + n;
-      if (n < 4 && wrow < rows) {
-        const int L = clamp_len(a.row_len[lo * P + wrow / a.H], MB);
-        a.block_scores[((int64_t)lo * rows + wrow) * MB + b] = (b * kBlock < L) ? __builtin_nanf("") : -INFINITY;
+      const int b = (int)(u - pre[rlo]);
+      for (int i = 0; i < rows; ++i) {
+        const int L0 = clamp_len(a.row_len[rlo * P + i / a.H], MB);
+        a.block_scores[((int64_t)rlo * rows + i) * MB + b] = (b * kBlock < L0) ? __builtin_nanf("") : -INFINITY;
       }
     }
     return;
   }
-  while (pos < end) {
-    int lo = 0, hi = R;  // the request holding page pos: pre[lo] <= pos < pre[lo + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if ((int64_t)__builtin_amdgcn_readfirstlane(pre[mid]) <= pos) lo = mid; else hi = mid;
+  for (uint32_t rl = lo; rl < hi;) {
+    int r0 = 0, rhi = R;  // pre[r0] <= rl < pre[r0 + 1]
+    while (rhi - r0 > 1) {
+      const int mid = (r0 + rhi) >> 1;
+      if (uniform(pre[mid]) <= rl) r0 = mid; else rhi = mid;
     }
-    const int64_t first = __builtin_amdgcn_readfirstlane(pre[lo]);
-    const int b_s = (int)(pos - first);
-    const int nbg = (int)(__builtin_amdgcn_readfirstlane(pre[lo + 1]) - first);
-    const int cnt = (int)min<int64_t>(min<int64_t>(end - pos, nbg - b_s), kTaskPages);
-    score_task<FMT>(a, lo, b_s, cnt, lane, n, g, stage[wave]);
-    pos += cnt;
+    const int rend = min(R, r0 + kRoundReqs);
+    const uint32_t rh = min(min(hi, rl + (uint32_t)kRoundPages), uniform(pre[rend]));
+    int nreq = 0;
+    while (r0 + nreq < rend && uniform(pre[r0 + nreq]) < rh) ++nreq;
+    const int np = (int)(rh - rl);
+    setup_round<FMT>(a, L, pre, r0, nreq, rl, np, tid);
+    __syncthreads();
+    stream_round<FMT>(a, L, rl, np, lane, n, g);
+    __syncthreads();
+    write_round(a, L, rl, np, tid);
+    __syncthreads();
+    rl = rh;
   }
+  (void)wave;
 }
 
 namespace {
-// workgroups that fit on the device at once for this kernel (cached per device)
+size_t dyn_bytes(int n_req) { return (size_t)(n_req + 1) * sizeof(uint32_t); }
+
+// Workgroups that fit on the device at once (cached per device), with the
+// dynamic LDS limit raised to what the largest request count needs.
 template <int FMT>
-int resident_workgroups(size_t smem) {
+int resident_workgroups() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cache[dev] > 0) return cache[dev];
+  const size_t smem = dyn_bytes(IDX_MAX_REQ);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_kernel<FMT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
@@ -429,24 +567,20 @@ int resident_workgroups(size_t smem) {
   cache[dev] = cus * per_cu;
   return cache[dev];
 }
+
+template <int FMT>
+void launch(const StepArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(score_kernel<FMT>, dim3(resident_workgroups<FMT>()), dim3(kThreads),
+                     dyn_bytes(a.n_req), stream, a);
+}
 }  // namespace
 
 hipError_t launch_score(const StepArgs& a, hipStream_t stream) {
   if (a.n_req == 0 || a.max_blocks == 0) return hipSuccess;
-  const size_t smem = (size_t)(IDX_MAX_REQ + 1) * sizeof(uint32_t);  // sized for the limit
   switch (a.k_format) {
-    case IDX_K_BF16:
-      hipLaunchKernelGGL(score_kernel<IDX_K_BF16>, dim3(resident_workgroups<IDX_K_BF16>(smem)),
-                         dim3(kThreads), smem, stream, a);
-      break;
-    case IDX_K_FP8_E4M3:
-      hipLaunchKernelGGL(score_kernel<IDX_K_FP8_E4M3>, dim3(resident_workgroups<IDX_K_FP8_E4M3>(smem)),
-                         dim3(kThreads), smem, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL(score_kernel<IDX_K_NVFP4>, dim3(resident_workgroups<IDX_K_NVFP4>(smem)),
-                         dim3(kThreads), smem, stream, a);
-      break;
+    case IDX_K_BF16: launch<IDX_K_BF16>(a, stream); break;
+    case IDX_K_FP8_E4M3: launch<IDX_K_FP8_E4M3>(a, stream); break;
+    default: launch<IDX_K_NVFP4>(a, stream); break;
   }
   return hipGetLastError();
 }

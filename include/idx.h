@@ -69,8 +69,6 @@ enum {
 #define IDX_MAX_BLOCKS 8192
 /* Largest n_req (graph pads included) one call accepts. */
 #define IDX_MAX_REQ 8192
-/* Bytes of the scheduling state a scoring call needs (see idx_params.sched). */
-#define IDX_SCHED_BYTES 64
 
 /*
  * Parameters of one indexer step (one layer, all requests of the batch).
@@ -102,13 +100,6 @@ enum {
  *                to the lower id, NaN below every number.
  *   topk_scores  fp32 [R*P][H][topk]: block_scores of each selected id, -inf
  *                padding.
- *   sched        device memory of IDX_SCHED_BYTES bytes, 4-byte aligned, owned
- *                by the caller: the scoring kernel's work counters.  Fill it
- *                with zeros once before its first use; every scoring call that
- *                runs to completion leaves it zero again.  Scoring calls that
- *                share one sched buffer must not run at the same time (issue
- *                them on one stream, or order them); give concurrent calls
- *                buffers of their own.
  */
 typedef struct idx_params {
   int32_t k_format;       /* IDX_K_*                                        */
@@ -133,7 +124,6 @@ typedef struct idx_params {
   float* block_scores;
   int32_t* topk_ids;
   float* topk_scores;
-  uint32_t* sched;        /* scoring only; see above                         */
 } idx_params;
 
 /*
@@ -153,13 +143,13 @@ int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_ro
                   int64_t n_slots, void* stream);
 
 /* Block scores of every (row, head, block) [P1, P2]: reads q, k, k_scale,
- * req_slot, block_table, row_len; writes block_scores (all R*P*H*MB entries);
- * uses sched.  topk_ids / topk_scores may be NULL. */
+ * req_slot, block_table, row_len; writes block_scores (all R*P*H*MB entries).
+ * topk_ids / topk_scores may be NULL. */
 int idx_score_packed(const idx_params* p, void* stream);
 
 /* Forced top-k [P2] over an existing block_scores: reads req_slot, row_len,
- * block_scores; writes topk_ids and topk_scores.  q, k, k_scale, block_table
- * and sched may be NULL. */
+ * block_scores; writes topk_ids and topk_scores.  q, k, k_scale and
+ * block_table may be NULL. */
 int idx_block_topk(const idx_params* p, void* stream);
 
 /* idx_score_packed then idx_block_topk on the same stream. */

@@ -52,13 +52,12 @@ int check(const idx_params* p, int need) {
   if (!p->req_slot || !p->row_len) return fail(IDX_E_NULL, "req_slot and row_len are required");
   if (!p->block_scores) return fail(IDX_E_NULL, "block_scores is required");
   if (need & kScore) {
-    if (!p->q || !p->k || !p->block_table || !p->sched)
-      return fail(IDX_E_NULL, "q, k, block_table and sched are required for scoring");
+    if (!p->q || !p->k || !p->block_table)
+      return fail(IDX_E_NULL, "q, k and block_table are required for scoring");
     if (p->k_format == IDX_K_NVFP4 && !p->k_scale)
       return fail(IDX_E_NULL, "k_scale is required for NVFP4 keys");
     if (!aligned16(p->q) || !aligned16(p->k))
       return fail(IDX_E_ALIGN, "q and k must be 16-byte aligned");
-    if (reinterpret_cast<uintptr_t>(p->sched) & 3u) return fail(IDX_E_ALIGN, "sched must be 4-byte aligned");
     if (p->k_format == IDX_K_NVFP4 && (reinterpret_cast<uintptr_t>(p->k_scale) & 1u))
       return fail(IDX_E_ALIGN, "k_scale must be 2-byte aligned");
   }
@@ -80,7 +79,6 @@ idx::StepArgs args_of(const idx_params* p) {
   a.block_scores = p->block_scores;
   a.topk_ids = p->topk_ids;
   a.topk_scores = p->topk_scores;
-  a.sched = p->sched;
   a.n_pages = p->n_pages;
   a.k_format = p->k_format;
   a.n_req = p->n_req;

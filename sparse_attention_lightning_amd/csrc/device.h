@@ -30,7 +30,6 @@ struct StepArgs {
   float* block_scores;
   int32_t* topk_ids;
   float* topk_scores;
-  uint32_t* sched;  // scoring work counters (caller's, zero between calls)
   int64_t n_pages;
   int32_t k_format;
   int32_t n_req, n_slot_rows, P, H, max_blocks, topk, init_blocks, local_blocks;

@@ -21,7 +21,6 @@ IDX_OK, IDX_E_NULL, IDX_E_FORMAT, IDX_E_SHAPE, IDX_E_PACK = 0, -1, -2, -3, -4
 IDX_E_TOPK, IDX_E_LAUNCH, IDX_E_ALIGN = -5, -6, -7
 IDX_K_BF16, IDX_K_FP8_E4M3, IDX_K_NVFP4 = 0, 1, 2
 IDX_MAX_BLOCKS = 8192
-IDX_SCHED_BYTES = 64
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error")
 
 
@@ -42,7 +41,6 @@ class IdxParams(C.Structure):
         ("q", C.c_void_p), ("k", C.c_void_p), ("k_scale", C.c_void_p),
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
         ("block_scores", C.c_void_p), ("topk_ids", C.c_void_p), ("topk_scores", C.c_void_p),
-        ("sched", C.c_void_p),
     ]
 
 
@@ -113,14 +111,9 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
                 block_scores: torch.Tensor, topk_ids: torch.Tensor | None,
                 topk_scores: torch.Tensor | None, packed_queries: int, gqa: int, topk: int,
                 init_blocks: int, local_blocks: int, max_blocks: int | None = None,
-                n_slot_rows: int | None = None, n_pages: int | None = None,
-                sched: torch.Tensor | None = None) -> IdxParams:
+                n_slot_rows: int | None = None, n_pages: int | None = None) -> IdxParams:
     """Build the parameter block from tensors (sizes read from their shapes
-    unless given).  ``sched`` is the scoring kernel's work-counter buffer
-    (int32, >= IDX_SCHED_BYTES bytes, zero when first used); by default a
-    zeroed one is allocated for this parameter block, which is then not to be
-    used by two scoring calls at the same time.  The returned object keeps
-    the tensors alive."""
+    unless given).  The returned object keeps the tensors alive."""
     if k_format not in _K_DTYPES:
         raise ValueError(f"unknown k_format {k_format}")
     p = IdxParams()
@@ -141,11 +134,6 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
     p.block_scores = _dev(block_scores, "block_scores", (torch.float32,))
     p.topk_ids = _dev(topk_ids, "topk_ids", (torch.int32,), optional=True)
     p.topk_scores = _dev(topk_scores, "topk_scores", (torch.float32,), optional=True)
-    if sched is None:
-        sched = torch.zeros(IDX_SCHED_BYTES // 4, dtype=torch.int32, device=block_scores.device)
-    p.sched = _dev(sched, "sched", (torch.int32,))
-    if sched.numel() * 4 < IDX_SCHED_BYTES:
-        raise ValueError(f"sched must hold at least {IDX_SCHED_BYTES} bytes")
     p.n_req = req_slot.numel()
     if max_blocks is None:
         max_blocks = block_table.shape[-1] if block_table is not None else (
@@ -173,8 +161,7 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
     for t, n in ((topk_ids, "topk_ids"), (topk_scores, "topk_scores")):
         if t is not None and t.numel() < rows * topk:
             raise ValueError(f"{n} is smaller than n_req * P * H * topk")
-    p._keep = (q, k, k_scale, req_slot, block_table, row_len, block_scores, topk_ids, topk_scores,
-               sched)
+    p._keep = (q, k, k_scale, req_slot, block_table, row_len, block_scores, topk_ids, topk_scores)
     return p
 
 

@@ -42,7 +42,7 @@ def good_params() -> I.IdxParams:
     p.packed_queries, p.gqa, p.head_dim, p.block_size = 4, 4, 128, 128
     p.max_blocks, p.topk, p.init_blocks, p.local_blocks, p.n_pages = 16, 8, 1, 2, 64
     for i, f in enumerate(["q", "k", "k_scale", "req_slot", "block_table", "row_len",
-                           "block_scores", "topk_ids", "topk_scores", "sched"]):
+                           "block_scores", "topk_ids", "topk_scores"]):
         setattr(p, f, 0x100000 * (i + 1))
     return p
 
@@ -72,8 +72,6 @@ REFUSALS = [
     ("block_scores", None, I.IDX_E_NULL),
     ("topk_ids", None, I.IDX_E_NULL),
     ("topk_scores", None, I.IDX_E_NULL),
-    ("sched", None, I.IDX_E_NULL),
-    ("sched", 0xA00002, I.IDX_E_ALIGN),
     ("q", 0x100008, I.IDX_E_ALIGN),
     ("k", 0x100004, I.IDX_E_ALIGN),
 ]

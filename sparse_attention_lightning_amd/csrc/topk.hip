@@ -7,18 +7,20 @@
 // highest block scores, ties to the lower block id.  Selection is exact.
 //
 // One workgroup of 256 threads per (row, head).  Thread t owns the contiguous
-// blocks [t*C, t*C + C), C = ceil(max_blocks / 256) <= 16 or 32 (rounded up to a
-// multiple of 4 when rows are 16-byte aligned), and loads their scores into
-// registers first thing; the row's slot and length are fetched before them
-// and the score loads do not wait for them.  Keys are 32-bit integers whose unsigned order is the selection
-// order: NaN below every number, -0 equal to +0.  A radix select over the
-// non-forced keys finds the k-th largest key T, k = topk - |forced|: it starts
-// at the highest bit where the row's keys differ, takes up to 8 bits a pass
-// (per-wave LDS histograms, summed per bin), and stops early once the chosen
-// bin holds exactly the keys still needed.  One packed scan of
-// (taken-for-sure, equal-to-T) counts then gives every thread its output
-// position, so ids leave in ascending order without a sort.  Scans and
-// reductions inside a wave use DPP; waves meet through LDS.
+// blocks [t*C, t*C + C), C = ceil(max_blocks / 256) <= 16 or 32 (rounded up to
+// a multiple of 4 when rows are 16-byte aligned), and loads their scores into
+// registers first thing; the row's slot and length are fetched before them and
+// the score loads do not wait for them.  Keys are 32-bit integers whose
+// unsigned order is the selection order: NaN below every number, -0 equal to
+// +0; each thread computes its keys once and marks its competing and forced
+// blocks in two bit masks.  A radix select over the competing keys finds the
+// k-th largest key T, k = topk - |forced|: it starts at the highest bit where
+// those keys differ, takes up to 12 bits a pass into a 4,096-bin LDS histogram
+// (thread t scans and clears 16 bins), and stops once the chosen bin holds
+// exactly the keys still needed.  One packed scan of (taken-for-sure,
+// equal-to-T) counts then gives every thread its output positions, so ids
+// leave in ascending order without a sort.  Reductions and scans inside a
+// wave use DPP; waves meet through LDS.
 #include "device.h"
 
 namespace idx {
@@ -68,10 +70,34 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot, u
   return before + incl - v;
 }
 
+// Within each row of 16 lanes every lane gets the row's min / max / sum
+// (quad_perm and row_ror patterns keep every lane's source valid).
+template <int OP>
+__device__ __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
+  return OP == 0 ? min(a, b) : OP == 1 ? max(a, b) : a + b;
+}
+template <int OP>
+__device__ __forceinline__ uint32_t row16_reduce(uint32_t x) {
+  x = combine<OP>(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = combine<OP>(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = combine<OP>(x, dpp_u32<0x124>(x));  // row_ror:4
+  x = combine<OP>(x, dpp_u32<0x128>(x));  // row_ror:8
+  return x;
+}
+
+// Whole-wave reduction (0 min, 1 max, 2 sum), returned wave-uniform.
+template <int OP>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
+  x = row16_reduce<OP>(x);
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return combine<OP>(combine<OP>(a, b), combine<OP>(c, d));
+}
+
 // PER: blocks per thread (16 covers max_blocks <= 4096, 32 the full limit).
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
-  constexpr int kPerThread = PER;
+  static_assert(PER <= 32, "per-thread block sets are 32-bit masks");
   constexpr int kBins = 4096, kBinsPerThread = kBins / kTopkThreads;  // 16
   __shared__ u32x4 hist4[kBins / 4];
   uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
@@ -94,20 +120,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
 
   // this thread's scores (they do not wait for the length); 16-byte loads
   // when every thread's range starts 16-byte aligned
-  const int C = (MB % 4 == 0) ? ((MB / 4 + kTopkThreads - 1) / kTopkThreads) * 4
-                              : (MB + kTopkThreads - 1) / kTopkThreads;
+  const bool vec = (MB % 4) == 0 && (reinterpret_cast<uintptr_t>(a.block_scores) & 15u) == 0;
+  const int C = vec ? ((MB / 4 + kTopkThreads - 1) / kTopkThreads) * 4 : (MB + kTopkThreads - 1) / kTopkThreads;
   const int b0 = tid * C;
-  float sv[kPerThread];
-  if (MB % 4 == 0) {
+  float sv[PER];
+  if (vec) {
 #pragma unroll
-    for (int q = 0; q < kPerThread / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       f32x4 v = (4 * q < C && b0 + 4 * q < MB) ? *reinterpret_cast<const f32x4*>(bs + b0 + 4 * q)
                                                : f32x4{0.f, 0.f, 0.f, 0.f};
       sv[4 * q] = v[0]; sv[4 * q + 1] = v[1]; sv[4 * q + 2] = v[2]; sv[4 * q + 3] = v[3];
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
+    for (int j = 0; j < PER; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
   }
 
   // this thread's 16 bins, highest digits first: bins [kBins - 16(t+1), kBins - 16 t)
@@ -128,28 +154,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     return;
   }
 
+  // keys once; bit j of `cand` marks a block that competes, of `forced` one
+  // that is always taken
   const int cnt = max(0, min(C, nb - b0));
   const int init = a.init_blocks, local_from = nb - a.local_blocks;
-  // keys are recomputed from the scores where needed (fewer live registers)
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nforced = 0;
+  uint32_t key[PER];
+  uint32_t cand = 0, forced = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < PER; ++j) {
     const int b = b0 + j;
-    const bool forced = b < init || b >= local_from;
-    const uint32_t k = order_key(sv[j]);
-    if (j < cnt && !forced) {
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
+    const bool is_forced = b < init || b >= local_from;
+    key[j] = order_key(sv[j]);
+    if (j < cnt) {
+      if (is_forced) {
+        forced |= 1u << j;
+      } else {
+        cand |= 1u << j;
+        kmin = min(kmin, key[j]);
+        kmax = max(kmax, key[j]);
+      }
     }
-    nforced += (j < cnt && forced) ? 1u : 0u;
   }
-  // one combined reduction: min, max, forced count
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
-    nforced += (uint32_t)__shfl_xor((int)nforced, d);
-  }
+  kmin = wave_reduce<0>(kmin);
+  kmax = wave_reduce<1>(kmax);
+  const uint32_t nforced = wave_reduce<2>((uint32_t)__builtin_popcount(forced));
   if (lane == 0) {
     red[0][wave] = kmin;
     red[1][wave] = kmax;
@@ -164,7 +192,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     F += red[2][w];
   }
 
-  // radix select of the want-th largest non-forced key
+  // radix select of the want-th largest competing key
   uint32_t want = (uint32_t)K - F;  // the free slots (F <= init + local <= K)
   uint32_t prefix = kmin, tshift = 0;
   if (want > 0 && kmin != kmax) {
@@ -174,33 +202,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
       const int lo = max(hi - 11, 0);
       const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
 #pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int b = b0 + j;
-        const bool forced = b < init || b >= local_from;
-        const uint32_t k = order_key(sv[j]);
-        const bool match = (hi == 31) || ((k >> (hi + 1)) == (prefix >> (hi + 1)));
-        if (j < cnt && !forced && match) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+      for (int j = 0; j < PER; ++j) {
+        const bool match = (hi == 31) || ((key[j] >> (hi + 1)) == (prefix >> (hi + 1)));
+        if (((cand >> j) & 1u) && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1u);
       }
       __syncthreads();
-      // sum and clear this thread's 16 bins (descending digits)
-      uint32_t local = 0;
+      // this thread's 16 bins (descending digits) into registers, then clear them
+      uint32_t h[kBinsPerThread];
 #pragma unroll
       for (int q = 0; q < kBinsPerThread / 4; ++q) {
         const u32x4 v = hist4[bin0 / 4 + q];
-        local += v[0] + v[1] + v[2] + v[3];
+        h[4 * q] = v[0]; h[4 * q + 1] = v[1]; h[4 * q + 2] = v[2]; h[4 * q + 3] = v[3];
       }
+      uint32_t local = 0;
+#pragma unroll
+      for (int q = 0; q < kBinsPerThread; ++q) local += h[q];
       uint32_t tot;
-      uint32_t above = block_scan(local, wave_tot[0], &tot);
+      const uint32_t above = block_scan(local, wave_tot[0], &tot);
       if (above < want && want <= above + local) {
         // the cut is in this thread's bins: walk them from the highest digit
+        uint32_t run = above;
+#pragma unroll
         for (int q = kBinsPerThread - 1; q >= 0; --q) {
-          const uint32_t hq = hist[bin0 + q];
-          if (above < want && want <= above + hq) {
+          if (run < want && want <= run + h[q]) {
             pick_digit = (uint32_t)(bin0 + q);
-            pick_above = above;
-            pick_count = hq;
+            pick_above = run;
+            pick_count = h[q];
           }
-          above += hq;
+          run += h[q];
         }
       }
 #pragma unroll
@@ -215,38 +244,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   }
   const uint32_t T = prefix >> tshift;
 
-  // positions: forced and > T are taken; of the keys == T, the `want` lowest ids
-  uint32_t sure = 0, eq = 0;
+  // taken: forced, competing keys above T, and of the keys equal to T the
+  // `want` with the lowest ids
+  uint32_t sure = forced, eq = 0;
+  if (want > 0) {
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int b = b0 + j;
-    const bool forced = b < init || b >= local_from;
-    const uint32_t kt = order_key(sv[j]) >> tshift;
-    if (j < cnt) {
-      sure += (forced || (want > 0 && kt > T)) ? 1u : 0u;
-      eq += (!forced && want > 0 && kt == T) ? 1u : 0u;
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t kt = key[j] >> tshift;
+      if ((cand >> j) & 1u) {
+        if (kt > T) sure |= 1u << j;
+        else if (kt == T) eq |= 1u << j;
+      }
     }
   }
   uint32_t total;
-  const uint32_t ex = block_scan((sure << 16) | eq, wave_tot[1], &total);
-  uint32_t eq_rank = ex & 0xFFFFu;
-  uint32_t pos = (ex >> 16) + min(eq_rank, want);
+  const uint32_t packed = ((uint32_t)__builtin_popcount(sure) << 16) | (uint32_t)__builtin_popcount(eq);
+  const uint32_t ex = block_scan(packed, wave_tot[1], &total);
+  // equal keys taken by lower threads, and how many are left for this one
+  // (no conditional subtraction here: hipcc's optimizer turned the form
+  // `want > x ? min(n, want - x) : 0` into one that dropped the min below)
+  const uint32_t eq_taken_before = min(ex & 0xFFFFu, want);
+  uint32_t take_eq = min((uint32_t)__builtin_popcount(eq), want - eq_taken_before);
+  uint32_t taken = sure;
+  for (uint32_t e = eq; take_eq > 0; --take_eq) {  // the lowest take_eq equal keys
+    const uint32_t low = e & (0u - e);
+    taken |= low;
+    e ^= low;
+  }
+  uint32_t pos = (ex >> 16) + eq_taken_before;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int b = b0 + j;
-    const bool forced = b < init || b >= local_from;
-    const uint32_t kt = order_key(sv[j]) >> tshift;
-    if (j < cnt) {
-      bool take = forced || (want > 0 && kt > T);
-      if (!forced && want > 0 && kt == T) {
-        take = eq_rank < want;
-        ++eq_rank;
-      }
-      if (take && pos < (uint32_t)K) {
-        ids[pos] = b;
+  for (int j = 0; j < PER; ++j) {
+    if ((taken >> j) & 1u) {
+      if (pos < (uint32_t)K) {
+        ids[pos] = b0 + j;
         sc[pos] = sv[j];
       }
-      pos += take ? 1u : 0u;
+      ++pos;
     }
   }
 }

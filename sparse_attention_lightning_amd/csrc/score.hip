@@ -67,7 +67,7 @@ namespace idx {
 #endif
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRoundPages = 1024;  // pages a workgroup stages at once
+constexpr int kRoundPages = 768;   // pages a workgroup stages at once
 constexpr int kRoundReqs = 8;      // requests a round may touch
 constexpr int kQStride = 136;      // 16-bit values per query row in LDS (272 B: rows change banks)
 
@@ -257,14 +257,17 @@ struct RoundLds {
   uint32_t next;                                  // pages handed out
 };
 static_assert(offsetof(RoundLds, q) % 16 == 0 && offsetof(RoundLds, req) % 16 == 0, "16-byte LDS rows");
+// with the per-request arrays for the largest request count, one workgroup
+// still fits in the 160 KB of LDS of a CU
+static_assert(sizeof(RoundLds) + 64 + (2 * IDX_MAX_REQ + 1) * 4 <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Fill the round's LDS (all threads; one barrier inside).  Pages [lo, lo + np)
 // of the step belong to requests r0 .. r0 + nreq - 1.
 template <int FMT>
-__device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre, int r0, int nreq,
-                            uint32_t lo, int np, int tid) {
+__device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre, const int32_t* slot_of, int r0,
+                            int nreq, uint32_t lo, int np, int tid) {
   const int P = a.P, H = a.H, rows = P * H, MB = a.max_blocks;
   if (tid < nreq) {
     const int r = r0 + tid;
@@ -287,7 +290,7 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     int j = 0;
     while (j + 1 < nreq && pre[r0 + j + 1] <= u) ++j;
     const int r = r0 + j;
-    const int slot = a.req_slot[r];  // a request with pages is no graph pad
+    const int slot = slot_of[r];  // a request with pages is no graph pad
     L.pid[k] = a.block_table[(int64_t)slot * MB + (int)(u - pre[r])];
     L.ridx[k] = (uint8_t)j;
   }
@@ -464,21 +467,24 @@ __device__ __forceinline__ void write_round(const StepArgs& a, const RoundLds& L
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
-  extern __shared__ uint32_t pre[];  // n_req + 1 prefix sums of per-request block counts
+  extern __shared__ uint32_t pre[];  // n_req + 1 prefix sums of per-request block counts, then n_req slots
   __shared__ RoundLds L;
   __shared__ uint32_t wave_tot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int P = a.P, rows = P * a.H, MB = a.max_blocks, R = a.n_req;
+  int32_t* slot_of = reinterpret_cast<int32_t*>(pre + R + 1);
 
-  // 1. pages each request's group reads (0 for graph pads) and their prefix sums
+  // 1. pages each request's group reads (0 for graph pads) and their prefix
+  // sums; the slots stay in LDS for the rounds
   uint32_t carry = 0;
   for (int base = 0; base < R; base += kThreads) {
     const int r = base + tid;
     uint32_t nbg = 0;
     if (r < R) {
       const int slot = a.req_slot[r];
+      slot_of[r] = slot;
       if (slot >= 0 && slot < a.n_slot_rows) {
         int lmax = 0;
         for (int j = 0; j < P; ++j) lmax = max(lmax, clamp_len(a.row_len[r * P + j], MB));
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
     int nreq = 0;
     while (r0 + nreq < rend && uniform(pre[r0 + nreq]) < rh) ++nreq;
     const int np = (int)(rh - rl);
-    setup_round<FMT>(a, L, pre, r0, nreq, rl, np, tid);
+    setup_round<FMT>(a, L, pre, slot_of, r0, nreq, rl, np, tid);
     __syncthreads();
     stream_round<FMT>(a, L, rl, np, lane, n, g);
     __syncthreads();
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
 }
 
 namespace {
-size_t dyn_bytes(int n_req) { return (size_t)(n_req + 1) * sizeof(uint32_t); }
+size_t dyn_bytes(int n_req) { return (size_t)(2 * n_req + 1) * sizeof(uint32_t); }
 
 // Workgroups that fit on the device at once (cached per device), with the
 // dynamic LDS limit raised to what the largest request count needs.

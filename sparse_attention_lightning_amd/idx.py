@@ -21,6 +21,7 @@ IDX_OK, IDX_E_NULL, IDX_E_FORMAT, IDX_E_SHAPE, IDX_E_PACK = 0, -1, -2, -3, -4
 IDX_E_TOPK, IDX_E_LAUNCH, IDX_E_ALIGN = -5, -6, -7
 IDX_K_BF16, IDX_K_FP8_E4M3, IDX_K_NVFP4 = 0, 1, 2
 IDX_MAX_BLOCKS = 8192
+IDX_MAX_REQ = 8192
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error")
 
 

@@ -128,3 +128,13 @@ def test_fp4_store_refusals(lib, case):
 
 def test_fp4_store_empty_is_ok(lib):
     assert lib.idx_fp4_store(None, 0, 128, None, None, None, 0, None) == I.IDX_OK
+
+
+def test_binding_constants_match_header():
+    text = (ROOT / "include" / "idx.h").read_text()
+    for name in ("IDX_MAX_BLOCKS", "IDX_MAX_REQ"):
+        m = re.search(rf"#define\s+{name}\s+(\d+)", text)
+        assert m and int(m.group(1)) == getattr(I, name), name
+    enums = dict((k, int(v)) for k, v in re.findall(r"(IDX_\w+)\s*=\s*(-?\d+)", text))
+    for k, v in enums.items():
+        assert getattr(I, k) == v, k

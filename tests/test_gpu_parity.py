@@ -301,6 +301,40 @@ def test_repeat_launches_identical():
 
 
 # ---------------------------------------------------------------------------
+# many requests: a workgroup's share spans several rounds (a round touches at
+# most 8 requests), up to the request-count limit
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R,maxlen,fmt", [(2000, 1000, W.K_FP8_E4M3), (I.IDX_MAX_REQ - 2, 300, W.K_BF16)],
+                         ids=["2000req", "max_req"])
+def test_many_requests(oracle, R, maxlen, fmt):
+    say("many requests", R, maxlen, fmt)
+    rng = np.random.default_rng(R)
+    lens = rng.integers(1, maxlen + 1, size=R)
+    w = W.make(name="many", R=R, P=1, H=1, k_format=fmt, req_len=lens, topk=3, init_blocks=1,
+               local_blocks=1, seed=R, pads=2, pad_len=maxlen, device="cuda")
+    assert w.n_req <= I.IDX_MAX_REQ
+    a = w.oracle_args()
+    g = Hn.gpu_step(w)
+    o = oracle.step(**a)
+    Hn.assert_parity(g, o, a)
+
+
+def test_shares_longer_than_a_round(oracle):
+    """More than 768 pages per workgroup: a share runs as several rounds."""
+    R, L = 50, 4000 * 128
+    say("long shares", R, L)
+    w = W.make(name="long", R=R, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=np.full(R, L - 3),
+               topk=64, init_blocks=1, local_blocks=2, seed=77, device="cuda")
+    assert w.pool_pages_used() > 256 * 768
+    a = w.oracle_args()
+    g = Hn.gpu_step(w)
+    sample = [0, 24, 49]
+    sub = Hn.subset_args(a, sample, 4, 4)
+    o = oracle.step(**sub)
+    Hn.assert_parity({k: v[Hn.rows_of(sample, 16)] for k, v in g.items()}, o, sub)
+
+
+# ---------------------------------------------------------------------------
 # the five workloads at full size, in the benchmark's launch configuration
 # ---------------------------------------------------------------------------
 def _full(oracle, idx, sample, local_blocks=None):

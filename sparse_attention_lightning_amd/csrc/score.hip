@@ -59,8 +59,14 @@
 namespace idx {
 
 // Tuning knobs (compile-time; none of them changes what is computed).
-#ifndef IDX_SCORE_RING
-#define IDX_SCORE_RING 0         // half-page buffers per wave (0: per-format default)
+#ifndef IDX_SCORE_RING_BF16
+#define IDX_SCORE_RING_BF16 2    // half-page register buffers per wave, bf16 K (16 KB a wave each)
+#endif
+#ifndef IDX_SCORE_RING_FP8
+#define IDX_SCORE_RING_FP8 4     // fp8 K (8 KB a wave each)
+#endif
+#ifndef IDX_SCORE_RING_FP4
+#define IDX_SCORE_RING_FP4 4     // NVFP4 K (4.5 KB a wave each, with scales)
 #endif
 #ifndef IDX_SCORE_NT
 #define IDX_SCORE_NT 0           // 1: non-temporal (streaming) K loads
@@ -76,8 +82,7 @@ struct Fmt;
 
 template <>
 struct Fmt<IDX_K_BF16> {
-  // half pages in flight per wave (registers bound it: a bf16 half is 16 KB a wave)
-  static constexpr int kRing = IDX_SCORE_RING ? IDX_SCORE_RING : 2;
+  static constexpr int kRing = IDX_SCORE_RING_BF16;
   static constexpr int kRowBytes = 256;
   static constexpr int kLoads = 4;  // 16-byte loads per lane per tile
   typedef bf16x8 Op;
@@ -87,8 +92,7 @@ struct Fmt<IDX_K_BF16> {
 
 template <>
 struct Fmt<IDX_K_FP8_E4M3> {
-  // half pages in flight per wave (registers bound it: a bf16 half is 16 KB a wave)
-  static constexpr int kRing = IDX_SCORE_RING ? IDX_SCORE_RING : 4;
+  static constexpr int kRing = IDX_SCORE_RING_FP8;
   static constexpr int kRowBytes = 128;
   static constexpr int kLoads = 2;
   typedef bf16x8 Op;
@@ -98,8 +102,7 @@ struct Fmt<IDX_K_FP8_E4M3> {
 
 template <>
 struct Fmt<IDX_K_NVFP4> {
-  // half pages in flight per wave (registers bound it: a bf16 half is 16 KB a wave)
-  static constexpr int kRing = IDX_SCORE_RING ? IDX_SCORE_RING : 4;
+  static constexpr int kRing = IDX_SCORE_RING_FP4;
   static constexpr int kRowBytes = 64;
   static constexpr int kLoads = 1;
   typedef f16x8 Op;

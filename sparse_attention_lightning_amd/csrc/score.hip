@@ -9,23 +9,21 @@
 //
 // Work split.  One workgroup of eight waves per CU stays resident for the
 // whole launch.  The pages of the step, in (request, block) order, are cut
-// into chunks that never cross a request: 32 pages, so that a row's scores of
-// a chunk fill one 128-byte line, except in the last twentieth of the step,
-// where chunks have 8 pages so that the launch ends evenly.  Workgroups take
-// chunks from a counter in the caller's scheduling state (the first two per
-// workgroup are fixed, so the launch does not open with every workgroup on
-// the counter), and waves take single pages from their workgroup's chunks
-// through LDS.  Both levels are dynamic because shares of the memory system
-// are not even: the two waves of a SIMD do not get equal shares of its
-// memory pipeline (the older runs about twice as fast) and CUs do not get
-// equal shares of HBM, so with fixed slices a launch lasts as long as its
-// slowest wave.  The workgroup that finishes last returns the counter to
-// zero for the next launch.
-//
-// A chunk's LDS slot holds its page ids, the request's query tile and row
-// lengths (copied in by the wave that fetched the chunk, so a change of
-// request costs a wave LDS reads only) and the chunk's block scores; the
-// wave that completes the chunk's last page writes its rows out.
+// into equal contiguous shares, one per workgroup, and a workgroup takes its
+// share in rounds of at most 768 pages touching at most 8 requests.  A round
+// first stages its page ids, the query tiles and row lengths of its requests
+// in LDS; the eight waves then take pages one at a time from an LDS counter,
+// so a wave that is served faster by the memory system simply takes more
+// pages (the two waves of a SIMD do not get equal shares of its memory
+// pipeline: the older one runs about twice as fast).  Pages are handed out in
+// order of their place in the pool (a counting sort of the round's page ids
+// into 256 equal buckets of the pool): every workgroup's share is spread over
+// the whole pool, so all workgroups then sweep it from its low pages to its
+// high ones together, which the memory system serves faster than the same
+// pages in random order.  Each page's 16 row
+// maxima go to an LDS stage, and after a barrier the whole workgroup writes
+// the round's block scores out as runs of consecutive blocks per row, so the
+// output leaves in whole 128-byte lines.
 //
 // Each wave streams its pages as 64-token halves through a ring of register
 // buffers, keeping RING - 1 halves in flight while the matrix cores work on
@@ -70,6 +68,15 @@ namespace idx {
 #endif
 #ifndef IDX_SCORE_NT
 #define IDX_SCORE_NT 0           // 1: non-temporal (streaming) K loads
+#endif
+#ifndef IDX_SCORE_SORT_BUCKETS
+#define IDX_SCORE_SORT_BUCKETS 256  // page-id buckets of the pool for the hand-out order (0: round order)
+#endif
+#ifndef IDX_SCORE_SORT_MIN
+#define IDX_SCORE_SORT_MIN 64       // rounds with fewer pages keep round order
+#endif
+#ifndef IDX_SCORE_NT_OUT
+#define IDX_SCORE_NT_OUT 0       // 1: non-temporal block-score stores
 #endif
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -252,17 +259,21 @@ struct RoundReq {
 
 struct RoundLds {
   float stage[kTileRows][kRoundPages];            // block scores of the round
-  int32_t pid[kRoundPages];                       // page ids
-  uint8_t ridx[kRoundPages];                      // each page's request within the round
+  int32_t pid[kRoundPages];                       // page ids, in hand-out order
+  uint16_t sk[kRoundPages];                       // in hand-out order: round page | request in the round << 10
+  uint8_t ridx[kRoundPages];                      // each round page's request within the round
   uint16_t q[kRoundReqs][kTileRows][kQStride];    // query tiles (bf16, or f16 scaled by 2^sigma)
   RoundReq req[kRoundReqs];
   uint32_t amax[kRoundReqs];                      // NVFP4: largest |q| of each tile (float bits)
   uint32_t next;                                  // pages handed out
+  uint32_t wave_tot[kWaves];                      // scan scratch
 };
 static_assert(offsetof(RoundLds, q) % 16 == 0 && offsetof(RoundLds, req) % 16 == 0, "16-byte LDS rows");
 // with the per-request arrays for the largest request count, one workgroup
 // still fits in the 160 KB of LDS of a CU
 static_assert(sizeof(RoundLds) + 64 + (2 * IDX_MAX_REQ + 1) * 4 <= 160 * 1024, "LDS budget");
+static_assert(kRoundPages <= 2 * kThreads && kRoundPages <= 1024 && kRoundReqs <= 8, "round page fields");
+static_assert(IDX_SCORE_SORT_BUCKETS <= kTileRows * kRoundPages, "the bucket histogram fits the stage");
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -288,14 +299,69 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     const int j = tid / kTileRows, i = tid % kTileRows;
     L.req[j].len[i] = (i < rows) ? clamp_len(a.row_len[(r0 + j) * P + i / H], MB) : 0;
   }
-  for (int k = tid; k < np; k += kThreads) {
-    const uint32_t u = lo + (uint32_t)k;
-    int j = 0;
-    while (j + 1 < nreq && pre[r0 + j + 1] <= u) ++j;
-    const int r = r0 + j;
-    const int slot = slot_of[r];  // a request with pages is no graph pad
-    L.pid[k] = a.block_table[(int64_t)slot * MB + (int)(u - pre[r])];
-    L.ridx[k] = (uint8_t)j;
+  int pk[2], jk[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int k = tid + kThreads * m;
+    pk[m] = -1;
+    jk[m] = 0;
+    if (k < np) {
+      const uint32_t u = lo + (uint32_t)k;
+      int j = 0;
+      while (j + 1 < nreq && pre[r0 + j + 1] <= u) ++j;
+      const int r = r0 + j;
+      const int slot = slot_of[r];  // a request with pages is no graph pad
+      pk[m] = a.block_table[(int64_t)slot * MB + (int)(u - pre[r])];
+      jk[m] = j;
+      L.ridx[k] = (uint8_t)j;
+    }
+  }
+  int pos[2] = {tid, tid + kThreads};  // hand-out position of each page
+#if IDX_SCORE_SORT_BUCKETS > 0
+  if (np >= IDX_SCORE_SORT_MIN) {
+    // by page id: a counting sort into NB equal buckets of the pool, so that
+    // all workgroups sweep the pool from its low pages to its high ones
+    // together
+    constexpr int NB = IDX_SCORE_SORT_BUCKETS;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(&L.stage[0][0]);
+    for (int b = tid; b < NB; b += kThreads) hist[b] = 0;
+    __syncthreads();
+    int bk[2];
+    uint32_t rank[2] = {0, 0};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int k = tid + kThreads * m;
+      const int pid = pk[m];
+      bk[m] = (pid >= 0 && pid < a.n_pages) ? (int)((uint64_t)pid * NB / (uint64_t)a.n_pages) : NB - 1;
+      if (k < np) rank[m] = atomicAdd(&hist[bk[m]], 1u);
+    }
+    __syncthreads();
+    constexpr int PER = (NB + kThreads - 1) / kThreads;  // bins a thread scans
+    uint32_t h[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      h[i] = (PER * tid + i < NB) ? hist[PER * tid + i] : 0u;
+      sum += h[i];
+    }
+    uint32_t tot;
+    uint32_t start = block_exclusive_scan<kThreads>(sum, L.wave_tot, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (PER * tid + i < NB) hist[PER * tid + i] = start;
+      start += h[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) pos[m] = (int)(hist[bk[m]] + rank[m]);
+  }
+#endif
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int k = tid + kThreads * m;
+    if (k < np) {
+      L.pid[pos[m]] = pk[m];
+      L.sk[pos[m]] = (uint16_t)(k | (jk[m] << 10));
+    }
   }
   // query tiles: piece e = (request j, row, group of 8 values); 4 per thread
   u32x4 pc[4];
@@ -384,8 +450,8 @@ __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uin
         k = uniform(k);
         if (k < (uint32_t)np) {
           pid = (int)uniform((uint32_t)L.pid[k]);
-          tag = (int)(k | ((uint32_t)L.ridx[k] << 16));
-          tag = (int)uniform((uint32_t)tag);
+          const uint32_t skv = uniform((uint32_t)L.sk[k]);
+          tag = (int)((skv & 1023u) | ((skv >> 10) << 16));
           last = p;
         } else {
           done = true;
@@ -464,8 +530,27 @@ __device__ __forceinline__ void write_round(const StepArgs& a, const RoundLds& L
     for (int k = tid; k < np; k += kThreads) {
       const RoundReq& rq = L.req[L.ridx[k]];
       const int b = (int)(lo + (uint32_t)k) - rq.p0;
+#if IDX_SCORE_NT_OUT
+      __builtin_nontemporal_store(L.stage[i][k], &a.block_scores[((int64_t)rq.r * rows + i) * MB + b]);
+#else
       a.block_scores[((int64_t)rq.r * rows + i) * MB + b] = L.stage[i][k];
+#endif
     }
+}
+
+// The request holding step page x: the largest r < R with pre[r] <= x, in
+// every lane of the wave (pre[0] = 0 <= x).  Each pass checks 64 evenly
+// spaced candidates with one LDS read per lane.
+__device__ __forceinline__ int request_of(const uint32_t* pre, int R, uint32_t x, int lane) {
+  int lo = 0, hi = R;  // the answer lies in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) >> 6;
+    const int r = lo + step * lane;
+    const int below = __popcll(__ballot(r < hi && pre[min(r, R)] <= x));  // a prefix of the lanes, lane 0 included
+    lo += step * (below - 1);
+    hi = min(hi, lo + step);
+  }
+  return lo;
 }
 
 template <int FMT>
@@ -487,12 +572,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
     uint32_t nbg = 0;
     if (r < R) {
       const int slot = a.req_slot[r];
+      int lmax = 0;  // loaded without waiting for the slot
+      for (int j = 0; j < P; ++j) lmax = max(lmax, clamp_len(a.row_len[r * P + j], MB));
       slot_of[r] = slot;
-      if (slot >= 0 && slot < a.n_slot_rows) {
-        int lmax = 0;
-        for (int j = 0; j < P; ++j) lmax = max(lmax, clamp_len(a.row_len[r * P + j], MB));
-        nbg = (uint32_t)blocks_of(lmax);
-      }
+      if (slot >= 0 && slot < a.n_slot_rows) nbg = (uint32_t)blocks_of(lmax);
     }
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan<kThreads>(nbg, wave_tot, &tot);
@@ -503,16 +586,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   __syncthreads();
   const uint32_t N = uniform(carry);
 
-  // 2. -inf past each group's extent, and everywhere for graph pads: one
-  // output row per workgroup in turn
-  for (int q = blockIdx.x; q < R * rows; q += gridDim.x) {
-    const int r = q / rows;
-    const int nbg = (int)(uniform(pre[r + 1]) - uniform(pre[r]));
-    float* out = a.block_scores + (int64_t)q * MB;
-    for (int c = nbg + tid; c < MB; c += kThreads) out[c] = -INFINITY;
-  }
-
-  // 3. this workgroup's equal share of the step's pages, in rounds
+  // 2. this workgroup's equal share of the step's pages, in rounds
   const uint32_t lo = (uint32_t)((uint64_t)blockIdx.x * N / gridDim.x);
   const uint32_t hi = (uint32_t)((uint64_t)(blockIdx.x + 1) * N / gridDim.x);
   if (a.n_pages == 0) {
@@ -529,26 +603,33 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
         a.block_scores[((int64_t)rlo * rows + i) * MB + b] = (b * kBlock < L0) ? __builtin_nanf("") : -INFINITY;
       }
     }
-    return;
-  }
-  for (uint32_t rl = lo; rl < hi;) {
-    int r0 = 0, rhi = R;  // pre[r0] <= rl < pre[r0 + 1]
-    while (rhi - r0 > 1) {
-      const int mid = (r0 + rhi) >> 1;
-      if (uniform(pre[mid]) <= rl) r0 = mid; else rhi = mid;
+  } else {
+    for (uint32_t rl = lo; rl < hi;) {
+      const int r0 = request_of(pre, R, rl, lane);  // pre[r0] <= rl < pre[r0 + 1]
+      const int rend = min(R, r0 + kRoundReqs);
+      const uint32_t rh = min(min(hi, rl + (uint32_t)kRoundPages), uniform(pre[rend]));
+      // requests r0 .. rend - 1 that start before rh (a prefix: pre does not decrease)
+      const bool starts = lane < rend - r0 && pre[min(r0 + lane, R)] < rh;
+      const int nreq = __popcll(__ballot(starts));
+      const int np = (int)(rh - rl);
+      setup_round<FMT>(a, L, pre, slot_of, r0, nreq, rl, np, tid);
+      __syncthreads();
+      stream_round<FMT>(a, L, rl, np, lane, n, g);
+      __syncthreads();
+      write_round(a, L, rl, np, tid);
+      __syncthreads();
+      rl = rh;
     }
-    const int rend = min(R, r0 + kRoundReqs);
-    const uint32_t rh = min(min(hi, rl + (uint32_t)kRoundPages), uniform(pre[rend]));
-    int nreq = 0;
-    while (r0 + nreq < rend && uniform(pre[r0 + nreq]) < rh) ++nreq;
-    const int np = (int)(rh - rl);
-    setup_round<FMT>(a, L, pre, slot_of, r0, nreq, rl, np, tid);
-    __syncthreads();
-    stream_round<FMT>(a, L, rl, np, lane, n, g);
-    __syncthreads();
-    write_round(a, L, rl, np, tid);
-    __syncthreads();
-    rl = rh;
+  }
+
+  // 3. -inf past each group's extent, and everywhere for graph pads: one
+  // output row per workgroup in turn, after the rounds so that the first K
+  // loads do not wait for it
+  for (int q = blockIdx.x; q < R * rows; q += gridDim.x) {
+    const int r = q / rows;
+    const int nbg = (int)(uniform(pre[r + 1]) - uniform(pre[r]));
+    float* out = a.block_scores + (int64_t)q * MB;
+    for (int c = nbg + tid; c < MB; c += kThreads) out[c] = -INFINITY;
   }
   (void)wave;
 }

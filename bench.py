@@ -41,6 +41,10 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="workload index 0..4 (default 3)")
     ap.add_argument("--local-blocks", type=int, default=None)
+    ap.add_argument("--score-mode", choices=("max", "lse"), default="max",
+                    help="block reduction: max (default) or lse")
+    ap.add_argument("--sm-scale", type=float, default=1 / 128 ** 0.5,
+                    help="softmax scale of the lse mode (default 1/sqrt(128))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=None,
                     help="requests in the CPU-oracle sample (default: all real requests)")
@@ -119,10 +123,12 @@ def main() -> int:
         sel = torch.as_tensor(new_rows, device=dev)
         step_staging = w.staging.index_select(0, sel).contiguous()
         step_slots = w.slot_mapping.index_select(0, sel).contiguous()
+    mode = ({"score_mode": I.IDX_SCORE_LSE, "sm_scale": args.sm_scale} if args.score_mode == "lse"
+            else {"score_mode": I.IDX_SCORE_MAX})
     p = I.make_params(k_format=w.k_format, q=w.q, k=w.k, k_scale=w.k_scale, req_slot=w.req_slot,
                       block_table=w.block_table, row_len=w.row_len, packed_queries=w.packed_queries,
                       gqa=w.gqa, topk=K, init_blocks=w.init_blocks, local_blocks=w.local_blocks,
-                      max_blocks=MB, n_slot_rows=w.n_slot_rows, n_pages=w.n_pages, **outs)
+                      max_blocks=MB, n_slot_rows=w.n_slot_rows, n_pages=w.n_pages, **mode, **outs)
 
     # algorithmic bytes (token-exact K of each real request's longest row)
     P, H = w.packed_queries, w.gqa
@@ -191,7 +197,9 @@ def main() -> int:
     achieved = score_bytes / score_mean_s / 1e9
     digest = source_digest()
     fmt_name = {W.K_BF16: "bf16", W.K_FP8_E4M3: "fp8", W.K_NVFP4: "nvfp4"}[w.k_format]
-    traffic = traffic_from_profiles(f"score_kernel_{fmt_name}", W.CONFIG_NAMES[args.config], digest)
+    # the committed counter profiles are of the max reduction
+    traffic = (traffic_from_profiles(f"score_kernel_{fmt_name}", W.CONFIG_NAMES[args.config], digest)
+               if args.score_mode == "max" else None)
 
     line = {
         "metric": METRIC,
@@ -208,6 +216,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": w.name, "requests": w.n_real, "graph_pads": w.n_req - w.n_real,
+            "block_score": args.score_mode,
+            **({"sm_scale": args.sm_scale} if args.score_mode == "lse" else {}),
             "packed_queries": P, "gqa": H, "head_dim": 128, "block": 128,
             "k_format": W.FORMAT_NAMES[w.k_format], "q": "bf16",
             "context_tokens": [int(w.req_len.min()), int(w.req_len.max() + P - 1)],
@@ -237,12 +247,12 @@ def main() -> int:
         line["fp4_store_pool"] = pool_store
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests, mode)
     print(json.dumps(line), flush=True)
     return 0
 
 
-def cpu_baseline(w, n_sample) -> dict:
+def cpu_baseline(w, n_sample, mode) -> dict:
     """The oracle, untuned, on the host cores: the step over the first
     ``n_sample`` real requests (default all), scaled to one full step."""
     import numpy as np
@@ -259,7 +269,7 @@ def cpu_baseline(w, n_sample) -> dict:
     else:
         a = w.oracle_args()
     q = a["q"].reshape(a["n_req"], P * H, 128)[sel].reshape(-1, H, 128)
-    sub = dict(a, n_req=n, q=np.ascontiguousarray(q), req_slot=np.ascontiguousarray(a["req_slot"][sel]),
+    sub = dict(a, **mode, n_req=n, q=np.ascontiguousarray(q), req_slot=np.ascontiguousarray(a["req_slot"][sel]),
                row_len=np.ascontiguousarray(a["row_len"].reshape(a["n_req"], P)[sel].reshape(-1)))
     times = []
     for _ in range(3):

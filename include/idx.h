@@ -3,9 +3,10 @@
  *
  * The step scores, for every request, its packed query rows (draft row x
  * index head) against the request's paged index-K cache, reduces each
- * 128-token block to its max score under each row's own length, and selects
- * the top-k blocks per (row, head) with the init and local-window blocks
- * always selected.  Sources (by page title and section):
+ * 128-token block to one score under each row's own length (the max, or the
+ * log-sum-exp), and selects the top-k blocks per (row, head) with the init
+ * and local-window blocks always selected.  Sources (by page title and
+ * section):
  *
  *  [P1] sglang PR 45451, "packed decode score kernel", Modifications: a
  *       request's rows share one 16-row dot tile so each K tile loads once;
@@ -17,7 +18,8 @@
  *       masks and forced init/local blocks use each row's own length; a slot
  *       past the request table (graph padding) reads no K.  Accuracy Tests:
  *       selection is exact; K is addressed through a permuted, gapped slot
- *       table.
+ *       table.  [P1] Accuracy Tests: the selected-block scores are tested
+ *       both as the max and as the lse of the block.
  *  [P3] ROCm/ATOM PR 2745, "NVFP4 index cache", Summary: per key (D = 128)
  *       a 64 B e2m1 payload, two codes a byte with the even element in the
  *       low nibble, and 8 B of E4M3 scales, one per 16 elements, unit outer
@@ -55,7 +57,13 @@ enum {
   IDX_E_PACK = -4,   /* packed_queries * gqa > 16: the rows do not fit one tile [P1] */
   IDX_E_TOPK = -5,   /* topk < 1, init/local < 0, or topk < init_blocks + local_blocks */
   IDX_E_LAUNCH = -6, /* the HIP runtime rejected a kernel launch                      */
-  IDX_E_ALIGN = -7   /* q, k, k_scale or staging not 16-byte aligned                  */
+  IDX_E_ALIGN = -7,  /* q, k, k_scale or staging not 16-byte aligned                  */
+  IDX_E_MODE = -8    /* unknown score_mode, or an lse sm_scale that is not finite > 0 */
+};
+
+enum {
+  IDX_SCORE_MAX = 0, /* block score: max over the block's visible tokens of q.k        */
+  IDX_SCORE_LSE = 1  /* block score: ln sum over those tokens of exp(sm_scale * q.k)    */
 };
 
 enum {
@@ -90,8 +98,11 @@ enum {
  *   row_len      int32 [R*P]: tokens visible to each draft row.  Negative
  *                values count as 0, values above MB*B as MB*B.
  *   block_scores fp32 [R*P][H][MB]: for block b of a row with nb =
- *                ceil(row_len/B) blocks, the max over that block's visible
- *                tokens of the raw dot q.k (fp32 accumulation); -inf for
+ *                ceil(row_len/B) blocks, a reduction over that block's
+ *                visible tokens of the raw dot q.k (fp32 accumulation):
+ *                IDX_SCORE_MAX: the max; IDX_SCORE_LSE: the natural log of
+ *                the sum of exp(sm_scale * q.k), in fp32 from the block's max
+ *                (the [P1] Accuracy Tests name both reductions).  -inf for
  *                b >= nb and for graph pads.
  *   topk_ids     int32 [R*P][H][topk]: selected block ids, ascending, padded
  *                with -1.  If nb <= topk every block is selected; otherwise
@@ -113,6 +124,8 @@ typedef struct idx_params {
   int32_t topk;           /* >= 1                                            */
   int32_t init_blocks;    /* forced leading blocks, >= 0                     */
   int32_t local_blocks;   /* forced trailing blocks, >= 0                    */
+  int32_t score_mode;     /* IDX_SCORE_MAX or IDX_SCORE_LSE                  */
+  float sm_scale;         /* IDX_SCORE_LSE: finite, > 0; ignored for MAX     */
   int32_t reserved;       /* must be 0                                       */
   int64_t n_pages;        /* pages in the K pool, >= 0                       */
   const void* q;

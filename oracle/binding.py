@@ -23,7 +23,8 @@ class OracleParams(C.Structure):
         ("k_format", C.c_int32), ("n_req", C.c_int32), ("n_slot_rows", C.c_int32),
         ("packed_queries", C.c_int32), ("gqa", C.c_int32), ("head_dim", C.c_int32),
         ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
-        ("init_blocks", C.c_int32), ("local_blocks", C.c_int32), ("reserved", C.c_int32),
+        ("init_blocks", C.c_int32), ("local_blocks", C.c_int32), ("score_mode", C.c_int32),
+        ("sm_scale", C.c_float), ("reserved", C.c_int32),
         ("n_pages", C.c_int64),
         ("q", C.c_void_p), ("k", C.c_void_p), ("k_scale", C.c_void_p),
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
@@ -125,6 +126,8 @@ class Oracle:
         for f in ("k_format", "n_req", "n_slot_rows", "packed_queries", "gqa", "max_blocks",
                   "topk", "init_blocks", "local_blocks", "n_pages"):
             setattr(p, f, int(a[f]))
+        p.score_mode = int(a.get("score_mode", 0))
+        p.sm_scale = float(a.get("sm_scale", 0.0))
         p.head_dim = int(a.get("head_dim", 128))
         p.block_size = int(a.get("block_size", 128))
         p.q = _ptr(a["q"])

@@ -170,6 +170,8 @@ static int check_params(const oracle_params* p) {
   if (p->topk < 1 || p->init_blocks < 0 || p->local_blocks < 0 ||
       p->topk < p->init_blocks + p->local_blocks)
     return -1;
+  if (p->score_mode != ORACLE_SCORE_MAX && p->score_mode != ORACLE_SCORE_LSE) return -1;
+  if (p->score_mode == ORACLE_SCORE_LSE && !(p->sm_scale > 0.0f && isfinite(p->sm_scale))) return -1;
   return 0;
 }
 
@@ -258,6 +260,8 @@ int oracle_score_packed(const oracle_params* p) {
     int end[256];
     int64_t page = -1;
     int page_ok = 0, any = 0;
+    int lse = p->score_mode == ORACLE_SCORE_LSE;
+    double* sv = lse ? (double*)malloc(sizeof(double) * 128 * (size_t)rows) : NULL; /* lse: each row's token scores */
 
     /* which tokens of block b each tile row sees */
     for (i = 0; i < rows; i++) {
@@ -290,14 +294,24 @@ int oracle_score_packed(const oracle_params* p) {
           if (t >= end[i]) continue;
           for (d = 0; d < 128; d++) s += bf16_value(q[qrow * 128 + d]) * v[d];
           if (s > best[i]) best[i] = s;
+          if (sv) sv[i * 128 + t] = s;
         }
       }
     }
     for (i = 0; i < rows; i++) {
       float out = (float)best[i];
+      if (sv && end[i] > 0 && page_ok) {
+        /* lse over the visible tokens, written from their max m:
+         * ln sum exp(c s_t) = c m + ln sum exp(c (s_t - m)) */
+        double c = MUTANT(14) ? 1.0 : (double)p->sm_scale; /* mutant 14: scale dropped */
+        double sum = 0.0;
+        for (t = 0; t < end[i]; t++) sum += exp(c * (sv[i * 128 + t] - best[i]));
+        out = (float)(c * best[i] + log(sum));
+      }
       if (end[i] > 0 && !page_ok) out = NAN; /* visible block, page id out of range */
       p->block_scores[((int64_t)r * rows + i) * MB + b] = out;
     }
+    free(sv);
   }
   return 0;
 }

@@ -16,14 +16,19 @@
  *    slot table; a slot past the request table (graph padding) reads no K;
  *    selection is exact.
  *  - sglang PR 45451 ("packed decode score kernel"), Modifications: each row
- *    keeps its own length mask and the block score is the max score.
+ *    keeps its own length mask and the block score is the max score; its
+ *    Accuracy Tests check the selected-block scores both as the max and as
+ *    the lse.  The pages give no formula for the lse; the reading taken is
+ *    ln sum_t exp(sm_scale * q.k_t) over the row's visible tokens of the
+ *    block, with the caller's softmax scale sm_scale > 0.
  *  - ROCm/ATOM PR 2745 (NVFP4 index cache), Summary and Validation: per key a
  *    64 B e2m1 payload (two codes a byte, even element in the low nibble) and
  *    8 B of E4M3 scales, one per 16 elements, unit outer scale; the store uses
  *    scale = e4m3(amax / 6) and codes rounded half-to-even, saturating at 6.
  *
  * All arithmetic is plain loops.  Token scores are accumulated in double; the
- * block max is rounded once to float, and selection compares those floats.
+ * block max (or the lse, in double) is rounded once to float, and selection
+ * compares those floats.
  */
 #ifndef SAL_ORACLE_H
 #define SAL_ORACLE_H
@@ -40,6 +45,11 @@ enum {
   ORACLE_K_NVFP4 = 2     /* 64 B e2m1 payload + 8 B E4M3 scales per token  */
 };
 
+enum {
+  ORACLE_SCORE_MAX = 0,  /* block score: max of q.k over the visible tokens      */
+  ORACLE_SCORE_LSE = 1   /* block score: ln sum exp(sm_scale * q.k) over them    */
+};
+
 /* Same field order and meaning as the GPU library's parameter block. */
 typedef struct oracle_params {
   int32_t k_format;
@@ -53,6 +63,8 @@ typedef struct oracle_params {
   int32_t topk;
   int32_t init_blocks;
   int32_t local_blocks;
+  int32_t score_mode;     /* ORACLE_SCORE_MAX or ORACLE_SCORE_LSE                */
+  float   sm_scale;       /* lse: the softmax scale, finite and > 0              */
   int32_t reserved;
   int64_t n_pages;        /* pages in the K pool                                 */
   const void*    q;        /* bf16 [n_req*P][H][D]                               */
@@ -66,8 +78,8 @@ typedef struct oracle_params {
   float*   topk_scores;    /* [n_req*P][H][topk]                                 */
 } oracle_params;
 
-/* Block max of every (row, head, block); -inf past the row's own block count,
- * NaN for a visible block whose page id is outside [0, n_pages). */
+/* Block max (or lse) of every (row, head, block); -inf past the row's own
+ * block count, NaN for a visible block whose page id is outside [0, n_pages). */
 int oracle_score_packed(const oracle_params* p);
 /* Forced top-k over block_scores; ids ascending, padded with -1 / -inf. */
 int oracle_block_topk(const oracle_params* p);

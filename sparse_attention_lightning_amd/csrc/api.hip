@@ -44,6 +44,10 @@ int check(const idx_params* p, int need) {
   if (p->max_blocks < 0 || p->max_blocks > IDX_MAX_BLOCKS)
     return fail(IDX_E_SHAPE, "max_blocks %d outside [0, %d]", p->max_blocks, IDX_MAX_BLOCKS);
   if (p->reserved != 0) return fail(IDX_E_SHAPE, "reserved field must be 0");
+  if (p->score_mode != IDX_SCORE_MAX && p->score_mode != IDX_SCORE_LSE)
+    return fail(IDX_E_MODE, "unknown score_mode %d", p->score_mode);
+  if (p->score_mode == IDX_SCORE_LSE && !(p->sm_scale > 0.0f && p->sm_scale <= 3.402823466e38f))
+    return fail(IDX_E_MODE, "lse needs a finite sm_scale > 0 (got %g)", (double)p->sm_scale);
   if (p->n_pages > (int64_t)1 << 40) return fail(IDX_E_SHAPE, "n_pages %lld too large", (long long)p->n_pages);
   if (p->topk < 1 || p->init_blocks < 0 || p->local_blocks < 0 ||
       (int64_t)p->topk < (int64_t)p->init_blocks + p->local_blocks)
@@ -89,6 +93,8 @@ idx::StepArgs args_of(const idx_params* p) {
   a.topk = p->topk;
   a.init_blocks = p->init_blocks;
   a.local_blocks = p->local_blocks;
+  a.score_mode = p->score_mode;
+  a.sm_scale = p->sm_scale;
   return a;
 }
 

@@ -33,6 +33,8 @@ struct StepArgs {
   int64_t n_pages;
   int32_t k_format;
   int32_t n_req, n_slot_rows, P, H, max_blocks, topk, init_blocks, local_blocks;
+  int32_t score_mode;  // IDX_SCORE_MAX or IDX_SCORE_LSE
+  float sm_scale;      // lse only
 };
 
 hipError_t launch_score(const StepArgs& a, hipStream_t stream);
@@ -61,6 +63,16 @@ __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
   x = fmaxf(x, dpp_mov<0x124>(x));  // row_ror:4
   x = fmaxf(x, dpp_mov<0x128>(x));  // row_ror:8
+  return x;
+}
+
+// Sum over the 16 lanes of a DPP row, in every lane (the rotations reach
+// offsets 0, 4, 8 and 12 after the quad steps).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x124>(x);  // row_ror:4
+  x += dpp_mov<0x128>(x);  // row_ror:8
   return x;
 }
 

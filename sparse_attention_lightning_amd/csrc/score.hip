@@ -124,13 +124,6 @@ struct Half {
   uint32_t sc[4];  // NVFP4: this lane's two scale bytes of each tile
 };
 
-// E4M3 byte (non-negative scales; the sign bit is honoured) to float.
-__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15, m = b & 7;
-  float v = (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120) << 23) | (m << 20));
-  return (b & 0x80) ? -v : v;
-}
-
 // Buffer descriptor of one page.  Word 3 is the raw 32-bit data format of
 // gfx9 MUBUF descriptors.  A page the kernel must not read gets size 0: every
 // load through it is out of range, returns zeros and touches no memory.  Its
@@ -203,10 +196,14 @@ __device__ __forceinline__ f32x4 mfma(typename Fmt<FMT>::Op a, typename Fmt<FMT>
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Fold one half page into the running per-row maxima of this lane's 4 rows.
-template <int FMT>
+// Fold one half page into the running state of this lane's 4 rows.
+// IDX_SCORE_MAX: st0 = the running max of q.k.  IDX_SCORE_LSE: st0 = the
+// running max m of v = c2 * q.k and st1 = the sum of 2^(v - m) (c2 carries
+// sm_scale, log2 e and, for NVFP4, the query tile's 2^-sigma).
+template <int FMT, int MODE>
 __device__ __forceinline__ void score_half(const Half<FMT>& h, const typename Fmt<FMT>::Op* qf,
-                                           bool full, int pos0, const int* len, float* mx) {
+                                           bool full, int pos0, const int* len, float* st0, float* st1,
+                                           float c2) {
   f32x4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -217,30 +214,65 @@ __device__ __forceinline__ void score_half(const Half<FMT>& h, const typename Fm
   (void)mant;
   if constexpr (FMT == IDX_K_NVFP4) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      // the two scale bytes through the hardware E4M3 conversion (unit scale)
+      scale[t][0] = __builtin_amdgcn_cvt_scalef32_f32_fp8(h.sc[t], 1.0f, 0);
+      scale[t][1] = __builtin_amdgcn_cvt_scalef32_f32_fp8(h.sc[t], 1.0f, 1);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const float s = e4m3_to_float((h.sc[t] >> (8 * q)) & 0xFF);
-        scale[t][q] = s;  // the conversion applies the exponent of s
-        const _Float16 f = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+        // the fp4 conversion applies the exponent of the scale; its mantissa
+        // factor 1.m (at most 3 bits) is exact in f16
+        const _Float16 f =
+            (_Float16)__uint_as_float((__float_as_uint(scale[t][q]) & 0x007FFFFFu) | 0x3F800000u);
         mant[t][q] = f16x2{f, f};
       }
+    }
   }
   // k-step outer, tile inner: four independent accumulation chains
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = mfma<FMT>(qf[s], operand<FMT>(h, t, s, scale[t], mant[t]), acc[t]);
-  if (full) {
+  if constexpr (MODE == IDX_SCORE_MAX) {
+    (void)st1;
+    (void)c2;
+    if (full) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], acc[t][j]);
+        for (int j = 0; j < 4; ++j) st0[j] = fmaxf(st0[j], acc[t][j]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st0[j] = fmaxf(st0[j], (pos0 + 16 * t < len[j]) ? acc[t][j] : -INFINITY);
+    }
+  } else if (full) {
+    // every token visible: the new max is finite (c2 > 0)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float am = fmaxf(fmaxf(acc[0][j], acc[1][j]), fmaxf(acc[2][j], acc[3][j]));
+      const float mnew = fmaxf(st0[j], am * c2);
+      float sum = st1[j] * __builtin_amdgcn_exp2f(st0[j] - mnew);  // 0 while st0 is -inf
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][j], c2, -mnew));
+      st1[j] = sum;
+      st0[j] = mnew;
+    }
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int j = 0; j < 4; ++j) {
+      float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], (pos0 + 16 * t < len[j]) ? acc[t][j] : -INFINITY);
+      for (int t = 0; t < 4; ++t) v[t] = (pos0 + 16 * t < len[j]) ? acc[t][j] * c2 : -INFINITY;
+      const float mnew = fmaxf(st0[j], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      const float base = (mnew == -INFINITY) ? 0.f : mnew;  // nothing visible yet: every term is 0
+      float sum = st1[j] * __builtin_amdgcn_exp2f(st0[j] - base);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sum += __builtin_amdgcn_exp2f(v[t] - base);
+      st1[j] = sum;
+      st0[j] = mnew;
+    }
   }
 }
 
@@ -416,7 +448,7 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
 // One wave's part of a round: pages from the round's counter until none is
 // left.  Wave page p (two units) is described by lane p % 64 of vm_tag (round
 // page | request << 16, or -1) and vm_pid.
-template <int FMT>
+template <int FMT, int MODE>
 __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uint32_t lo, int np, int lane,
                                              int n, int g) {
   typedef typename Fmt<FMT>::Op Op;
@@ -434,11 +466,13 @@ __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uin
   int last = -1;  // last wave page that holds a page
 
   int cur = -1, p0 = 0, lmin = 0, sigma = 0, my_len = 0;
+  float c2 = 0.f;  // lse: sm_scale * log2 e * 2^-sigma
   int len[4] = {0, 0, 0, 0};
   Op qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = Op{};
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float st0[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float st1[4] = {0.f, 0.f, 0.f, 0.f};
 
   auto issue = [&](Half<FMT>& h, int V) {
     const int p = V >> 1;
@@ -482,6 +516,7 @@ __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uin
         p0 = (int)uniform((uint32_t)rq.p0);
         lmin = (int)uniform((uint32_t)rq.lmin);
         sigma = (int)uniform((uint32_t)rq.sigma);
+        if constexpr (MODE == IDX_SCORE_LSE) c2 = ldexpf(a.sm_scale * 1.44269504088896341f, -sigma);
         const u32x4 lv = *reinterpret_cast<const u32x4*>(&rq.len[4 * g]);
         len[0] = (int)lv.x; len[1] = (int)lv.y; len[2] = (int)lv.z; len[3] = (int)lv.w;
         my_len = (n == 0) ? len[0] : (n == 1) ? len[1] : (n == 2) ? len[2] : len[3];
@@ -490,17 +525,30 @@ __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uin
           qf[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(&L.q[j][n][Fmt<FMT>::d0(s, g)]));
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mx[e] = -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        st0[e] = -INFINITY;
+        st1[e] = 0.f;
+      }
     }
     const int b = (int)(lo + (uint32_t)k) - p0;
     const bool full = (b + 1) * kBlock <= lmin;
-    score_half<FMT>(h, qf, full, b * kBlock + 64 * (U & 1) + n, len, mx);
+    score_half<FMT, MODE>(h, qf, full, b * kBlock + 64 * (U & 1) + n, len, st0, st1, c2);
     if (U & 1) {
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = row16_max(mx[e]);
+      for (int e = 0; e < 4; ++e) {
+        const float m = row16_max(st0[e]);
+        if constexpr (MODE == IDX_SCORE_MAX) {
+          v[e] = m;
+        } else {
+          // the 16 lanes' sums rescaled to the block's max, then ln = log2 * ln 2
+          const float base = (m == -INFINITY) ? 0.f : m;
+          const float sum = row16_sum(st1[e] * __builtin_amdgcn_exp2f(st0[e] - base));
+          v[e] = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(sum)) * 0.693147180559945309f;
+        }
+      }
       float o = (n == 0) ? v[0] : (n == 1) ? v[1] : (n == 2) ? v[2] : v[3];
-      if constexpr (FMT == IDX_K_NVFP4) o = ldexpf(o, -sigma);
+      if constexpr (FMT == IDX_K_NVFP4 && MODE == IDX_SCORE_MAX) o = ldexpf(o, -sigma);
       const int pid = __builtin_amdgcn_readlane(vm_pid, p & 63);
       if (!(pid >= 0 && pid < a.n_pages)) o = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
       if (writer) L.stage[wrow][k] = o;
@@ -553,7 +601,7 @@ __device__ __forceinline__ int request_of(const uint32_t* pre, int R, uint32_t x
   return lo;
 }
 
-template <int FMT>
+template <int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   extern __shared__ uint32_t pre[];  // n_req + 1 prefix sums of per-request block counts, then n_req slots
   __shared__ RoundLds L;
@@ -614,7 +662,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
       const int np = (int)(rh - rl);
       setup_round<FMT>(a, L, pre, slot_of, r0, nreq, rl, np, tid);
       __syncthreads();
-      stream_round<FMT>(a, L, rl, np, lane, n, g);
+      stream_round<FMT, MODE>(a, L, rl, np, lane, n, g);
       __syncthreads();
       write_round(a, L, rl, np, tid);
       __syncthreads();
@@ -639,39 +687,47 @@ size_t dyn_bytes(int n_req) { return (size_t)(2 * n_req + 1) * sizeof(uint32_t);
 
 // Workgroups that fit on the device at once (cached per device), with the
 // dynamic LDS limit raised to what the largest request count needs.
-template <int FMT>
+template <int FMT, int MODE>
 int resident_workgroups() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cache[dev] > 0) return cache[dev];
   const size_t smem = dyn_bytes(IDX_MAX_REQ);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_kernel<FMT>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_kernel<FMT, MODE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(score_kernel<FMT>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(score_kernel<FMT, MODE>),
                                                    kThreads, smem) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   cache[dev] = cus * per_cu;
   return cache[dev];
 }
 
-template <int FMT>
+template <int FMT, int MODE>
 void launch(const StepArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(score_kernel<FMT>, dim3(resident_workgroups<FMT>()), dim3(kThreads),
+  hipLaunchKernelGGL((score_kernel<FMT, MODE>), dim3(resident_workgroups<FMT, MODE>()), dim3(kThreads),
                      dyn_bytes(a.n_req), stream, a);
+}
+
+template <int MODE>
+void launch_mode(const StepArgs& a, hipStream_t stream) {
+  switch (a.k_format) {
+    case IDX_K_BF16: launch<IDX_K_BF16, MODE>(a, stream); break;
+    case IDX_K_FP8_E4M3: launch<IDX_K_FP8_E4M3, MODE>(a, stream); break;
+    default: launch<IDX_K_NVFP4, MODE>(a, stream); break;
+  }
 }
 }  // namespace
 
 hipError_t launch_score(const StepArgs& a, hipStream_t stream) {
   if (a.n_req == 0 || a.max_blocks == 0) return hipSuccess;
-  switch (a.k_format) {
-    case IDX_K_BF16: launch<IDX_K_BF16>(a, stream); break;
-    case IDX_K_FP8_E4M3: launch<IDX_K_FP8_E4M3>(a, stream); break;
-    default: launch<IDX_K_NVFP4>(a, stream); break;
-  }
+  if (a.score_mode == IDX_SCORE_LSE)
+    launch_mode<IDX_SCORE_LSE>(a, stream);
+  else
+    launch_mode<IDX_SCORE_MAX>(a, stream);
   return hipGetLastError();
 }
 

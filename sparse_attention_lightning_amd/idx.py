@@ -18,8 +18,9 @@ import torch
 LIB_PATH = Path(__file__).resolve().parent / "libidx.so"
 
 IDX_OK, IDX_E_NULL, IDX_E_FORMAT, IDX_E_SHAPE, IDX_E_PACK = 0, -1, -2, -3, -4
-IDX_E_TOPK, IDX_E_LAUNCH, IDX_E_ALIGN = -5, -6, -7
+IDX_E_TOPK, IDX_E_LAUNCH, IDX_E_ALIGN, IDX_E_MODE = -5, -6, -7, -8
 IDX_K_BF16, IDX_K_FP8_E4M3, IDX_K_NVFP4 = 0, 1, 2
+IDX_SCORE_MAX, IDX_SCORE_LSE = 0, 1
 IDX_MAX_BLOCKS = 8192
 IDX_MAX_REQ = 8192
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error")
@@ -37,7 +38,8 @@ class IdxParams(C.Structure):
         ("k_format", C.c_int32), ("n_req", C.c_int32), ("n_slot_rows", C.c_int32),
         ("packed_queries", C.c_int32), ("gqa", C.c_int32), ("head_dim", C.c_int32),
         ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
-        ("init_blocks", C.c_int32), ("local_blocks", C.c_int32), ("reserved", C.c_int32),
+        ("init_blocks", C.c_int32), ("local_blocks", C.c_int32), ("score_mode", C.c_int32),
+        ("sm_scale", C.c_float), ("reserved", C.c_int32),
         ("n_pages", C.c_int64),
         ("q", C.c_void_p), ("k", C.c_void_p), ("k_scale", C.c_void_p),
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
@@ -112,9 +114,11 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
                 block_scores: torch.Tensor, topk_ids: torch.Tensor | None,
                 topk_scores: torch.Tensor | None, packed_queries: int, gqa: int, topk: int,
                 init_blocks: int, local_blocks: int, max_blocks: int | None = None,
-                n_slot_rows: int | None = None, n_pages: int | None = None) -> IdxParams:
+                n_slot_rows: int | None = None, n_pages: int | None = None,
+                score_mode: int = IDX_SCORE_MAX, sm_scale: float = 0.0) -> IdxParams:
     """Build the parameter block from tensors (sizes read from their shapes
-    unless given).  The returned object keeps the tensors alive."""
+    unless given).  ``score_mode`` IDX_SCORE_LSE takes ``sm_scale``.  The
+    returned object keeps the tensors alive."""
     if k_format not in _K_DTYPES:
         raise ValueError(f"unknown k_format {k_format}")
     p = IdxParams()
@@ -126,6 +130,8 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
     p.topk = topk
     p.init_blocks = init_blocks
     p.local_blocks = local_blocks
+    p.score_mode = score_mode
+    p.sm_scale = sm_scale
     p.q = _dev(q, "q", (torch.bfloat16,), optional=True)
     p.k = _dev(k, "k", _K_DTYPES[k_format], optional=True)
     p.k_scale = _dev(k_scale, "k_scale", (torch.uint8,), optional=True)

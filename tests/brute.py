@@ -2,8 +2,9 @@
 
 It decodes K through torch's own dtype conversions (bf16, float8_e4m3fn) or
 takes an already exact value pool, scores every visible token of every row one
-block at a time with a numpy matmul, and selects blocks by one full sort with
-the key (not forced, NaN last, -score, id).  The oracle uses none of this: it
+block at a time with a numpy matmul, reduces a block with numpy's max or
+scipy's logsumexp, and selects blocks by one full sort with the key (not
+forced, NaN last, -score, id).  The oracle uses none of this: it
 decodes the bits itself, accumulates dots in a loop and selects with a
 forced-flag pass plus a sort of the remaining blocks.
 """
@@ -13,6 +14,7 @@ import math
 
 import numpy as np
 import torch
+from scipy.special import logsumexp
 
 K_BF16, K_FP8_E4M3, K_NVFP4 = 0, 1, 2
 
@@ -39,6 +41,8 @@ def step(a: dict, pool: np.ndarray) -> dict:
     R, P, H = a["n_req"], a["packed_queries"], a["gqa"]
     MB, K = a["max_blocks"], a["topk"]
     init, local = a["init_blocks"], a["local_blocks"]
+    lse = a.get("score_mode", 0) == 1
+    scale = float(a.get("sm_scale", 0.0))
     q = bf16_values(a["q"]).reshape(R * P * H, 128)
     bt = a["block_table"].reshape(a["n_slot_rows"], MB)
     rows = R * P * H
@@ -60,7 +64,8 @@ def step(a: dict, pool: np.ndarray) -> dict:
                     continue
                 t0 = page * 128
                 toks = pool[t0: t0 + min(128, n - 128 * b)]
-                bs[o, b] = np.float32((toks @ q[o]).max())
+                s = toks @ q[o]
+                bs[o, b] = np.float32(logsumexp(scale * s) if lse else s.max())
 
             def key(b):
                 forced = b < init or b >= nb - local

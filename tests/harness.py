@@ -42,7 +42,8 @@ def gpu_outputs(w: W.Workload, fill: float = float("nan")) -> dict:
     }
 
 
-def gpu_params(w: W.Workload, outs: dict, k=None, k_scale=None) -> I.IdxParams:
+def gpu_params(w: W.Workload, outs: dict, k=None, k_scale=None, score_mode: int = I.IDX_SCORE_MAX,
+               sm_scale: float = 0.0) -> I.IdxParams:
     return I.make_params(
         k_format=w.k_format, q=w.q, k=w.k if k is None else k,
         k_scale=w.k_scale if k_scale is None else k_scale, req_slot=w.req_slot,
@@ -50,7 +51,7 @@ def gpu_params(w: W.Workload, outs: dict, k=None, k_scale=None) -> I.IdxParams:
         topk_ids=outs["topk_ids"], topk_scores=outs["topk_scores"],
         packed_queries=w.packed_queries, gqa=w.gqa, topk=w.topk, init_blocks=w.init_blocks,
         local_blocks=w.local_blocks, max_blocks=w.max_blocks, n_slot_rows=w.n_slot_rows,
-        n_pages=w.n_pages)
+        n_pages=w.n_pages, score_mode=score_mode, sm_scale=sm_scale)
 
 
 def gpu_fp4_store(w: W.Workload) -> None:
@@ -58,9 +59,10 @@ def gpu_fp4_store(w: W.Workload) -> None:
     I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale)
 
 
-def gpu_step(w: W.Workload) -> dict:
+def gpu_step(w: W.Workload, **mode) -> dict:
+    """idx_step on the workload; ``mode``: score_mode / sm_scale."""
     outs = gpu_outputs(w)
-    I.idx_step(gpu_params(w, outs))
+    I.idx_step(gpu_params(w, outs, **mode))
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in outs.items()}
 

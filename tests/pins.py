@@ -331,6 +331,59 @@ def pin_bruteforce_fp4(o) -> None:
     compare_step(o.step(**a), brute.step(a, exact_pool_from_staging(w, vals)), "nvfp4")
 
 
+def pin_bruteforce_lse(o) -> None:
+    """lse block scores against scipy's logsumexp over the visible tokens (the
+    sglang PR 45451 Accuracy Tests check the lse of the selected blocks)."""
+    for fmt, seed in ((W.K_BF16, 15), (W.K_FP8_E4M3, 16)):
+        w = small_workload(fmt, seed=seed, pads=1)
+        a = dict(w.oracle_args(), score_mode=1, sm_scale=0.3)
+        compare_step(o.step(**a), brute.step(a, brute.pool_values(fmt, a["k"])), f"lse {fmt}")
+
+
+def pin_lse_closed_form(o) -> None:
+    """A block whose visible tokens all hold the same key has lse =
+    c * q.k + ln(visible tokens); checked on every valid block, partial last
+    blocks included."""
+    w = small_workload(W.K_BF16, seed=17, R_lens=(300, 1022, 129))
+    a = dict(w.oracle_args(), score_mode=1, sm_scale=0.125)
+    k = a["k"].reshape(w.n_pages, 128, 128).copy()
+    k[:] = k[:, :1, :]  # every token of a page repeats the page's first key
+    a["k"] = k.reshape(-1, 128)
+    got = o.score_packed(**a)["block_scores"]
+    q = brute.bf16_values(a["q"]).reshape(-1, 128)
+    kv = brute.bf16_values(k[:, 0, :])
+    bt = a["block_table"].reshape(a["n_slot_rows"], -1)
+    rows = 16
+    checked = 0
+    for r in range(w.n_req):
+        slot = int(a["req_slot"][r])
+        for i in range(rows):
+            n = int(a["row_len"][r * 4 + i // 4])
+            for b in range((n + 127) // 128):
+                vis = min(128, n - 128 * b)
+                want = 0.125 * float(q[r * rows + i] @ kv[bt[slot, b]]) + np.log(vis)
+                g = float(got[r * rows + i, b])
+                assert abs(g - want) <= 1e-6 * max(abs(want), 1.0), (r, i, b, g, want)
+                checked += 1
+    assert checked > 100
+
+
+def pin_lse_bounds(o) -> None:
+    """c * max <= lse <= c * max + ln(visible tokens) on every valid block,
+    with the max from the max mode of the same oracle."""
+    w = small_workload(W.K_FP8_E4M3, seed=18)
+    a = w.oracle_args()
+    mx = o.score_packed(**a)["block_scores"].astype(np.float64)
+    ls = o.score_packed(**dict(a, score_mode=1, sm_scale=0.7))["block_scores"].astype(np.float64)
+    assert np.array_equal(np.isinf(mx), np.isinf(ls)), "lse and max disagree on which blocks are empty"
+    f = np.isfinite(mx)
+    lens = np.repeat(a["row_len"].astype(np.int64), 4).reshape(-1, 1)
+    vis = np.clip(lens - 128 * np.arange(mx.shape[1])[None, :], 0, 128)
+    tol = 1e-6 * np.maximum(np.abs(ls), 1.0)
+    assert np.all(ls[f] >= 0.7 * mx[f] - tol[f]), "lse below c * max"
+    assert np.all(ls[f] <= 0.7 * mx[f] + np.log(vis[f]) + tol[f]), "lse above c * max + ln n"
+
+
 def pin_fp4_equals_bf16_of_dequant(o) -> None:
     """NVFP4 scoring equals bf16 scoring fed the dequantized keys, bit for bit
     (ATOM PR 2745, Validation: e2m1 x E4M3 values are exact in bf16)."""
@@ -545,6 +598,7 @@ def pin_graph_pads(o) -> None:
 PINS = [
     pin_fp8_decode, pin_e2m1_decode, pin_golden_store, pin_fp4_roundtrip,
     pin_bruteforce_bf16, pin_bruteforce_fp8, pin_bruteforce_fp4, pin_fp4_equals_bf16_of_dequant,
+    pin_bruteforce_lse, pin_lse_closed_form, pin_lse_bounds,
     pin_topk_textbook, pin_topk_bruteforce, pin_topk_invariants, pin_exact_tie, pin_straddle,
     pin_packed_equals_per_row, pin_masking, pin_slot_permutation, pin_graph_pads,
     pin_scale_rounding, pin_code_rounding,

@@ -5,6 +5,7 @@ from __future__ import annotations
 
 import ctypes as C
 import re
+import subprocess
 from pathlib import Path
 
 import pytest
@@ -60,6 +61,8 @@ REFUSALS = [
     ("max_blocks", I.IDX_MAX_BLOCKS + 1, I.IDX_E_SHAPE),
     ("max_blocks", -1, I.IDX_E_SHAPE),
     ("reserved", 1, I.IDX_E_SHAPE),
+    ("score_mode", 2, I.IDX_E_MODE),
+    ("score_mode", -1, I.IDX_E_MODE),
     ("topk", 0, I.IDX_E_TOPK),
     ("topk", 2, I.IDX_E_TOPK),          # < init + local
     ("local_blocks", -1, I.IDX_E_TOPK),
@@ -83,6 +86,33 @@ def test_step_refusals(lib, field, value, code):
     setattr(p, field, value)
     assert lib.idx_step(C.byref(p), None) == code
     assert lib.idx_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan")])
+def test_lse_needs_a_finite_positive_scale(lib, scale):
+    p = good_params()
+    p.score_mode = I.IDX_SCORE_LSE
+    p.sm_scale = scale
+    assert lib.idx_step(C.byref(p), None) == I.IDX_E_MODE
+    assert lib.idx_score_packed(C.byref(p), None) == I.IDX_E_MODE
+    p.score_mode = I.IDX_SCORE_MAX  # the scale is ignored for the max
+    assert lib.idx_score_packed(C.byref(p), None) != I.IDX_E_MODE
+
+
+def test_params_layout_matches_header(tmp_path):
+    """The ctypes mirror has the C struct's size and field offsets (gcc reads
+    include/idx.h)."""
+    names = [f for f, _ in I.IdxParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "idx.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(idx_params));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(idx_params, {n}));\n' for n in names)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", f"-I{ROOT / 'include'}", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == C.sizeof(I.IdxParams)
+    assert got[1:] == [getattr(I.IdxParams, n).offset for n in names]
 
 
 def test_null_params(lib):

@@ -337,8 +337,8 @@ def test_shares_longer_than_a_round(oracle):
 # ---------------------------------------------------------------------------
 # the five workloads at full size, in the benchmark's launch configuration
 # ---------------------------------------------------------------------------
-def _full(oracle, idx, sample, local_blocks=None):
-    say("workload", W.CONFIG_NAMES[idx], "local", local_blocks, "sample", sample)
+def _full(oracle, idx, sample, local_blocks=None, **mode):
+    say("workload", W.CONFIG_NAMES[idx], "local", local_blocks, "sample", sample, mode)
     w = W.config(idx, device="cuda", local_blocks=local_blocks)
     P, H = w.packed_queries, w.gqa
     if w.k_format == W.K_NVFP4:
@@ -353,7 +353,8 @@ def _full(oracle, idx, sample, local_blocks=None):
         a = w.oracle_args(payload, scales)
     else:
         a = w.oracle_args()
-    g = Hn.gpu_step(w)
+    a = dict(a, **mode)
+    g = Hn.gpu_step(w, **mode)
     sub = Hn.subset_args(a, sample, P, H)
     o = oracle.step(**sub)
     rows = Hn.rows_of(sample, P * H)
@@ -397,3 +398,60 @@ def test_workload_3_fp8_524k_pads(oracle):
 
 def test_workload_4_nvfp4_150k(oracle):
     _full(oracle, 4, sample=[0, 33, 63])
+
+
+# ---------------------------------------------------------------------------
+# lse block scores (sglang PR 45451, Accuracy Tests: the selected-block scores
+# are checked as the max and as the lse)
+# ---------------------------------------------------------------------------
+LSE = dict(score_mode=I.IDX_SCORE_LSE, sm_scale=float(1 / np.sqrt(128)))
+
+
+@pytest.mark.parametrize("fmt", [W.K_BF16, W.K_FP8_E4M3, W.K_NVFP4], ids=["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("shape", [1, 2, 4, 6])
+def test_lse_small_shapes(oracle, fmt, shape):
+    P, H, lens, topk, init, local, pads = SHAPES[shape]
+    say("lse small", fmt, SHAPES[shape])
+    w = W.make(name="lse", R=len(lens), P=P, H=H, k_format=fmt, req_len=lens, topk=topk,
+               init_blocks=init, local_blocks=local, seed=200 + shape, pads=pads,
+               pad_len=4096, device="cuda")
+    if fmt == W.K_NVFP4:
+        Hn.gpu_fp4_store(w)
+        a = w.oracle_args(*Hn.oracle_pool(oracle, w))
+    else:
+        a = w.oracle_args()
+    a = dict(a, **LSE)
+    Hn.assert_parity(Hn.gpu_step(w, **LSE), oracle.step(**a), a)
+
+
+@pytest.mark.parametrize("scale", [0.01, 1.0, 4.0])
+def test_lse_scales(oracle, scale):
+    """Small and large softmax scales (a large one makes the block's max term
+    dominate; a small one sums 128 terms of nearly equal size)."""
+    say("lse scale", scale)
+    w = W.make(name="lse_scale", R=3, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[5000, 129, 2000],
+               topk=6, init_blocks=1, local_blocks=2, seed=303, device="cuda")
+    mode = dict(score_mode=I.IDX_SCORE_LSE, sm_scale=scale)
+    a = dict(w.oracle_args(), **mode)
+    Hn.assert_parity(Hn.gpu_step(w, **mode), oracle.step(**a), a)
+
+
+def test_lse_invalid_page_ids(oracle):
+    say("lse invalid page ids")
+    w = W.make(name="lse_badpage", R=2, P=4, H=4, k_format=W.K_BF16, req_len=[900, 1500],
+               topk=4, init_blocks=1, local_blocks=1, seed=8, device="cuda")
+    w.block_table[int(w.req_slot[0]), 3] = w.n_pages + 1
+    w.block_table[int(w.req_slot[1]), 0] = -1
+    a = dict(w.oracle_args(), **LSE)
+    g, o = Hn.gpu_step(w, **LSE), oracle.step(**a)
+    assert np.isnan(o["block_scores"]).any()
+    Hn.assert_parity(g, o, a)
+
+
+def test_lse_workload_3_fp8_524k_pads(oracle):
+    g, _ = _full(oracle, 3, sample=[0, 31, 33], **LSE)
+    assert (g["topk_ids"][32 * 16:] == -1).all() and np.isneginf(g["block_scores"][32 * 16:]).all()
+
+
+def test_lse_workload_4_nvfp4_150k(oracle):
+    _full(oracle, 4, sample=[5, 60], **LSE)

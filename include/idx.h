@@ -11,7 +11,9 @@
  *  [P1] sglang PR 45451, "packed decode score kernel", Modifications: a
  *       request's rows share one 16-row dot tile so each K tile loads once;
  *       each row keeps its own length mask; the packed form applies when
- *       packed_queries x gqa <= 16.
+ *       packed_queries x gqa <= 16 (wider packs and the many query rows of
+ *       a prefill chunk, which ATOM PR 2745's Summary scores with a prefill
+ *       block scorer, are cut into several tiles here).
  *  [P2] sglang PR 42614, "[AMD] MiniMax-M3 indexer CP: packed scoring for
  *       EAGLE verify rows", Modifications item 1: tile row i is (draft row
  *       i / gqa, head i % gqa); K is read up to the group's longest row while
@@ -54,7 +56,7 @@ enum {
   IDX_E_NULL = -1,   /* a required pointer is NULL                                  */
   IDX_E_FORMAT = -2, /* unknown k_format                                            */
   IDX_E_SHAPE = -3,  /* head_dim / block_size != 128, or a count out of range        */
-  IDX_E_PACK = -4,   /* packed_queries * gqa > 16: the rows do not fit one tile [P1] */
+  IDX_E_PACK = -4,   /* packed_queries * gqa > IDX_MAX_REQ_ROWS, or n_req * packed_queries * gqa > IDX_MAX_ROWS */
   IDX_E_TOPK = -5,   /* topk < 1, init/local < 0, or topk < init_blocks + local_blocks */
   IDX_E_LAUNCH = -6, /* the HIP runtime rejected a kernel launch                      */
   IDX_E_ALIGN = -7,  /* q, k, k_scale or staging not 16-byte aligned                  */
@@ -77,6 +79,13 @@ enum {
 #define IDX_MAX_BLOCKS 8192
 /* Largest n_req (graph pads included) one call accepts. */
 #define IDX_MAX_REQ 8192
+/* Largest packed_queries * gqa (rows of one request).  Up to 16 rows a
+ * request's rows form one tile that reads each K page once [P1]; above that
+ * (wide packs, the query rows of a prefill chunk) they are scored in tiles
+ * of 16 rows, 64 rows sharing each K page. */
+#define IDX_MAX_REQ_ROWS 65536
+/* Largest n_req * packed_queries * gqa (rows of one call). */
+#define IDX_MAX_ROWS (1 << 24)
 
 /*
  * Parameters of one indexer step (one layer, all requests of the batch).
@@ -117,7 +126,7 @@ typedef struct idx_params {
   int32_t n_req;          /* requests in the launch, graph pads included, <= IDX_MAX_REQ */
   int32_t n_slot_rows;    /* rows of block_table (the request table)         */
   int32_t packed_queries; /* draft rows per request, >= 1                    */
-  int32_t gqa;            /* index heads, >= 1; packed_queries*gqa <= 16     */
+  int32_t gqa;            /* index heads, >= 1; packed_queries*gqa <= IDX_MAX_REQ_ROWS */
   int32_t head_dim;       /* must be 128                                     */
   int32_t block_size;     /* must be 128                                     */
   int32_t max_blocks;     /* columns of block_table / block_scores, 0..IDX_MAX_BLOCKS */

@@ -165,7 +165,7 @@ static int check_params(const oracle_params* p) {
   if (p->head_dim != 128 || p->block_size != 128) return -1;
   if (p->k_format < ORACLE_K_BF16 || p->k_format > ORACLE_K_NVFP4) return -1;
   if (p->n_req < 0 || p->packed_queries < 1 || p->gqa < 1 || p->max_blocks < 0 ||
-      p->n_slot_rows < 0 || p->n_pages < 0 || p->packed_queries * p->gqa > 256)
+      p->n_slot_rows < 0 || p->n_pages < 0 || (int64_t)p->packed_queries * p->gqa > 65536)
     return -1;
   if (p->topk < 1 || p->init_blocks < 0 || p->local_blocks < 0 ||
       p->topk < p->init_blocks + p->local_blocks)
@@ -256,8 +256,8 @@ int oracle_score_packed(const oracle_params* p) {
     int slot = request_slot(p, r);
     const uint16_t* q = (const uint16_t*)p->q;
     int i, t, d;
-    double best[256];
-    int end[256];
+    double* best = (double*)malloc(sizeof(double) * (size_t)rows);
+    int* end = (int*)malloc(sizeof(int) * (size_t)rows);
     int64_t page = -1;
     int page_ok = 0, any = 0;
     int lse = p->score_mode == ORACLE_SCORE_LSE;
@@ -312,6 +312,8 @@ int oracle_score_packed(const oracle_params* p) {
       p->block_scores[((int64_t)r * rows + i) * MB + b] = out;
     }
     free(sv);
+    free(end);
+    free(best);
   }
   return 0;
 }

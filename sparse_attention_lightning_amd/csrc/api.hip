@@ -33,9 +33,12 @@ int check(const idx_params* p, int need) {
   if (p->packed_queries < 1 || p->gqa < 1)
     return fail(IDX_E_SHAPE, "packed_queries and gqa must be >= 1 (got %d, %d)",
                 p->packed_queries, p->gqa);
-  if ((int64_t)p->packed_queries * p->gqa > 16)
-    return fail(IDX_E_PACK, "packed_queries * gqa = %lld exceeds the 16-row tile",
-                (long long)p->packed_queries * p->gqa);
+  if ((int64_t)p->packed_queries * p->gqa > IDX_MAX_REQ_ROWS)
+    return fail(IDX_E_PACK, "packed_queries * gqa = %lld exceeds %d rows a request",
+                (long long)p->packed_queries * p->gqa, IDX_MAX_REQ_ROWS);
+  if ((int64_t)p->n_req * p->packed_queries * p->gqa > IDX_MAX_ROWS)
+    return fail(IDX_E_PACK, "n_req * packed_queries * gqa = %lld exceeds %d rows a call",
+                (long long)p->n_req * p->packed_queries * p->gqa, IDX_MAX_ROWS);
   if (p->n_req < 0 || p->n_slot_rows < 0 || p->n_pages < 0)
     return fail(IDX_E_SHAPE, "negative count (n_req %d, n_slot_rows %d, n_pages %lld)",
                 p->n_req, p->n_slot_rows, (long long)p->n_pages);

@@ -37,7 +37,8 @@ struct StepArgs {
   float sm_scale;      // lse only
 };
 
-hipError_t launch_score(const StepArgs& a, hipStream_t stream);
+hipError_t launch_score(const StepArgs& a, hipStream_t stream);       // any rows per request
+hipError_t launch_score_rows(const StepArgs& a, hipStream_t stream);  // more than 16 rows per request
 hipError_t launch_topk(const StepArgs& a, hipStream_t stream);
 hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t stride,
                             const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,
@@ -49,6 +50,9 @@ __device__ __forceinline__ int clamp_len(int32_t len, int max_blocks) {
 }
 
 __device__ __forceinline__ int blocks_of(int len) { return (len + kBlock - 1) / kBlock; }
+
+// A value every lane of the wave holds, as a scalar.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Lane permutation within DPP rows (16 lanes); CTRL is the DPP control word.
 template <int CTRL>

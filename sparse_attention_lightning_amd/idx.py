@@ -23,6 +23,8 @@ IDX_K_BF16, IDX_K_FP8_E4M3, IDX_K_NVFP4 = 0, 1, 2
 IDX_SCORE_MAX, IDX_SCORE_LSE = 0, 1
 IDX_MAX_BLOCKS = 8192
 IDX_MAX_REQ = 8192
+IDX_MAX_REQ_ROWS = 65536
+IDX_MAX_ROWS = 1 << 24
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error")
 
 

@@ -258,12 +258,13 @@ CONFIG_NAMES = {
     2: "16req_131k_fp8_straddle",
     3: "32req_524k_fp8_3pads",
     4: "64req_150k_nvfp4",
+    5: "4req_2k_prefill_32k_fp8",
 }
 
 
 def config(idx: int, device: str | torch.device = "cpu", local_blocks: int | None = None,
            n_real: int | None = None) -> Workload:
-    """Workload ``idx`` (0..4) with seed 1000 + idx.
+    """Workload ``idx`` (0..5) with seed 1000 + idx.
 
     ``local_blocks`` overrides the forced local window (the 0 variant of the
     straddling fp8 workload).  ``n_real`` keeps the first ``n_real`` request
@@ -289,6 +290,11 @@ def config(idx: int, device: str | torch.device = "cpu", local_blocks: int | Non
         lens = rng.integers(138240, 168957, size=64, endpoint=True)
         kw = dict(R=64, P=4, H=4, k_format=K_NVFP4, topk=64, init_blocks=1, local_blocks=2,
                   max_blocks=1320)
+    elif idx == 5:
+        # prefill chunks: 2,048 query rows a request at causal lengths L..L+2047
+        lens = rng.integers(30720, 30720 + 2048, size=4, endpoint=True)
+        kw = dict(R=4, P=2048, H=4, k_format=K_FP8_E4M3, topk=64, init_blocks=1, local_blocks=2,
+                  max_blocks=272)
     else:
         raise ValueError(idx)
     if local_blocks is not None:

@@ -524,6 +524,22 @@ def pin_packed_equals_per_row(o) -> None:
             assert same(rp[key], rr[key]), f"packed != per-row in {key}"
 
 
+def pin_many_rows_equal_per_row(o) -> None:
+    """Requests with many query rows (a prefill chunk: row j sees L + j
+    tokens, 4 heads, 300 rows a request) score exactly as each row run as its
+    own request, and the max scores match the brute force."""
+    w = W.make(name="pin_rows", R=2, P=75, H=4, k_format=W.K_FP8_E4M3, req_len=[700, 2000], topk=5,
+               init_blocks=1, local_blocks=2, seed=63, pads=1, pad_len=500)
+    a = w.oracle_args()
+    R, P, H = a["n_req"], a["packed_queries"], a["gqa"]
+    per = dict(a, n_req=R * P * H, packed_queries=1, gqa=1, q=a["q"].reshape(R * P * H, 128),
+               req_slot=np.repeat(a["req_slot"], P * H), row_len=np.repeat(a["row_len"], H))
+    rp, rr = o.step(**a), o.step(**per)
+    for key in rp:
+        assert same(rp[key], rr[key]), f"many rows != per-row in {key}"
+    compare_step(rp, brute.step(a, brute.pool_values(W.K_FP8_E4M3, a["k"])), "many rows")
+
+
 def _token_loc(a: dict, r: int, pos: int) -> int:
     slot = a["req_slot"][r]
     page = a["block_table"][slot, pos // 128]
@@ -600,6 +616,7 @@ PINS = [
     pin_bruteforce_bf16, pin_bruteforce_fp8, pin_bruteforce_fp4, pin_fp4_equals_bf16_of_dequant,
     pin_bruteforce_lse, pin_lse_closed_form, pin_lse_bounds,
     pin_topk_textbook, pin_topk_bruteforce, pin_topk_invariants, pin_exact_tie, pin_straddle,
-    pin_packed_equals_per_row, pin_masking, pin_slot_permutation, pin_graph_pads,
+    pin_packed_equals_per_row, pin_many_rows_equal_per_row, pin_masking, pin_slot_permutation,
+    pin_graph_pads,
     pin_scale_rounding, pin_code_rounding,
 ]

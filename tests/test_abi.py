@@ -54,8 +54,9 @@ REFUSALS = [
     ("head_dim", 64, I.IDX_E_SHAPE),
     ("block_size", 64, I.IDX_E_SHAPE),
     ("packed_queries", 0, I.IDX_E_SHAPE),
-    ("gqa", 17, I.IDX_E_PACK),
-    ("packed_queries", 5, I.IDX_E_PACK),
+    ("gqa", I.IDX_MAX_REQ_ROWS // 4 + 1, I.IDX_E_PACK),
+    ("packed_queries", I.IDX_MAX_REQ_ROWS // 4 + 1, I.IDX_E_PACK),
+    ("n_req", I.IDX_MAX_ROWS // 16 + 1, I.IDX_E_PACK),
     ("n_req", -1, I.IDX_E_SHAPE),
     ("n_pages", -2, I.IDX_E_SHAPE),
     ("max_blocks", I.IDX_MAX_BLOCKS + 1, I.IDX_E_SHAPE),
@@ -162,9 +163,11 @@ def test_fp4_store_empty_is_ok(lib):
 
 def test_binding_constants_match_header():
     text = (ROOT / "include" / "idx.h").read_text()
-    for name in ("IDX_MAX_BLOCKS", "IDX_MAX_REQ"):
+    for name in ("IDX_MAX_BLOCKS", "IDX_MAX_REQ", "IDX_MAX_REQ_ROWS"):
         m = re.search(rf"#define\s+{name}\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(I, name), name
+    m = re.search(r"#define\s+IDX_MAX_ROWS\s+\(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == I.IDX_MAX_ROWS
     enums = dict((k, int(v)) for k, v in re.findall(r"(IDX_\w+)\s*=\s*(-?\d+)", text))
     for k, v in enums.items():
         assert getattr(I, k) == v, k

@@ -231,14 +231,15 @@ def test_exact_tie_lower_id():
         assert b1 in ids and b2 not in ids
 
 
-def test_topk_synthetic_scores_exact(oracle):
+@pytest.mark.parametrize("R", [48, 1100], ids=["wg_per_row", "wave_per_row"])
+def test_topk_synthetic_scores_exact(oracle, R):
     """Selection alone on the same fp32 scores (many exact ties, NaN, -0):
-    ids and scores identical to the oracle's."""
+    ids and scores identical to the oracle's.  1,100 rows of at most 1,024
+    blocks take the one-wave-per-row kernel, 48 rows the workgroup kernel."""
     rng = np.random.default_rng(9)
     for MB, topk, init, local in [(40, 8, 1, 2), (300, 64, 1, 2), (1000, 64, 0, 0), (8192, 64, 3, 5),
-                                  (700, 1, 1, 0), (50, 50, 2, 2)]:
-        say("topk synthetic", MB, topk, init, local)
-        R = 48
+                                  (700, 1, 1, 0), (50, 50, 2, 2), (1024, 64, 1, 2)]:
+        say("topk synthetic", R, MB, topk, init, local)
         nb = rng.integers(0, MB + 1, size=R)
         nb[:3] = [MB, topk, topk + 1]
         vals = np.array([-1.0, 0.0, -0.0, 0.5, 1.0, 2.0, np.nan, -np.inf], np.float32)
@@ -455,3 +456,65 @@ def test_lse_workload_3_fp8_524k_pads(oracle):
 
 def test_lse_workload_4_nvfp4_150k(oracle):
     _full(oracle, 4, sample=[5, 60], **LSE)
+
+
+# ---------------------------------------------------------------------------
+# more than 16 rows a request: tiles of 16 rows, 64 sharing each K page (the
+# prefill scorer of ATOM PR 2745's Summary; wide packs).  Row j of a request
+# sees L + j tokens, which is the causal length of a prefill chunk's rows.
+# ---------------------------------------------------------------------------
+ROW_SHAPES = [  # (P, H, lens of the requests, topk, init, local, pads)
+    (5, 4, [300, 1022, 3000], 5, 1, 2, 1),      # 20 rows: one item, a partial wave
+    (32, 1, [129, 4000], 4, 1, 1, 0),           # 32 rows, one head
+    (100, 4, [5000, 64, 700], 8, 1, 2, 1),      # 400 rows: 7 row groups, causal extents
+    (3, 7, [2047, 2048, 2049], 6, 0, 3, 0),     # 21 rows, seven heads
+]
+
+
+@pytest.mark.parametrize("mode", ["max", "lse"])
+@pytest.mark.parametrize("fmt", [W.K_BF16, W.K_FP8_E4M3, W.K_NVFP4], ids=["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("shape", range(len(ROW_SHAPES)))
+def test_many_rows_shapes(oracle, fmt, shape, mode):
+    P, H, lens, topk, init, local, pads = ROW_SHAPES[shape]
+    say("many rows", fmt, mode, ROW_SHAPES[shape])
+    w = W.make(name="rows", R=len(lens), P=P, H=H, k_format=fmt, req_len=lens, topk=topk,
+               init_blocks=init, local_blocks=local, seed=400 + shape, pads=pads,
+               pad_len=3000, device="cuda")
+    if fmt == W.K_NVFP4:
+        Hn.gpu_fp4_store(w)
+        a = w.oracle_args(*Hn.oracle_pool(oracle, w))
+    else:
+        a = w.oracle_args()
+    m = LSE if mode == "lse" else {}
+    a = dict(a, **m)
+    Hn.assert_parity(Hn.gpu_step(w, **m), oracle.step(**a), a)
+
+
+def test_many_rows_equal_per_row():
+    """A request's 200 rows give bit-identical outputs to each row run as its
+    own request through the one-tile kernel."""
+    say("many rows == per-row")
+    w = W.make(name="rows_pr", R=2, P=50, H=4, k_format=W.K_FP8_E4M3, req_len=[900, 3000], topk=5,
+               init_blocks=1, local_blocks=2, seed=71, pads=1, pad_len=2000, device="cuda")
+    g = Hn.gpu_step(w)
+    R, P, H = w.n_req, 50, 4
+    per = W.Workload(**{**w.__dict__})
+    per.n_req, per.packed_queries, per.gqa = R * P * H, 1, 1
+    per.q = w.q.reshape(R * P * H, 1, 128).contiguous()
+    per.req_slot = w.req_slot.repeat_interleave(P * H).contiguous()
+    per.row_len = w.row_len.repeat_interleave(H).contiguous()
+    gp = Hn.gpu_step(per)
+    for key in g:
+        assert np.array_equal(g[key], gp[key], equal_nan=True), f"many rows != per-row ({key})"
+
+
+def test_many_rows_invalid_pages(oracle):
+    say("many rows, invalid page ids")
+    w = W.make(name="rows_bad", R=2, P=40, H=2, k_format=W.K_BF16, req_len=[1500, 900], topk=4,
+               init_blocks=1, local_blocks=1, seed=72, device="cuda")
+    w.block_table[int(w.req_slot[0]), 4] = w.n_pages + 9
+    w.block_table[int(w.req_slot[1]), 0] = -5
+    a = w.oracle_args()
+    g, o = Hn.gpu_step(w), oracle.step(**a)
+    assert np.isnan(o["block_scores"]).any()
+    Hn.assert_parity(g, o, a)

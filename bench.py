@@ -50,6 +50,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=None,
                     help="requests in the CPU-oracle sample (default: all real requests)")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="packed rows of the first request in the CPU-oracle sample when a request "
+                         "packs more than 16 rows (default 512)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MiB",
                     help="first run a plain device copy of this many MiB three times (a kernel of "
                          "known traffic, to scale hardware byte counters)")
@@ -253,14 +256,18 @@ def main() -> int:
         line["fp4_store_pool"] = pool_store
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests, mode)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests, args.cpu_rows, mode)
     print(json.dumps(line), flush=True)
     return 0
 
 
-def cpu_baseline(w, n_sample, mode) -> dict:
-    """The oracle, untuned, on the host cores: the step over the first
-    ``n_sample`` real requests (default all), scaled to one full step."""
+def cpu_baseline(w, n_sample, n_rows, mode) -> dict:
+    """The oracle, untuned, on the host cores, scaled to one full step.
+
+    Up to 16 rows a request: the step over the first ``n_sample`` real
+    requests (default all), scaled by request-tokens.  More rows a request
+    (prefill): the first ``n_rows`` packed rows of the first request, scaled
+    by the summed row lengths (the scoring work is linear in them)."""
     import numpy as np
 
     from oracle.binding import Oracle
@@ -268,26 +275,39 @@ def cpu_baseline(w, n_sample, mode) -> dict:
 
     o = Oracle()
     P, H = w.packed_queries, w.gqa
-    n = w.n_real if n_sample is None else min(n_sample, w.n_real)
-    sel = np.arange(n)
     if w.k_format == W.K_NVFP4:
         a = w.oracle_args(w.k.cpu().numpy(), w.k_scale.cpu().numpy())
     else:
         a = w.oracle_args()
-    q = a["q"].reshape(a["n_req"], P * H, 128)[sel].reshape(-1, H, 128)
-    sub = dict(a, **mode, n_req=n, q=np.ascontiguousarray(q), req_slot=np.ascontiguousarray(a["req_slot"][sel]),
-               row_len=np.ascontiguousarray(a["row_len"].reshape(a["n_req"], P)[sel].reshape(-1)))
+    R = a["n_req"]
+    q_all = a["q"].reshape(R, P * H, 128)
+    len_all = a["row_len"].reshape(R, P)
+    if P * H > 16:
+        n, p = 1, max(1, min(n_rows, P))
+        lw = len_all[: w.n_real].astype(np.int64)
+        frac = lw[0, :p].sum() / lw.sum()
+        what = f"score+top-k of the first {p} of {P} packed rows of request 0 ({w.n_real} requests)"
+        scale = "scaled by summed row lengths"
+    else:
+        n = w.n_real if n_sample is None else min(n_sample, w.n_real)
+        p = P
+        lmax = w.group_len()[: w.n_real].astype(np.int64)
+        frac = lmax[:n].sum() / lmax.sum()
+        what = (f"score+top-k of the first {n} of {w.n_real} requests "
+                f"({int(lmax[:n].sum())} request-tokens)")
+        scale = "scaled by token count"
+    q = q_all[:n, : p * H].reshape(-1, H, 128)
+    sub = dict(a, **mode, n_req=n, packed_queries=p, q=np.ascontiguousarray(q),
+               req_slot=np.ascontiguousarray(a["req_slot"][:n]),
+               row_len=np.ascontiguousarray(len_all[:n, :p].reshape(-1)))
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
         o.step(**sub)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    lmax = w.group_len()[: w.n_real].astype(np.int64)
-    frac = lmax[:n].sum() / lmax.sum()
-    return {"value": round(t / frac * 1e6, 1), "unit": "us", "cores": o.threads(), "kind": "oracle",
-            "sample": f"score+top-k of the first {n} of {w.n_real} requests "
-                      f"({int(lmax[:n].sum())} request-tokens), median of 3, scaled by token count"}
+    return {"value": round(float(t / frac) * 1e6, 1), "unit": "us", "cores": o.threads(),
+            "kind": "oracle", "sample": f"{what}, median of 3, {scale}"}
 
 
 if __name__ == "__main__":

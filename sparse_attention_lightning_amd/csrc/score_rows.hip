@@ -7,75 +7,81 @@
 // What is computed is the same as for the packed tile: row i of request r is
 // (query row i / gqa, head i % gqa) and scores each 128-token block under its
 // own length; only the work split differs.  A request's rows are cut into
-// groups of 256 (eight waves, each two 16-row tiles that share every decoded K
-// operand) and its blocks into chunks; an item is one (request, row group,
-// block chunk).  A workgroup stages each K page of its item in LDS once, and
-// the four waves score their tiles against it with the tile code of the
-// packed kernel, so a page crosses L2 once per 256 rows and the matrix cores,
-// not the memory, bound the kernel.  Pages reach LDS through a ring of
-// register buffers that keeps the next RING - 1 pages' loads in flight while
-// the waves score the current one; past the item's last page the ring loads
-// through empty descriptors, so the loop has no branches around its loads.
-// An item reads K only up to its longest row: with causal row lengths (a
-// prefill row at position p sees p + 1 tokens) items above the diagonal exit
-// at once.  Items are numbered request, then block chunk, then row group, and
-// each XCD takes a contiguous run of them, so the workgroups that read the
-// same K pages share an L2.  Each wave stages its rows' scores in LDS and
-// writes them out every 32 blocks as one 128-byte run per row.
+// groups of 512 (eight waves of 64 rows, four 16-row tiles each) and its
+// blocks into chunks; an item is one (request, row group, block chunk).
+//
+// A workgroup widens each K page of its item to bf16 once, as it copies the
+// page into LDS (fp8 e4m3 widens exactly; an NVFP4 value, e2m1 code times its
+// E4M3 group scale, has at most five fraction bits and is exact in bf16 too),
+// so every format is scored by the same bf16 MFMAs against the request's bf16
+// queries, and the eight waves share one decode.  Per 16-token tile and
+// 32-element k-step, one MFMA 16x16x32 takes the K tile as its A operand and
+// a 16-row query tile as B, so lane l = 16 g + n holds tokens 4g .. 4g+3 of
+// query row n: most of the max (or log-sum-exp) over a block is taken inside
+// the lane, and one exchange across the four lane groups leaves lane group g
+// with the block scores of tile g.  The four tiles of a wave share each K
+// operand read from LDS.
+//
+// Pages reach LDS through a ring of register buffers that keeps the next
+// RING - 1 pages' loads in flight while the waves score the current one; past
+// the item's last page the ring loads through empty descriptors, so the loop
+// has no branches around its loads.  An item reads K only up to its longest
+// row: with causal row lengths (a prefill row at position p sees p + 1
+// tokens) items above the diagonal exit at once.  Each XCD takes a contiguous
+// run of items, so the workgroups that read the same K pages share an L2.
+// Each wave stages its rows' scores in LDS and writes them out every 32 blocks
+// as one 128-byte run per row.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "tile.h"
 
 namespace idx {
 
 #ifndef IDX_ROWS_RING_BF16
-#define IDX_ROWS_RING_BF16 3  // pages in the register ring, bf16 K (16 VGPRs a page)
+#define IDX_ROWS_RING_BF16 2  // pages in the register ring, bf16 K (16 VGPRs a page)
 #endif
 #ifndef IDX_ROWS_RING_FP8
-#define IDX_ROWS_RING_FP8 6   // fp8 K (8 VGPRs a page)
+#define IDX_ROWS_RING_FP8 4   // fp8 K (8 VGPRs a page)
 #endif
 #ifndef IDX_ROWS_RING_FP4
-#define IDX_ROWS_RING_FP4 6   // NVFP4 K (8 VGPRs a page, with scales)
+#define IDX_ROWS_RING_FP4 4   // NVFP4 K (5 VGPRs a page, with scales)
 #endif
 constexpr int kRowWaves = 8;
 constexpr int kRowThreads = 64 * kRowWaves;
-constexpr int kWaveTiles = 2;                               // 16-row tiles a wave
-constexpr int kItemRows = kTileRows * kWaveTiles * kRowWaves;  // 256
-constexpr int kStageBlocks = 32;                            // blocks staged between write-outs
-constexpr int kMaxItemBlocks = 1024;                        // blocks of an item at most (page ids in LDS)
+constexpr int kWaveTiles = 4;                          // 16-row tiles a wave: one per lane group
+constexpr int kWaveRows = kTileRows * kWaveTiles;      // 64
+constexpr int kItemRows = kWaveRows * kRowWaves;       // 512
+constexpr int kStageBlocks = 32;                       // blocks staged between write-outs
+constexpr int kStagePitch = kStageBlocks + 1;          // words a staged row (odd: rows in different banks)
+constexpr int kMaxItemBlocks = 1024;                   // blocks of an item at most (page ids in LDS)
+constexpr int kPageUnits = kHeadDim * 2 / 16;          // 16-byte units of a bf16 token row
+constexpr int kPageStride = kPageUnits + 1;            // padded: the 16 lanes of a k-group hit different banks
 
 template <int FMT>
 constexpr int rows_ring() {
   return FMT == IDX_K_BF16 ? IDX_ROWS_RING_BF16 : FMT == IDX_K_FP8_E4M3 ? IDX_ROWS_RING_FP8 : IDX_ROWS_RING_FP4;
 }
 
-// One K page in LDS, in 16-byte units (typed so that every access is one
-// 16-byte LDS instruction): token rows padded by 16 bytes so that the 16
-// lanes of a k-group, which read 16 different tokens at one column, fall in
-// different banks.
-template <int FMT>
-struct PageLds {
-  static constexpr int kStride = Fmt<FMT>::kRowBytes / 16 + 1;  // 16-byte units per token row
-  u32x4 k[kBlock * kStride];
-  u32x4 sc[FMT == IDX_K_NVFP4 ? kBlock * 8 / 16 : 1];
-};
-
-template <int FMT>
+// LDS of a workgroup: two bf16 K pages in 16-byte units (typed so that each
+// access is one 16-byte LDS instruction), the waves' staged scores, the
+// item's page ids.
 struct RowsLds {
-  PageLds<FMT> page[2];
-  float stage[kRowWaves][kWaveTiles * kTileRows][kStageBlocks];
-  int32_t pid[kMaxItemBlocks];  // the item's page ids
+  u32x4 page[2][kBlock * kPageStride];
+  float stage[kRowWaves][kWaveRows * kStagePitch];
+  int32_t pid[kMaxItemBlocks];
   int32_t nbw[kRowWaves];
 };
 
 // A page's bytes in flight in registers: 16-byte pieces, consecutive threads
-// on consecutive pieces.
+// on consecutive pieces (bf16: 4 a thread, fp8: 2, NVFP4: 1 plus the two scale
+// bytes of its 32 values).
 template <int FMT>
 struct PageRegs {
   static constexpr int kPieces = kBlock * Fmt<FMT>::kRowBytes / 16 / kRowThreads;
   u32x4 v[kPieces];
-  u32x4 s;  // NVFP4: 16 bytes of the page's scale plane (threads < 64)
+  uint32_t s;
 };
 
 template <int FMT>
@@ -84,42 +90,148 @@ __device__ __forceinline__ void page_load(PageRegs<FMT>& pr, __amdgpu_buffer_rsr
 #pragma unroll
   for (int m = 0; m < PageRegs<FMT>::kPieces; ++m)
     pr.v[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * (tid + kRowThreads * m), 0, 0));
-  if constexpr (FMT == IDX_K_NVFP4)  // threads >= 64 read past the 1 KB plane: zeros, no memory touched
-    pr.s = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, 0, 0));
+  if constexpr (FMT == IDX_K_NVFP4)  // piece tid = token tid / 4, scale groups 2 (tid % 4), +1
+    pr.s = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * tid, 0, 0);
 }
 
+// Two fp8 bytes (byte pair HI of w) widened to a bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// The two e2m1 codes of byte SEL of w times the group scale, as a bf16 pair.
+// The products are exact in f32 and in bf16, so keeping the upper halves of
+// the f32 words is the exact conversion.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float scale) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  return __builtin_amdgcn_perm(__float_as_uint(v.y * scale), __float_as_uint(v.x * scale), 0x07060302u);
+}
+
+// Widen the page in flight to bf16 and write it to LDS page P.
 template <int FMT>
-__device__ __forceinline__ void page_store(const PageRegs<FMT>& pr, PageLds<FMT>& P, int tid) {
-  constexpr int kPerRow = Fmt<FMT>::kRowBytes / 16;  // pieces per token row
+__device__ __forceinline__ void page_store(const PageRegs<FMT>& pr, u32x4* P, int tid) {
+  if constexpr (FMT == IDX_K_BF16) {
 #pragma unroll
-  for (int m = 0; m < PageRegs<FMT>::kPieces; ++m) {
-    const int piece = tid + kRowThreads * m;
-    P.k[(piece / kPerRow) * PageLds<FMT>::kStride + piece % kPerRow] = pr.v[m];
+    for (int m = 0; m < PageRegs<FMT>::kPieces; ++m) {
+      const int piece = tid + kRowThreads * m;  // token piece / 16, unit piece % 16
+      P[(piece >> 4) * kPageStride + (piece & 15)] = pr.v[m];
+    }
+  } else if constexpr (FMT == IDX_K_FP8_E4M3) {
+#pragma unroll
+    for (int m = 0; m < PageRegs<FMT>::kPieces; ++m) {
+      const int piece = tid + kRowThreads * m;  // token piece / 8, dims 16 (piece % 8) ..
+      const u32x4 w = pr.v[m];
+      u32x4* dst = P + (piece >> 3) * kPageStride + 2 * (piece & 7);
+      dst[0] = u32x4{fp8_pair<false>(w.x), fp8_pair<true>(w.x), fp8_pair<false>(w.y), fp8_pair<true>(w.y)};
+      dst[1] = u32x4{fp8_pair<false>(w.z), fp8_pair<true>(w.z), fp8_pair<false>(w.w), fp8_pair<true>(w.w)};
+    }
+  } else {
+    // token tid / 4, dims 32 (tid % 4) ..: bytes 0-7 in scale group 2 (tid % 4), bytes 8-15 in the next
+    const float s0 = __builtin_amdgcn_cvt_scalef32_f32_fp8(pr.s, 1.0f, 0);
+    const float s1 = __builtin_amdgcn_cvt_scalef32_f32_fp8(pr.s, 1.0f, 1);
+    const u32x4 w = pr.v[0];
+    u32x4* dst = P + (tid >> 2) * kPageStride + 4 * (tid & 3);
+    dst[0] = u32x4{fp4_pair<0>(w.x, s0), fp4_pair<1>(w.x, s0), fp4_pair<2>(w.x, s0), fp4_pair<3>(w.x, s0)};
+    dst[1] = u32x4{fp4_pair<0>(w.y, s0), fp4_pair<1>(w.y, s0), fp4_pair<2>(w.y, s0), fp4_pair<3>(w.y, s0)};
+    dst[2] = u32x4{fp4_pair<0>(w.z, s1), fp4_pair<1>(w.z, s1), fp4_pair<2>(w.z, s1), fp4_pair<3>(w.z, s1)};
+    dst[3] = u32x4{fp4_pair<0>(w.w, s1), fp4_pair<1>(w.w, s1), fp4_pair<2>(w.w, s1), fp4_pair<3>(w.w, s1)};
   }
-  if constexpr (FMT == IDX_K_NVFP4)
-    if (tid < kBlock * 8 / 16) P.sc[tid] = pr.s;
 }
 
-// One lane's share of half page `half` from LDS, in the layout load_half
-// gives from HBM.
-template <int FMT>
-__device__ __forceinline__ void half_from_lds(Half<FMT>& h, const PageLds<FMT>& P, int half, int n, int g) {
-  const int tok0 = half * 64 + n;
+// The running block state of this lane's tokens, per tile: IDX_SCORE_MAX
+// keeps the max of q.k in m; IDX_SCORE_LSE the max m of v = c2 q.k and
+// s = sum of 2^(v - m).
+struct BlockState {
+  float m[kWaveTiles];
+  float s[kWaveTiles];
+};
+
+// Fold one half page's dot products (acc[u][t][e]: tile u's row n against
+// token 16 t + 4 g + e of the half, whose block position is pos0 + 16 t + e)
+// into the state.  len[u]: the length of tile u's row n.  FULL: every token
+// of the block is visible to every row of the wave (no masks).
+template <int MODE, bool FULL>
+__device__ __forceinline__ void fold_half(const f32x4 (*acc)[4], int pos0, const int* len, BlockState& st,
+                                          float c2) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int row = (tok0 + 16 * t) * PageLds<FMT>::kStride;
+  for (int u = 0; u < kWaveTiles; ++u) {
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < Fmt<FMT>::kLoads; ++i) h.v[t][i] = P.k[row + Fmt<FMT>::off(i, g) / 16];
-    if constexpr (FMT == IDX_K_NVFP4)
-      h.sc[t] = reinterpret_cast<const uint16_t*>(P.sc)[(tok0 + 16 * t) * 4 + g];
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * t + e] = (FULL || pos0 + 16 * t + e < len[u]) ? acc[u][t][e] : -INFINITY;
+    float am = v[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) am = fmaxf(am, v[i]);
+    if constexpr (MODE == IDX_SCORE_MAX) {
+      st.m[u] = fmaxf(st.m[u], am);
+    } else if constexpr (FULL) {
+      // every token visible: the new max is finite (c2 > 0, finite dots)
+      const float mnew = fmaxf(st.m[u], am * c2);
+      float sum = st.s[u] * __builtin_amdgcn_exp2f(st.m[u] - mnew);  // 0 while m is -inf
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(v[i], c2, -mnew));
+      st.s[u] = sum;
+      st.m[u] = mnew;
+    } else {
+      const float mnew = fmaxf(st.m[u], am * c2);  // -inf * c2 = -inf
+      const float base = (mnew == -INFINITY) ? 0.f : mnew;  // nothing visible yet: every term is 0
+      float sum = st.s[u] * __builtin_amdgcn_exp2f(st.m[u] - base);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(v[i] * c2 - base);
+      st.s[u] = sum;
+      st.m[u] = mnew;
+    }
+  }
+}
+
+// Two partial log-sum-exp states (max m, sum s of 2^(v - m)) merged.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  const float base = (mn == -INFINITY) ? 0.f : mn;
+  s = s * __builtin_amdgcn_exp2f(m - base) + s2 * __builtin_amdgcn_exp2f(m2 - base);
+  m = mn;
+}
+
+// Reduce per-tile values over the four lane groups (lanes n, n + 16, n + 32,
+// n + 48) so that lane group g ends with tile g's: two exchange steps, each
+// lane keeping half of what it holds and receiving the partner's copy of it.
+template <int MODE>
+__device__ __forceinline__ void group_reduce(BlockState& st, int g, float& m, float& s) {
+  const bool o1 = g & 1, o2 = g & 2;
+  float a_m[2], a_s[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // keep tiles (g & 1) and 2 + (g & 1), send the others
+    a_m[i] = o1 ? st.m[2 * i + 1] : st.m[2 * i];
+    const float rm = __shfl_xor(o1 ? st.m[2 * i] : st.m[2 * i + 1], 16);
+    if constexpr (MODE == IDX_SCORE_MAX) {
+      a_m[i] = fmaxf(a_m[i], rm);
+    } else {
+      a_s[i] = o1 ? st.s[2 * i + 1] : st.s[2 * i];
+      const float rs = __shfl_xor(o1 ? st.s[2 * i] : st.s[2 * i + 1], 16);
+      lse_merge(a_m[i], a_s[i], rm, rs);
+    }
+  }
+  // a[0]: tile g & 1, a[1]: tile 2 + (g & 1), over groups g, g ^ 1
+  m = o2 ? a_m[1] : a_m[0];
+  const float rm = __shfl_xor(o2 ? a_m[0] : a_m[1], 32);
+  if constexpr (MODE == IDX_SCORE_MAX) {
+    m = fmaxf(m, rm);
+    s = 0.f;
+  } else {
+    s = o2 ? a_s[1] : a_s[0];
+    const float rs = __shfl_xor(o2 ? a_s[0] : a_s[1], 32);
+    lse_merge(m, s, rm, rs);
   }
 }
 
 // One item (all threads of the workgroup; every early return is taken by the
 // whole workgroup).  G row groups a request, C chunks of CB blocks each.
 template <int FMT, int MODE>
-__device__ __forceinline__ void score_item(const StepArgs& a, RowsLds<FMT>& L, int item, int G, int C, int CB) {
-  typedef typename Fmt<FMT>::Op Op;
+__device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int item, int G, int C, int CB) {
   constexpr int kPageBytes = kBlock * Fmt<FMT>::kRowBytes;
   constexpr int D = rows_ring<FMT>();
   const int tid = threadIdx.x, lane = tid & 63;
@@ -129,26 +241,24 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds<FMT>& L, i
   const int PH = a.P * a.H, MB = a.max_blocks;
   const int slot = a.req_slot[r];
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
-  const int wrow0 = gi * kItemRows + kWaveTiles * kTileRows * wave;  // the wave's first row in the request
+  const int wrow0 = gi * kItemRows + kWaveRows * wave;  // the wave's first row in the request
 
-  // lengths of tile u: this lane's rows 4g + e, and row 4g + n for a writer
-  // lane (n < 4); rows past the request have none
+  // lengths: row n of each tile, and row 16 g + n (the row this lane scores
+  // out); rows past the request have none
   auto row_len = [&](int i) -> int {
     const int row = wrow0 + i;
     return (row < PH && !pad) ? clamp_len(a.row_len[r * a.P + row / a.H], MB) : 0;
   };
-  int len[kWaveTiles][4], my_len[kWaveTiles];
+  int len[kWaveTiles];
   int nbw = 0, lmin = INT_MAX;
 #pragma unroll
   for (int u = 0; u < kWaveTiles; ++u) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) len[u][e] = row_len(kTileRows * u + 4 * g + e);
-    my_len[u] = (n == 0) ? len[u][0] : (n == 1) ? len[u][1] : (n == 2) ? len[u][2] : len[u][3];
-    const int ln = row_len(kTileRows * u + n);
-    nbw = max(nbw, blocks_of(ln));
-    if (wrow0 + kTileRows * u + n < PH) lmin = min(lmin, ln);
+    len[u] = row_len(kTileRows * u + n);
+    nbw = max(nbw, blocks_of(len[u]));
+    if (wrow0 + kTileRows * u + n < PH) lmin = min(lmin, len[u]);
   }
-  // the wave's extent and its shortest real row (the fast path skips masks)
+  const int my_len = row_len(kTileRows * g + n);
+  // the wave's extent and its shortest real row (full blocks skip the masks)
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
     nbw = max(nbw, __shfl_xor(nbw, o));
@@ -166,7 +276,7 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds<FMT>& L, i
   // blocks no item covers (past the row group's longest row, every block of a
   // graph pad) get -inf from the chunk-0 workgroup of the row group
   if (c == 0) {
-    for (int i = 0; i < kWaveTiles * kTileRows; ++i) {
+    for (int i = 0; i < kWaveRows; ++i) {
       const int row = wrow0 + i;
       if (row >= PH) break;
       float* out = a.block_scores + ((int64_t)r * PH + row) * MB;
@@ -179,58 +289,24 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds<FMT>& L, i
   const bool active = wrow0 < PH;  // the wave has rows
   for (int j = tid; j < nblk; j += kRowThreads) L.pid[j] = a.block_table[(int64_t)slot * MB + b0 + j];
 
-  // the wave's query tiles (bf16, or f16 under 2^sigma for NVFP4; one sigma
-  // for both tiles)
-  Op qf[kWaveTiles][4];
-  int sigma = 0;
-  float c2 = 0.f;  // lse: sm_scale * log2 e * 2^-sigma
-  {
-    u32x4 pc[kWaveTiles][4];
+  // the wave's query tiles as B operands: row n of tile u, k-step s = dims
+  // d0(s, g) .. +8, the one-tile kernel's order for the format (the K operand
+  // reads the same dims), so both kernels sum the same products in the same
+  // order
+  bf16x8 qf[kWaveTiles][4];
 #pragma unroll
-    for (int u = 0; u < kWaveTiles; ++u)
+  for (int u = 0; u < kWaveTiles; ++u) {
+    const int row = wrow0 + kTileRows * u + n;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        pc[u][s] = u32x4{0u, 0u, 0u, 0u};
-        const int row = wrow0 + kTileRows * u + n;
-        if (row < PH)
-          pc[u][s] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                     ((int64_t)r * PH + row) * kHeadDim + Fmt<FMT>::d0(s, g));
-      }
-    if constexpr (FMT == IDX_K_NVFP4) {
-      float m = 0.f;
-#pragma unroll
-      for (int u = 0; u < kWaveTiles; ++u)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            m = fmaxf(m, fmaxf(fabsf(__uint_as_float(pc[u][s][w] << 16)),
-                               fabsf(__uint_as_float(pc[u][s][w] & 0xFFFF0000u))));
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-      if (m > 0.f) {
-        int ex;
-        frexpf(m, &ex);  // m < 2^ex
-        sigma = 15 - ex;
-      }
-#pragma unroll
-      for (int u = 0; u < kWaveTiles; ++u)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const _Float16 lo16 = (_Float16)ldexpf(__uint_as_float(pc[u][s][w] << 16), sigma);
-            const _Float16 hi16 = (_Float16)ldexpf(__uint_as_float(pc[u][s][w] & 0xFFFF0000u), sigma);
-            pc[u][s][w] = (uint32_t)__builtin_bit_cast(uint16_t, lo16) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, hi16) << 16);
-          }
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (row < PH)
+        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                            ((int64_t)r * PH + row) * kHeadDim + Fmt<FMT>::d0(s, g));
+      qf[u][s] = __builtin_bit_cast(bf16x8, v);
     }
-#pragma unroll
-    for (int u = 0; u < kWaveTiles; ++u)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qf[u][s] = __builtin_bit_cast(Op, pc[u][s]);
   }
-  if constexpr (MODE == IDX_SCORE_LSE) c2 = ldexpf(a.sm_scale * 1.44269504088896341f, -sigma);
+  const float c2 = (MODE == IDX_SCORE_LSE) ? a.sm_scale * 1.44269504088896341f : 0.f;
 
   // page j of the item: its id (-1 past the item) and descriptors
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k);
@@ -242,62 +318,90 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds<FMT>& L, i
     page_load<FMT>(pr, rk, rs, tid);
   };
 
-  const int wrow = 4 * g + n;  // lanes n < 4 hold row 4g + n of each tile
+  float* stage = L.stage[wave];
+  // tile T's K operands (16 tokens x the four k-steps) from LDS page P
+  auto k_ops = [&](const u32x4* P, int T, u32x4* ko) {
+    const u32x4* kr = P + (16 * T + n) * kPageStride;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ko[s] = kr[Fmt<FMT>::d0(s, g) / 8];
+  };
+  // the page's eight 16-token tiles against the wave's four query tiles
+  // (acc[u]: tile u's row n x tokens 16 T + 4 g .. +3), the next tile's K
+  // operands read while this one's MFMAs run; max folds each tile as it is
+  // done, lse a half page at a time (one rescaling exp per 16 values)
+  auto page_dots = [&](const u32x4* P, auto full_tag, int b, BlockState& st) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    u32x4 ko[2][4];
+    f32x4 acch[kWaveTiles][4];
+    k_ops(P, 0, ko[0]);
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      if (T + 1 < 8) k_ops(P, T + 1, ko[(T + 1) & 1]);
+      f32x4 acc[kWaveTiles];
+#pragma unroll
+      for (int u = 0; u < kWaveTiles; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < kWaveTiles; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ko[T & 1][s]), qf[u][s],
+                                                           acc[u], 0, 0, 0);
+      const int pos0 = b * kBlock + 16 * T + 4 * g;  // block position of acc[u][0]
+      if constexpr (MODE == IDX_SCORE_MAX) {
+#pragma unroll
+        for (int u = 0; u < kWaveTiles; ++u) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (FULL || pos0 + e < len[u]) ? acc[u][e] : -INFINITY;
+          st.m[u] = fmaxf(fmaxf(st.m[u], fmaxf(v[0], v[1])), fmaxf(v[2], v[3]));
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kWaveTiles; ++u) acch[u][T & 3] = acc[u];
+        if ((T & 3) == 3) fold_half<MODE, FULL>(acch, pos0 - 48, len, st, c2);
+      }
+    }
+  };
   auto score_page = [&](int k, int pid) {
     const int b = b0 + k;
-    const PageLds<FMT>& P = L.page[k & 1];
-    float st0[kWaveTiles][4], st1[kWaveTiles][4];
-#pragma unroll
-    for (int u = 0; u < kWaveTiles; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        st0[u][e] = -INFINITY;
-        st1[u][e] = 0.f;
-      }
-    const bool full = (b + 1) * kBlock <= lmin;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      Half<FMT> h;
-      half_from_lds<FMT>(h, P, half, n, g);
-      f32x4 acc[kWaveTiles][4];
-      half_dot<FMT, kWaveTiles>(h, qf, acc);
-#pragma unroll
-      for (int u = 0; u < kWaveTiles; ++u)
-        fold<MODE>(acc[u], full, b * kBlock + 64 * half + n, len[u], st0[u], st1[u], c2);
-    }
-    const bool ok = pid >= 0 && pid < a.n_pages;
+    const u32x4* P = L.page[k & 1];
+    BlockState st;
 #pragma unroll
     for (int u = 0; u < kWaveTiles; ++u) {
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float m = row16_max(st0[u][e]);
-        if constexpr (MODE == IDX_SCORE_MAX) {
-          v[e] = m;
-        } else {
-          const float base = (m == -INFINITY) ? 0.f : m;
-          const float sum = row16_sum(st1[u][e] * __builtin_amdgcn_exp2f(st0[u][e] - base));
-          v[e] = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(sum)) * 0.693147180559945309f;
-        }
-      }
-      float o = (n == 0) ? v[0] : (n == 1) ? v[1] : (n == 2) ? v[2] : v[3];
-      if constexpr (FMT == IDX_K_NVFP4 && MODE == IDX_SCORE_MAX) o = ldexpf(o, -sigma);
-      if (!ok) o = (b * kBlock < my_len[u]) ? __builtin_nanf("") : -INFINITY;
-      if (n < 4) L.stage[wave][kTileRows * u + wrow][k % kStageBlocks] = o;
+      st.m[u] = -INFINITY;
+      st.s[u] = 0.f;
     }
-    // every 32 blocks, and after the last: the wave's rows out as runs
+    // a wave-uniform branch: blocks every row of the wave sees whole skip
+    // the per-token masks
+    if ((b + 1) * kBlock <= lmin)
+      page_dots(P, std::true_type{}, b, st);
+    else
+      page_dots(P, std::false_type{}, b, st);
+    float m, s;
+    group_reduce<MODE>(st, g, m, s);
+    float o;
+    if constexpr (MODE == IDX_SCORE_MAX)
+      o = m;
+    else
+      o = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(s)) * 0.693147180559945309f;
+    const bool ok = pid >= 0 && pid < a.n_pages;
+    if (!ok) o = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
+    stage[(kTileRows * g + n) * kStagePitch + k % kStageBlocks] = o;
+    // every 32 blocks, and after the last: the wave's rows out as runs, two
+    // rows an instruction
     if (k % kStageBlocks == kStageBlocks - 1 || k == nblk - 1) {
       const int k0 = k - k % kStageBlocks, cnt = k - k0 + 1;
-      for (int i = 0; i < kWaveTiles * kTileRows; ++i) {
-        const int row = wrow0 + i;
-        if (row >= PH) break;
-        if (lane < cnt) a.block_scores[((int64_t)r * PH + row) * MB + b0 + k0 + lane] = L.stage[wave][i][lane];
+      const int col = lane & 31;
+      for (int i = 0; i < kWaveRows; i += 2) {
+        const int ri = i + (lane >> 5), row = wrow0 + ri;
+        if (row < PH && col < cnt)
+          a.block_scores[((int64_t)r * PH + row) * MB + b0 + k0 + col] = stage[ri * kStagePitch + col];
       }
     }
   };
 
   // the ring: slot u holds page k (k % D == u) from its issue D - 1 steps
-  // ahead until it is copied to LDS buffer k & 1
+  // ahead until it is widened into LDS page k & 1
   __syncthreads();  // page ids
   PageRegs<FMT> ring[D];
 #pragma unroll
@@ -323,7 +427,7 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds<FMT>& L, i
 // XCD (w, w + 8, ... when the grid is a multiple of 8) take a contiguous run.
 template <int FMT, int MODE>
 __global__ __launch_bounds__(kRowThreads) void rows_kernel(const StepArgs a, int G, int C, int CB, int M) {
-  __shared__ RowsLds<FMT> L;
+  __shared__ RowsLds L;
   const int per = (M + 7) / 8;
   for (int x = blockIdx.x; x < 8 * per; x += gridDim.x) {
     const int item = (x % 8) * per + x / 8;

@@ -25,12 +25,15 @@
 // Pages reach LDS through a ring of register buffers that keeps the next
 // RING - 1 pages' loads in flight while the waves score the current one; past
 // the item's last page the ring loads through empty descriptors, so the loop
-// has no branches around its loads.  An item reads K only up to its longest
-// row: with causal row lengths (a prefill row at position p sees p + 1
-// tokens) items above the diagonal exit at once.  Each XCD takes a contiguous
-// run of items, so the workgroups that read the same K pages share an L2.
-// Each wave stages its rows' scores in LDS and writes them out every 32 blocks
-// as one 128-byte run per row.
+// has no branches around its loads.  The next page's copy into the second LDS
+// buffer runs among the current page's MFMAs.  An item reads K only up to its
+// longest row (with causal row lengths, a prefill row at position p sees
+// p + 1 tokens, items above the diagonal exit at once) and the C chunks of a
+// row group split that extent evenly, so the chunks of a row group are equal
+// however long its rows are.  Each XCD takes a contiguous run of items, so
+// the workgroups that read the same K pages share an L2.  Each wave stages its
+// rows' scores in LDS and writes them out every 32 blocks as one 128-byte run
+// per row.
 #include <algorithm>
 #include <climits>
 #include <type_traits>
@@ -48,16 +51,35 @@ namespace idx {
 #ifndef IDX_ROWS_RING_FP4
 #define IDX_ROWS_RING_FP4 4   // NVFP4 K (5 VGPRs a page, with scales)
 #endif
+#ifndef IDX_ROWS_STORE_AT
+#define IDX_ROWS_STORE_AT 3   // max: the next page is copied to LDS after this 16-token tile (0..7);
+                              // lse: after the page (its half-page accumulators leave no registers)
+#endif
+
+#ifndef IDX_ROWS_ITEMS
+#define IDX_ROWS_ITEMS 1      // items per resident workgroup the block chunks aim at
+#endif
+// Eight waves of four tiles: two waves a SIMD share the matrix core (one
+// wave of eight tiles a SIMD measured a third slower: it cannot keep the
+// core busy through its own waits).
 constexpr int kRowWaves = 8;
 constexpr int kRowThreads = 64 * kRowWaves;
-constexpr int kWaveTiles = 4;                          // 16-row tiles a wave: one per lane group
-constexpr int kWaveRows = kTileRows * kWaveTiles;      // 64
-constexpr int kItemRows = kWaveRows * kRowWaves;       // 512
+constexpr int kWaveTiles = 4;                          // lane group g ends with tiles g, g + 4, ...
+constexpr int kWaveRows = kTileRows * kWaveTiles;
+constexpr int kItemRows = kWaveRows * kRowWaves;
+static_assert(kWaveTiles % 4 == 0, "tiles a wave: a multiple of the four lane groups");
 constexpr int kStageBlocks = 32;                       // blocks staged between write-outs
 constexpr int kStagePitch = kStageBlocks + 1;          // words a staged row (odd: rows in different banks)
 constexpr int kMaxItemBlocks = 1024;                   // blocks of an item at most (page ids in LDS)
-constexpr int kPageUnits = kHeadDim * 2 / 16;          // 16-byte units of a bf16 token row
-constexpr int kPageStride = kPageUnits + 1;            // padded: the 16 lanes of a k-group hit different banks
+constexpr int kPageUnits = kHeadDim * 2 / 16;          // 16-byte units of a bf16 token row (16)
+
+// LDS slot of 16-byte unit `unit` of token `tok` in a page: rows of 256 bytes,
+// the unit index XORed with the token's low four bits.  Sixteen lanes that
+// read one unit of sixteen consecutive tokens (the MFMA operand reads), or
+// the units of one row (the page copy), then touch sixteen different bank
+// groups; padding the rows by 16 bytes instead measured about four conflict
+// cycles per 16-byte read on gfx950.
+__device__ __forceinline__ int page_slot(int tok, int unit) { return tok * kPageUnits + (unit ^ (tok & 15)); }
 
 template <int FMT>
 constexpr int rows_ring() {
@@ -68,7 +90,7 @@ constexpr int rows_ring() {
 // access is one 16-byte LDS instruction), the waves' staged scores, the
 // item's page ids.
 struct RowsLds {
-  u32x4 page[2][kBlock * kPageStride];
+  u32x4 page[2][kBlock * kPageUnits];
   float stage[kRowWaves][kWaveRows * kStagePitch];
   int32_t pid[kMaxItemBlocks];
   int32_t nbw[kRowWaves];
@@ -117,29 +139,46 @@ __device__ __forceinline__ void page_store(const PageRegs<FMT>& pr, u32x4* P, in
 #pragma unroll
     for (int m = 0; m < PageRegs<FMT>::kPieces; ++m) {
       const int piece = tid + kRowThreads * m;  // token piece / 16, unit piece % 16
-      P[(piece >> 4) * kPageStride + (piece & 15)] = pr.v[m];
+      P[page_slot(piece >> 4, piece & 15)] = pr.v[m];
     }
   } else if constexpr (FMT == IDX_K_FP8_E4M3) {
 #pragma unroll
     for (int m = 0; m < PageRegs<FMT>::kPieces; ++m) {
       const int piece = tid + kRowThreads * m;  // token piece / 8, dims 16 (piece % 8) ..
       const u32x4 w = pr.v[m];
-      u32x4* dst = P + (piece >> 3) * kPageStride + 2 * (piece & 7);
-      dst[0] = u32x4{fp8_pair<false>(w.x), fp8_pair<true>(w.x), fp8_pair<false>(w.y), fp8_pair<true>(w.y)};
-      dst[1] = u32x4{fp8_pair<false>(w.z), fp8_pair<true>(w.z), fp8_pair<false>(w.w), fp8_pair<true>(w.w)};
+      const int tok = piece >> 3, u0 = 2 * (piece & 7);
+      P[page_slot(tok, u0)] = u32x4{fp8_pair<false>(w.x), fp8_pair<true>(w.x), fp8_pair<false>(w.y), fp8_pair<true>(w.y)};
+      P[page_slot(tok, u0 + 1)] =
+          u32x4{fp8_pair<false>(w.z), fp8_pair<true>(w.z), fp8_pair<false>(w.w), fp8_pair<true>(w.w)};
     }
   } else {
+    static_assert(kBlock * Fmt<IDX_K_NVFP4>::kRowBytes == 16 * kRowThreads, "one 16-byte NVFP4 piece a thread");
     // token tid / 4, dims 32 (tid % 4) ..: bytes 0-7 in scale group 2 (tid % 4), bytes 8-15 in the next
     const float s0 = __builtin_amdgcn_cvt_scalef32_f32_fp8(pr.s, 1.0f, 0);
     const float s1 = __builtin_amdgcn_cvt_scalef32_f32_fp8(pr.s, 1.0f, 1);
     const u32x4 w = pr.v[0];
-    u32x4* dst = P + (tid >> 2) * kPageStride + 4 * (tid & 3);
-    dst[0] = u32x4{fp4_pair<0>(w.x, s0), fp4_pair<1>(w.x, s0), fp4_pair<2>(w.x, s0), fp4_pair<3>(w.x, s0)};
-    dst[1] = u32x4{fp4_pair<0>(w.y, s0), fp4_pair<1>(w.y, s0), fp4_pair<2>(w.y, s0), fp4_pair<3>(w.y, s0)};
-    dst[2] = u32x4{fp4_pair<0>(w.z, s1), fp4_pair<1>(w.z, s1), fp4_pair<2>(w.z, s1), fp4_pair<3>(w.z, s1)};
-    dst[3] = u32x4{fp4_pair<0>(w.w, s1), fp4_pair<1>(w.w, s1), fp4_pair<2>(w.w, s1), fp4_pair<3>(w.w, s1)};
+    const int tok = tid >> 2, u0 = 4 * (tid & 3);
+    P[page_slot(tok, u0)] = u32x4{fp4_pair<0>(w.x, s0), fp4_pair<1>(w.x, s0), fp4_pair<2>(w.x, s0), fp4_pair<3>(w.x, s0)};
+    P[page_slot(tok, u0 + 1)] =
+        u32x4{fp4_pair<0>(w.y, s0), fp4_pair<1>(w.y, s0), fp4_pair<2>(w.y, s0), fp4_pair<3>(w.y, s0)};
+    P[page_slot(tok, u0 + 2)] =
+        u32x4{fp4_pair<0>(w.z, s1), fp4_pair<1>(w.z, s1), fp4_pair<2>(w.z, s1), fp4_pair<3>(w.z, s1)};
+    P[page_slot(tok, u0 + 3)] =
+        u32x4{fp4_pair<0>(w.w, s1), fp4_pair<1>(w.w, s1), fp4_pair<2>(w.w, s1), fp4_pair<3>(w.w, s1)};
   }
 }
+
+// max(a, b) as the median of (a, b, +inf): a NaN operand is dropped as fmaxf
+// drops it, and MFMA results need no canonicalizing first (an fmaxf on them
+// costs one extra VALU op per value).  The +inf comes from a scalar move the
+// compiler cannot see through; with a literal it turns the median back into
+// fmaxf.
+__device__ __forceinline__ float opaque_inf() {
+  float x;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(x));
+  return x;
+}
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, opaque_inf()); }
 
 // The running block state of this lane's tokens, per tile: IDX_SCORE_MAX
 // keeps the max of q.k in m; IDX_SCORE_LSE the max m of v = c2 q.k and
@@ -165,7 +204,7 @@ __device__ __forceinline__ void fold_half(const f32x4 (*acc)[4], int pos0, const
       for (int e = 0; e < 4; ++e) v[4 * t + e] = (FULL || pos0 + 16 * t + e < len[u]) ? acc[u][t][e] : -INFINITY;
     float am = v[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) am = fmaxf(am, v[i]);
+    for (int i = 1; i < 16; ++i) am = max2(am, v[i]);
     if constexpr (MODE == IDX_SCORE_MAX) {
       st.m[u] = fmaxf(st.m[u], am);
     } else if constexpr (FULL) {
@@ -196,42 +235,56 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
-// Reduce per-tile values over the four lane groups (lanes n, n + 16, n + 32,
-// n + 48) so that lane group g ends with tile g's: two exchange steps, each
-// lane keeping half of what it holds and receiving the partner's copy of it.
-template <int MODE>
-__device__ __forceinline__ void group_reduce(BlockState& st, int g, float& m, float& s) {
+// The value lane l ^ 16 (x16) or l ^ 32 (x32) holds, through the gfx950 lane
+// swaps (VALU, no LDS round trip): a swap of v with itself leaves the partner
+// row's copy in the second result on lanes 0-15 and 32-47 (x16) or 0-31
+// (x32), and in the first on the others.
+__device__ __forceinline__ float x16(float v, int g) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((g & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float x32(float v, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((g & 2) ? r[0] : r[1]);
+}
+
+// Reduce the values of tiles Q .. Q+3 over the four lane groups (lanes n,
+// n + 16, n + 32, n + 48) so that lane group g ends with tile Q + g's: two
+// exchange steps, each lane keeping half of what it holds and receiving the
+// partner's copy of it.
+template <int MODE, int Q>
+__device__ __forceinline__ void group_reduce(const BlockState& st, int g, float& m, float& s) {
   const bool o1 = g & 1, o2 = g & 2;
   float a_m[2], a_s[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {  // keep tiles (g & 1) and 2 + (g & 1), send the others
-    a_m[i] = o1 ? st.m[2 * i + 1] : st.m[2 * i];
-    const float rm = __shfl_xor(o1 ? st.m[2 * i] : st.m[2 * i + 1], 16);
+  for (int i = 0; i < 2; ++i) {  // keep tiles Q + (g & 1) and Q + 2 + (g & 1), send the others
+    a_m[i] = o1 ? st.m[Q + 2 * i + 1] : st.m[Q + 2 * i];
+    const float rm = x16(o1 ? st.m[Q + 2 * i] : st.m[Q + 2 * i + 1], g);
     if constexpr (MODE == IDX_SCORE_MAX) {
       a_m[i] = fmaxf(a_m[i], rm);
     } else {
-      a_s[i] = o1 ? st.s[2 * i + 1] : st.s[2 * i];
-      const float rs = __shfl_xor(o1 ? st.s[2 * i] : st.s[2 * i + 1], 16);
+      a_s[i] = o1 ? st.s[Q + 2 * i + 1] : st.s[Q + 2 * i];
+      const float rs = x16(o1 ? st.s[Q + 2 * i] : st.s[Q + 2 * i + 1], g);
       lse_merge(a_m[i], a_s[i], rm, rs);
     }
   }
   // a[0]: tile g & 1, a[1]: tile 2 + (g & 1), over groups g, g ^ 1
   m = o2 ? a_m[1] : a_m[0];
-  const float rm = __shfl_xor(o2 ? a_m[0] : a_m[1], 32);
+  const float rm = x32(o2 ? a_m[0] : a_m[1], g);
   if constexpr (MODE == IDX_SCORE_MAX) {
     m = fmaxf(m, rm);
     s = 0.f;
   } else {
     s = o2 ? a_s[1] : a_s[0];
-    const float rs = __shfl_xor(o2 ? a_s[0] : a_s[1], 32);
+    const float rs = x32(o2 ? a_s[0] : a_s[1], g);
     lse_merge(m, s, rm, rs);
   }
 }
 
 // One item (all threads of the workgroup; every early return is taken by the
-// whole workgroup).  G row groups a request, C chunks of CB blocks each.
+// whole workgroup).  G row groups a request, C block chunks a row group.
 template <int FMT, int MODE>
-__device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int item, int G, int C, int CB) {
+__device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int item, int G, int C) {
   constexpr int kPageBytes = kBlock * Fmt<FMT>::kRowBytes;
   constexpr int D = rows_ring<FMT>();
   const int tid = threadIdx.x, lane = tid & 63;
@@ -257,7 +310,9 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
     nbw = max(nbw, blocks_of(len[u]));
     if (wrow0 + kTileRows * u + n < PH) lmin = min(lmin, len[u]);
   }
-  const int my_len = row_len(kTileRows * g + n);
+  int my_len[kWaveTiles / 4];  // row 16 (4 q + g) + n, scored out by this lane
+#pragma unroll
+  for (int q = 0; q < kWaveTiles / 4; ++q) my_len[q] = row_len(kTileRows * (4 * q + g) + n);
   // the wave's extent and its shortest real row (full blocks skip the masks)
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
@@ -283,9 +338,12 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
       for (int b = nb_item + lane; b < MB; b += 64) out[b] = -INFINITY;
     }
   }
-  const int b0 = c * CB;
-  if (b0 >= nb_item) return;
-  const int nblk = min(CB, nb_item - b0);
+  // chunk c of C: an even share of the row group's own extent, so the items
+  // of a row group do the same work whatever its rows' lengths (at most
+  // kMaxItemBlocks blocks: the launch makes ceil(max_blocks / C) no more)
+  const int b0 = (int)((int64_t)c * nb_item / C);
+  const int nblk = (int)((int64_t)(c + 1) * nb_item / C) - b0;
+  if (nblk <= 0) return;
   const bool active = wrow0 < PH;  // the wave has rows
   for (int j = tid; j < nblk; j += kRowThreads) L.pid[j] = a.block_table[(int64_t)slot * MB + b0 + j];
 
@@ -321,15 +379,14 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   float* stage = L.stage[wave];
   // tile T's K operands (16 tokens x the four k-steps) from LDS page P
   auto k_ops = [&](const u32x4* P, int T, u32x4* ko) {
-    const u32x4* kr = P + (16 * T + n) * kPageStride;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ko[s] = kr[Fmt<FMT>::d0(s, g) / 8];
+    for (int s = 0; s < 4; ++s) ko[s] = P[page_slot(16 * T + n, Fmt<FMT>::d0(s, g) / 8)];
   };
   // the page's eight 16-token tiles against the wave's four query tiles
   // (acc[u]: tile u's row n x tokens 16 T + 4 g .. +3), the next tile's K
   // operands read while this one's MFMAs run; max folds each tile as it is
   // done, lse a half page at a time (one rescaling exp per 16 values)
-  auto page_dots = [&](const u32x4* P, auto full_tag, int b, BlockState& st) {
+  auto page_dots = [&](const u32x4* P, auto full_tag, int b, BlockState& st, auto&& mid) {
     constexpr bool FULL = decltype(full_tag)::value;
     u32x4 ko[2][4];
     f32x4 acch[kWaveTiles][4];
@@ -353,16 +410,20 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (FULL || pos0 + e < len[u]) ? acc[u][e] : -INFINITY;
-          st.m[u] = fmaxf(fmaxf(st.m[u], fmaxf(v[0], v[1])), fmaxf(v[2], v[3]));
+          st.m[u] = max2(st.m[u], max2(max2(v[0], v[1]), max2(v[2], v[3])));
         }
       } else {
 #pragma unroll
         for (int u = 0; u < kWaveTiles; ++u) acch[u][T & 3] = acc[u];
         if ((T & 3) == 3) fold_half<MODE, FULL>(acch, pos0 - 48, len, st, c2);
       }
+      if constexpr (MODE == IDX_SCORE_MAX)
+        if (T == IDX_ROWS_STORE_AT) mid();
     }
   };
-  auto score_page = [&](int k, int pid) {
+  // mid(): the next page's copy into the other LDS buffer, placed among this
+  // page's MFMAs so that its conversions and LDS writes overlap them
+  auto score_page = [&](int k, int pid, auto&& mid) {
     const int b = b0 + k;
     const u32x4* P = L.page[k & 1];
     BlockState st;
@@ -374,19 +435,25 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
     // a wave-uniform branch: blocks every row of the wave sees whole skip
     // the per-token masks
     if ((b + 1) * kBlock <= lmin)
-      page_dots(P, std::true_type{}, b, st);
+      page_dots(P, std::true_type{}, b, st, mid);
     else
-      page_dots(P, std::false_type{}, b, st);
-    float m, s;
-    group_reduce<MODE>(st, g, m, s);
-    float o;
-    if constexpr (MODE == IDX_SCORE_MAX)
-      o = m;
-    else
-      o = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(s)) * 0.693147180559945309f;
+      page_dots(P, std::false_type{}, b, st, mid);
     const bool ok = pid >= 0 && pid < a.n_pages;
-    if (!ok) o = (b * kBlock < my_len) ? __builtin_nanf("") : -INFINITY;
-    stage[(kTileRows * g + n) * kStagePitch + k % kStageBlocks] = o;
+    auto out = [&](auto q_tag) {
+      constexpr int q = decltype(q_tag)::value;
+      float m, s;
+      group_reduce<MODE, 4 * q>(st, g, m, s);
+      float o;
+      if constexpr (MODE == IDX_SCORE_MAX)
+        o = m;
+      else
+        o = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(s)) * 0.693147180559945309f;
+      if (!ok) o = (b * kBlock < my_len[q]) ? __builtin_nanf("") : -INFINITY;
+      stage[(kTileRows * (4 * q + g) + n) * kStagePitch + k % kStageBlocks] = o;
+    };
+    out(std::integral_constant<int, 0>{});
+    if constexpr (kWaveTiles > 4) out(std::integral_constant<int, 1>{});
+    static_assert(kWaveTiles <= 8, "tiles a wave: at most 8");
     // every 32 blocks, and after the last: the wave's rows out as runs, two
     // rows an instruction
     if (k % kStageBlocks == kStageBlocks - 1 || k == nblk - 1) {
@@ -398,6 +465,7 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
           a.block_scores[((int64_t)r * PH + row) * MB + b0 + k0 + col] = stage[ri * kStagePitch + col];
       }
     }
+    if constexpr (MODE == IDX_SCORE_LSE) mid();
   };
 
   // the ring: slot u holds page k (k % D == u) from its issue D - 1 steps
@@ -415,8 +483,11 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
       const int pid = page_of(k);
       if (u == 0 || k < nblk) {  // (u == 0: k < nblk by the loop bound)
         issue(ring[u], page_of(k + D));  // slot u's page k is in LDS already
-        if (active) score_page(k, pid);
-        page_store<FMT>(ring[(u + 1) % D], L.page[(k + 1) & 1], tid);
+        auto store_next = [&] { page_store<FMT>(ring[(u + 1) % D], L.page[(k + 1) & 1], tid); };
+        if (active)
+          score_page(k, pid, store_next);
+        else
+          store_next();
       }
       __syncthreads();
     }
@@ -426,12 +497,12 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
 // A resident grid walks the M = n_req * C * G items; the workgroups of each
 // XCD (w, w + 8, ... when the grid is a multiple of 8) take a contiguous run.
 template <int FMT, int MODE>
-__global__ __launch_bounds__(kRowThreads) void rows_kernel(const StepArgs a, int G, int C, int CB, int M) {
+__global__ __launch_bounds__(kRowThreads) void rows_kernel(const StepArgs a, int G, int C, int M) {
   __shared__ RowsLds L;
   const int per = (M + 7) / 8;
   for (int x = blockIdx.x; x < 8 * per; x += gridDim.x) {
     const int item = (x % 8) * per + x / 8;
-    if (item < M) score_item<FMT, MODE>(a, L, item, G, C, CB);
+    if (item < M) score_item<FMT, MODE>(a, L, item, G, C);
     __syncthreads();  // LDS free for the next item
   }
 }
@@ -458,18 +529,17 @@ template <int FMT, int MODE>
 void launch_rows(const StepArgs& a, hipStream_t stream) {
   const int PH = a.P * a.H;
   const int G = (PH + kItemRows - 1) / kItemRows;
-  // block chunks: about two items per resident workgroup (an item loads its
-  // query tiles and page ids once, so items should not be short), at most
-  // kMaxItemBlocks blocks each
+  // block chunks: about IDX_ROWS_ITEMS items per resident workgroup (an item
+  // loads its query tiles and page ids and fills its ring once, so items
+  // should not be short), at most kMaxItemBlocks blocks each
   const int slots = rows_resident<FMT, MODE>();
   const int64_t groups = (int64_t)a.n_req * G;
-  const int64_t want = std::max<int64_t>(1, (2 * (int64_t)slots + groups - 1) / groups);
+  const int64_t want = std::max<int64_t>(1, (IDX_ROWS_ITEMS * (int64_t)slots + groups - 1) / groups);
   const int CB = (int)std::min<int64_t>(kMaxItemBlocks, std::max<int64_t>(1, (a.max_blocks + want - 1) / want));
   const int C = (a.max_blocks + CB - 1) / CB;
   const int64_t M = groups * C;
   const int64_t grid = std::min<int64_t>(8 * ((M + 7) / 8), 8 * ((slots + 7) / 8));
-  hipLaunchKernelGGL((rows_kernel<FMT, MODE>), dim3((unsigned)grid), dim3(kRowThreads), 0, stream, a, G, C, CB,
-                     (int)M);
+  hipLaunchKernelGGL((rows_kernel<FMT, MODE>), dim3((unsigned)grid), dim3(kRowThreads), 0, stream, a, G, C, (int)M);
 }
 
 template <int MODE>

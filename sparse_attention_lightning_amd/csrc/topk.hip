@@ -21,7 +21,15 @@
 // equal-to-T) counts then gives every thread its output positions, so ids
 // leave in ascending order without a sort.  Reductions and scans inside a
 // wave use DPP; waves meet through LDS.
+//
+// Many short rows (at least 1,024 rows of at most 1,024 blocks, as prefill
+// gives) take one wave a row and no LDS instead: lane l holds blocks l,
+// l + 64, ...; T is found bit by bit, each candidate threshold counted with
+// one ballot per 64 blocks, and ties and output positions come from the same
+// ballot masks.  An LDS-histogram version of that one-wave kernel measured
+// 20 % slower on 32,768 rows of 272 blocks.
 #include "device.h"
+
 
 namespace idx {
 
@@ -290,55 +298,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
 // workgroup barrier is needed.  Lane l owns the contiguous blocks
 // [l*C, l*C + C), C <= 16, and 16 bins of its wave's 1,024-bin histogram;
 // a pass takes up to 10 bits.
-constexpr int kWaveRows = kTopkThreads / 64;  // rows a workgroup
-constexpr int kWaveBins = 1024;
-
-// The wave's LDS operations stay in program order across its lanes (one
-// wave's LDS accesses are served in issue order).
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_wave_kernel(const StepArgs a) {
-  constexpr int PER = 16, kBinsPerLane = kWaveBins / 64;  // 16
-  __shared__ u32x4 hist_all[kWaveRows][kWaveBins / 4];
+// The same selection with one wave a row and no LDS, for rows of at most
+// 64 S blocks: lane l holds blocks l, l + 64, ... (slot j: block 64 j + l).
+// The want-th largest competing key is found bit by bit from the top: a
+// candidate threshold c (>= 1) is kept when at least `want` competing keys
+// reach it, each count one ballot per slot (blocks that do not compete hold
+// key 0 there, below every c).  Keys equal to the threshold are taken lowest
+// id first, and the output positions (ascending ids) come from the same
+// ballot masks.
+template <int S>
+__global__ __launch_bounds__(kTopkThreads) void topk_ballot_kernel(const StepArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  u32x4* hist4 = hist_all[wave];
-  uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
   const int rows = a.P * a.H;
-  const int64_t o = (int64_t)blockIdx.x * kWaveRows + wave;
+  const int64_t o = (int64_t)blockIdx.x * kTopkWaves + wave;
   if (o >= (int64_t)a.n_req * rows) return;
   const int r = (int)(o / rows), i = (int)(o - (int64_t)r * rows);
   const int K = a.topk, MB = a.max_blocks;
   const float* bs = a.block_scores + o * MB;
-
-  // the row's slot and length first, then 16-byte score loads
   const int slot = a.req_slot[r];
-  const int len_raw = a.row_len[r * a.P + i / a.H];
-  __builtin_amdgcn_sched_barrier(0);
-  const bool vec = (MB % 4) == 0 && (reinterpret_cast<uintptr_t>(a.block_scores) & 15u) == 0;
-  const int C = vec ? ((MB / 4 + 63) / 64) * 4 : (MB + 63) / 64;
-  const int b0 = lane * C;
-  float sv[PER];
-  if (vec) {
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      f32x4 v = (4 * q < C && b0 + 4 * q < MB) ? *reinterpret_cast<const f32x4*>(bs + b0 + 4 * q)
-                                               : f32x4{0.f, 0.f, 0.f, 0.f};
-      sv[4 * q] = v[0]; sv[4 * q + 1] = v[1]; sv[4 * q + 2] = v[2]; sv[4 * q + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
-  }
-  const int bin0 = kWaveBins - kBinsPerLane * (lane + 1);  // this lane's bins, highest digits first
-#pragma unroll
-  for (int q = 0; q < kBinsPerLane / 4; ++q) hist4[bin0 / 4 + q] = u32x4{0u, 0u, 0u, 0u};
-
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
-  const int nb = pad ? 0 : blocks_of(clamp_len(len_raw, MB));
+  const int nb = pad ? 0 : blocks_of(clamp_len(a.row_len[r * a.P + i / a.H], MB));
   int32_t* ids = a.topk_ids + o * K;
   float* sc = a.topk_scores + o * K;
   if (nb <= K) {
@@ -349,117 +334,94 @@ __global__ __launch_bounds__(kTopkThreads) void topk_wave_kernel(const StepArgs 
     return;
   }
 
-  const int cnt = max(0, min(C, nb - b0));
   const int init = a.init_blocks, local_from = nb - a.local_blocks;
-  uint32_t key[PER];
+  float sv[S];
+  uint32_t key[S], ckey[S];  // ckey: the key where the block competes, else 0
   uint32_t cand = 0, forced = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int b = b0 + j;
-    const bool is_forced = b < init || b >= local_from;
+  for (int j = 0; j < S; ++j) {
+    const int b = 64 * j + lane;
+    const bool in = b < nb;
+    sv[j] = in ? bs[b] : -INFINITY;
     key[j] = order_key(sv[j]);
-    if (j < cnt) {
-      if (is_forced) {
-        forced |= 1u << j;
-      } else {
-        cand |= 1u << j;
-        kmin = min(kmin, key[j]);
-        kmax = max(kmax, key[j]);
-      }
+    const bool f = in && (b < init || b >= local_from);
+    const bool c = in && !f;
+    forced |= (uint32_t)f << j;
+    cand |= (uint32_t)c << j;
+    ckey[j] = c ? key[j] : 0u;
+    if (c) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
     }
   }
-  kmin = wave_reduce<0>(kmin);
-  kmax = wave_reduce<1>(kmax);
-  const uint32_t F = wave_reduce<2>((uint32_t)__builtin_popcount(forced));
+  uint32_t F = 0;
+#pragma unroll
+  for (int j = 0; j < S; ++j) F += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((forced >> j) & 1u));
+  const uint32_t want = (uint32_t)K - F;  // nb > K >= init + local: every forced block exists
 
-  // radix select of the want-th largest competing key
-  uint32_t want = (uint32_t)K - F;
-  uint32_t prefix = kmin, tshift = 0;
-  if (want > 0 && kmin != kmax) {
-    int hi = 31 - __builtin_clz(kmin ^ kmax);
-    prefix = (hi == 31) ? 0u : (kmin >> (hi + 1)) << (hi + 1);
-    wave_lds_order();  // the bins are clear
-    while (hi >= 0) {
-      const int lo = max(hi - 9, 0);
-      const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+  // T: the want-th largest competing key.  Every threshold tried is >= 1;
+  // T stays 0 only when fewer than `want` competing keys are above 0 (NaN
+  // scores have key 0).  The bits above the highest one in which the
+  // competing keys differ are theirs in common.
+  uint32_t T = 0u;
+  if (want > 0) {
+    kmin = wave_reduce<0>(kmin);
+    kmax = wave_reduce<1>(kmax);
+    int hi = 31;
+    if (kmin != kmax) {
+      hi = 31 - __builtin_clz(kmin ^ kmax);
+      T = (hi == 31) ? 0u : (kmin >> (hi + 1)) << (hi + 1);
+    } else {
+      T = kmin;
+      hi = -1;
+    }
+    for (int bit = hi; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      uint32_t n = 0;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const bool match = (hi == 31) || ((key[j] >> (hi + 1)) == (prefix >> (hi + 1)));
-        if (((cand >> j) & 1u) && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1u);
-      }
-      wave_lds_order();  // the counts are final
-      uint32_t h[kBinsPerLane];
-#pragma unroll
-      for (int q = 0; q < kBinsPerLane / 4; ++q) {
-        const u32x4 v = hist4[bin0 / 4 + q];
-        h[4 * q] = v[0]; h[4 * q + 1] = v[1]; h[4 * q + 2] = v[2]; h[4 * q + 3] = v[3];
-      }
-      uint32_t local = 0;
-#pragma unroll
-      for (int q = 0; q < kBinsPerLane; ++q) local += h[q];
-      const uint32_t above = wave_inclusive_sum(local) - local;
-      // the one lane whose bins hold the want-th largest key walks them
-      const bool mine = above < want && want <= above + local;
-      const uint64_t mb = __ballot(mine);  // exactly one lane: 1 <= want <= the pass's count
-      const int cut = mb ? (int)__builtin_ctzll(mb) : 0;
-      uint32_t dig = 0, abv = 0, cntd = 0, run = above;
-#pragma unroll
-      for (int q = kBinsPerLane - 1; q >= 0; --q) {
-        if (run < want && want <= run + h[q]) {
-          dig = (uint32_t)(bin0 + q);
-          abv = run;
-          cntd = h[q];
-        }
-        run += h[q];
-      }
-      dig = __builtin_amdgcn_readlane(dig, cut);
-      abv = __builtin_amdgcn_readlane(abv, cut);
-      cntd = __builtin_amdgcn_readlane(cntd, cut);
-#pragma unroll
-      for (int q = 0; q < kBinsPerLane / 4; ++q) hist4[bin0 / 4 + q] = u32x4{0u, 0u, 0u, 0u};
-      wave_lds_order();  // the bins are clear for the next pass
-      prefix |= dig << lo;
-      want -= abv;
-      tshift = (uint32_t)lo;
-      if (cntd == want) break;  // the whole bin is taken
-      hi = lo - 1;
+      for (int j = 0; j < S; ++j) n += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(ckey[j] >= c));
+      if (n >= want) T = c;
     }
   }
-  const uint32_t T = prefix >> tshift;
 
-  // taken: forced, competing keys above T, and of the keys equal to T the
-  // `want` with the lowest ids (the same final pass as the workgroup kernel)
-  uint32_t sure = forced, eq = 0;
+  // taken: forced, competing keys above T, and of those equal to T the first
+  // `rem` in id order; written at their rank in id order
+  uint32_t above = 0;
   if (want > 0) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const uint32_t kt = key[j] >> tshift;
-      if ((cand >> j) & 1u) {
-        if (kt > T) sure |= 1u << j;
-        else if (kt == T) eq |= 1u << j;
-      }
-    }
+    for (int j = 0; j < S; ++j)
+      above += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(((cand >> j) & 1u) && key[j] > T));
   }
-  const uint32_t packed = ((uint32_t)__builtin_popcount(sure) << 16) | (uint32_t)__builtin_popcount(eq);
-  const uint32_t ex = wave_inclusive_sum(packed) - packed;
-  const uint32_t eq_taken_before = min(ex & 0xFFFFu, want);
-  uint32_t take_eq = min((uint32_t)__builtin_popcount(eq), want - eq_taken_before);
-  uint32_t taken = sure;
-  for (uint32_t e = eq; take_eq > 0; --take_eq) {  // the lowest take_eq equal keys
-    const uint32_t low = e & (0u - e);
-    taken |= low;
-    e ^= low;
-  }
-  uint32_t pos = (ex >> 16) + eq_taken_before;
+  const uint32_t rem = want - above;  // keys equal to T to take (>= 1 when want > 0)
+  uint32_t eq_before = 0, sel_before = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if ((taken >> j) & 1u) {
-      if (pos < (uint32_t)K) {
-        ids[pos] = b0 + j;
-        sc[pos] = sv[j];
-      }
-      ++pos;
+  for (int j = 0; j < S; ++j) {
+    const bool c = (cand >> j) & 1u;
+    const bool eq = want > 0 && c && key[j] == T;
+    const uint64_t em = __builtin_amdgcn_ballot_w64(eq);
+    const bool take =
+        ((forced >> j) & 1u) || (want > 0 && c && key[j] > T) || (eq && eq_before + lanes_below(em) < rem);
+    const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
+    const uint32_t pos = sel_before + lanes_below(tm);
+    if (take && pos < (uint32_t)K) {  // exactly K are taken: F forced + want
+      ids[pos] = 64 * j + lane;
+      sc[pos] = sv[j];
     }
+    eq_before += (uint32_t)__builtin_popcountll(em);
+    sel_before += (uint32_t)__builtin_popcountll(tm);
+  }
+}
+
+// topk_ballot_kernel for the row's slot count S = ceil(max_blocks / 64), 1..16.
+template <int S>
+void launch_ballot(const StepArgs& a, int64_t rows, hipStream_t stream) {
+  if constexpr (S > 16) {
+    (void)a, (void)rows, (void)stream;
+  } else if (a.max_blocks > 64 * S) {
+    launch_ballot<S + 1>(a, rows, stream);
+  } else {
+    hipLaunchKernelGGL(topk_ballot_kernel<S>, dim3((unsigned)((rows + kTopkWaves - 1) / kTopkWaves)),
+                       dim3(kTopkThreads), 0, stream, a);
   }
 }
 
@@ -471,8 +433,7 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   // one wave a row once there are enough rows to fill the device four
   // times over with a workgroup each; fewer rows keep four waves a row
   if (a.max_blocks <= 16 * 64 && grid >= 1024)
-    hipLaunchKernelGGL(topk_wave_kernel, dim3((unsigned)((grid + kWaveRows - 1) / kWaveRows)), dim3(kTopkThreads), 0,
-                       stream, a);
+    launch_ballot<1>(a, grid, stream);
   else if (a.max_blocks <= 16 * kTopkThreads)
     hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   else

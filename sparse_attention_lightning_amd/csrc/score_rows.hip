@@ -31,9 +31,9 @@
 // p + 1 tokens, items above the diagonal exit at once) and the C chunks of a
 // row group split that extent evenly, so the chunks of a row group are equal
 // however long its rows are.  Each XCD takes a contiguous run of items, so
-// the workgroups that read the same K pages share an L2.  Each wave stages its
-// rows' scores in LDS and writes them out every 32 blocks as one 128-byte run
-// per row.
+// the workgroups that read the same K pages share an L2.  Each lane writes its
+// row's score of each page straight out; the L2 assembles each row's lines
+// over consecutive pages.
 #include <algorithm>
 #include <climits>
 #include <type_traits>
@@ -68,8 +68,6 @@ constexpr int kWaveTiles = 4;                          // lane group g ends with
 constexpr int kWaveRows = kTileRows * kWaveTiles;
 constexpr int kItemRows = kWaveRows * kRowWaves;
 static_assert(kWaveTiles % 4 == 0, "tiles a wave: a multiple of the four lane groups");
-constexpr int kStageBlocks = 32;                       // blocks staged between write-outs
-constexpr int kStagePitch = kStageBlocks + 1;          // words a staged row (odd: rows in different banks)
 constexpr int kMaxItemBlocks = 1024;                   // blocks of an item at most (page ids in LDS)
 constexpr int kPageUnits = kHeadDim * 2 / 16;          // 16-byte units of a bf16 token row (16)
 
@@ -87,11 +85,9 @@ constexpr int rows_ring() {
 }
 
 // LDS of a workgroup: two bf16 K pages in 16-byte units (typed so that each
-// access is one 16-byte LDS instruction), the waves' staged scores, the
-// item's page ids.
+// access is one 16-byte LDS instruction) and the item's page ids.
 struct RowsLds {
   u32x4 page[2][kBlock * kPageUnits];
-  float stage[kRowWaves][kWaveRows * kStagePitch];
   int32_t pid[kMaxItemBlocks];
   int32_t nbw[kRowWaves];
 };
@@ -376,7 +372,6 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
     page_load<FMT>(pr, rk, rs, tid);
   };
 
-  float* stage = L.stage[wave];
   // tile T's K operands (16 tokens x the four k-steps) from LDS page P
   auto k_ops = [&](const u32x4* P, int T, u32x4* ko) {
 #pragma unroll
@@ -449,22 +444,12 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
       else
         o = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(s)) * 0.693147180559945309f;
       if (!ok) o = (b * kBlock < my_len[q]) ? __builtin_nanf("") : -INFINITY;
-      stage[(kTileRows * (4 * q + g) + n) * kStagePitch + k % kStageBlocks] = o;
+      const int row = wrow0 + kTileRows * (4 * q + g) + n;
+      if (row < PH) a.block_scores[((int64_t)r * PH + row) * MB + b] = o;
     };
     out(std::integral_constant<int, 0>{});
     if constexpr (kWaveTiles > 4) out(std::integral_constant<int, 1>{});
     static_assert(kWaveTiles <= 8, "tiles a wave: at most 8");
-    // every 32 blocks, and after the last: the wave's rows out as runs, two
-    // rows an instruction
-    if (k % kStageBlocks == kStageBlocks - 1 || k == nblk - 1) {
-      const int k0 = k - k % kStageBlocks, cnt = k - k0 + 1;
-      const int col = lane & 31;
-      for (int i = 0; i < kWaveRows; i += 2) {
-        const int ri = i + (lane >> 5), row = wrow0 + ri;
-        if (row < PH && col < cnt)
-          a.block_scores[((int64_t)r * PH + row) * MB + b0 + k0 + col] = stage[ri * kStagePitch + col];
-      }
-    }
     if constexpr (MODE == IDX_SCORE_LSE) mid();
   };
 

@@ -93,6 +93,17 @@ def subset_args(a: dict, reqs, P: int, H: int) -> dict:
                 req_slot=np.ascontiguousarray(a["req_slot"][reqs]), row_len=np.ascontiguousarray(rl))
 
 
+def subset_rows_args(a: dict, req: int, qrows, P: int, H: int) -> dict:
+    """Oracle arguments for request ``req`` alone, restricted to its query rows
+    ``qrows`` (each with all H heads; the same pool, slot and lengths), as a
+    request of len(qrows) packed rows."""
+    qrows = np.asarray(qrows)
+    q = a["q"].reshape(a["n_req"], P, H, 128)[req, qrows].reshape(-1, H, 128)
+    rl = a["row_len"].reshape(a["n_req"], P)[req, qrows]
+    return dict(a, n_req=1, packed_queries=len(qrows), q=np.ascontiguousarray(q),
+                req_slot=np.ascontiguousarray(a["req_slot"][req:req + 1]), row_len=np.ascontiguousarray(rl))
+
+
 def rows_of(reqs, rows_per_req: int) -> np.ndarray:
     reqs = np.asarray(reqs)
     return (reqs[:, None] * rows_per_req + np.arange(rows_per_req)[None, :]).reshape(-1)

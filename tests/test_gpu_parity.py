@@ -458,6 +458,42 @@ def test_lse_workload_4_nvfp4_150k(oracle):
     _full(oracle, 4, sample=[5, 60], **LSE)
 
 
+def _full_prefill(oracle, req, qrows, **mode):
+    """The prefill workload at full size in the bench's launch configuration;
+    the oracle scores the sampled query rows (all heads) of one request, and
+    every row's selection is checked for validity."""
+    say("workload", W.CONFIG_NAMES[5], "request", req, "query rows", qrows, mode)
+    w = W.config(5, device="cuda")
+    P, H = w.packed_queries, w.gqa
+    a = dict(w.oracle_args(), **mode)
+    g = Hn.gpu_step(w, **mode)
+    sub = Hn.subset_rows_args(a, req, qrows, P, H)
+    o = oracle.step(**sub)
+    rows = (req * P * H + np.asarray(qrows)[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+    Hn.assert_parity({k: v[rows] for k, v in g.items()}, o, sub)
+    nbs = Hn.row_blocks(a)
+    ids = g["topk_ids"]
+    taken = (ids >= 0).sum(axis=1)
+    assert np.array_equal(taken, np.minimum(nbs, w.topk)), "selection sizes"
+    sel_sorted = np.where(ids >= 0, ids, np.iinfo(np.int32).max)
+    assert np.all(np.diff(sel_sorted, axis=1) > 0), "ids ascending and distinct"
+    assert np.all(ids[nbs > 0, 0] == 0), "block 0 (init) is always taken"
+    last = np.take_along_axis(ids, np.maximum(taken - 1, 0)[:, None], axis=1)[:, 0]
+    assert np.array_equal(last, nbs - 1), "the row's last block (local) is always taken"
+
+
+PREFILL_ROWS = [0, 1, 2, 255, 256, 1023, 1024, 1500, 2046, 2047]  # item edges and the chunk's ends
+
+
+@pytest.mark.parametrize("req", [0, 3])
+def test_workload_5_prefill_32k_fp8(oracle, req):
+    _full_prefill(oracle, req, PREFILL_ROWS)
+
+
+def test_lse_workload_5_prefill_32k_fp8(oracle):
+    _full_prefill(oracle, 2, PREFILL_ROWS, **LSE)
+
+
 # ---------------------------------------------------------------------------
 # more than 16 rows a request: tiles of 16 rows, 64 sharing each K page (the
 # prefill scorer of ATOM PR 2745's Summary; wide packs).  Row j of a request

@@ -475,14 +475,45 @@ def _full_prefill(oracle, req, qrows, **mode):
     ids = g["topk_ids"]
     taken = (ids >= 0).sum(axis=1)
     assert np.array_equal(taken, np.minimum(nbs, w.topk)), "selection sizes"
-    sel_sorted = np.where(ids >= 0, ids, np.iinfo(np.int32).max)
-    assert np.all(np.diff(sel_sorted, axis=1) > 0), "ids ascending and distinct"
+    assert np.all(np.diff(ids, axis=1)[ids[:, 1:] >= 0] > 0), "taken ids ascending and distinct"
     assert np.all(ids[nbs > 0, 0] == 0), "block 0 (init) is always taken"
     last = np.take_along_axis(ids, np.maximum(taken - 1, 0)[:, None], axis=1)[:, 0]
     assert np.array_equal(last, nbs - 1), "the row's last block (local) is always taken"
 
 
 PREFILL_ROWS = [0, 1, 2, 255, 256, 1023, 1024, 1500, 2046, 2047]  # item edges and the chunk's ends
+
+
+def test_max_blocks_limit(oracle):
+    """A request at the block limit: its longest row sees exactly
+    IDX_MAX_BLOCKS * 128 tokens (1,048,576), beside a short one."""
+    say("max blocks", I.IDX_MAX_BLOCKS)
+    lmax = I.IDX_MAX_BLOCKS * 128
+    w = W.make(name="maxblocks", R=2, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[lmax - 3, 5000], topk=64,
+               init_blocks=1, local_blocks=2, seed=81, device="cuda")
+    assert w.max_blocks == I.IDX_MAX_BLOCKS
+    a = w.oracle_args()
+    Hn.assert_parity(Hn.gpu_step(w), oracle.step(**a), a)
+
+
+def test_max_rows_per_request(oracle):
+    """One request at the rows limit: packed_queries x gqa = IDX_MAX_REQ_ROWS
+    (16,384 causal query rows x 4 heads); sampled query rows against the
+    oracle, every row's selection checked."""
+    say("max rows a request", I.IDX_MAX_REQ_ROWS)
+    P, H = I.IDX_MAX_REQ_ROWS // 4, 4
+    w = W.make(name="maxrows", R=1, P=P, H=H, k_format=W.K_BF16, req_len=[300], topk=8,
+               init_blocks=1, local_blocks=2, seed=82, device="cuda")
+    a = w.oracle_args()
+    g = Hn.gpu_step(w)
+    qrows = [0, 1, 511, 512, 8191, 8192, P - 2, P - 1]
+    sub = Hn.subset_rows_args(a, 0, qrows, P, H)
+    rows = (np.asarray(qrows)[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+    Hn.assert_parity({k: v[rows] for k, v in g.items()}, oracle.step(**sub), sub)
+    nbs = Hn.row_blocks(a)
+    ids = g["topk_ids"]
+    assert np.array_equal((ids >= 0).sum(axis=1), np.minimum(nbs, w.topk))
+    assert np.all(np.diff(ids, axis=1)[ids[:, 1:] >= 0] > 0), "taken ids ascending and distinct"
 
 
 @pytest.mark.parametrize("req", [0, 3])

@@ -59,7 +59,7 @@ enum {
   IDX_E_PACK = -4,   /* packed_queries * gqa > IDX_MAX_REQ_ROWS, or n_req * packed_queries * gqa > IDX_MAX_ROWS */
   IDX_E_TOPK = -5,   /* topk < 1, init/local < 0, or topk < init_blocks + local_blocks */
   IDX_E_LAUNCH = -6, /* the HIP runtime rejected a kernel launch                      */
-  IDX_E_ALIGN = -7,  /* q, k, k_scale or staging not 16-byte aligned                  */
+  IDX_E_ALIGN = -7,  /* a pointer below its required alignment (see each call)       */
   IDX_E_MODE = -8    /* unknown score_mode, or an lse sm_scale that is not finite > 0 */
 };
 
@@ -158,7 +158,8 @@ typedef struct idx_params {
  * to x/scale, ties to the even code, saturating at 6, with x's sign bit
  * (scale 0 gives magnitude 0).  A slot < 0 or >= n_slots is skipped; other
  * slots are left untouched.  NaN/Inf inputs give unspecified bytes.
- * Pointers: staging_bf16 and payload 16-byte aligned.
+ * Pointers: staging_bf16 and payload 16-byte aligned, scales 8-byte aligned
+ * (a key's eight scale bytes are written as one 8-byte store).
  */
 int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_row_stride,
                   const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,

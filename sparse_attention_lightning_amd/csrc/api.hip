@@ -153,6 +153,8 @@ int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_ro
     return fail(IDX_E_NULL, "staging, slot_mapping, payload and scales are required");
   if (!aligned16(staging_bf16) || !aligned16(payload))
     return fail(IDX_E_ALIGN, "staging and payload must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(scales) & 7u) != 0)
+    return fail(IDX_E_ALIGN, "scales must be 8-byte aligned");
   return launched(idx::launch_fp4_store(static_cast<const uint16_t*>(staging_bf16), n_tokens,
                                         staging_row_stride, slot_mapping, payload, scales, n_slots,
                                         (hipStream_t)stream),

@@ -40,10 +40,12 @@ __global__ __launch_bounds__(kStoreThreads) void fp4_store_kernel(
        item += (int64_t)gridDim.x * kStoreThreads) {
     const int64_t t = item >> 3;
     const int grp = (int)(item & 7);
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0 || slot >= n_slots) continue;
+    // the key's row is read whether or not its slot is valid, so the two
+    // loads overlap (the row is in range either way)
     const uint4* src = reinterpret_cast<const uint4*>(staging + t * stride + 16 * grp);
     const uint4 w0 = src[0], w1 = src[1];
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= n_slots) continue;  // the key's 8 lanes skip together
     const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     float x[16];
     float amax = 0.0f;
@@ -73,7 +75,13 @@ __global__ __launch_bounds__(kStoreThreads) void fp4_store_kernel(
       packed[j >> 3] |= code << (4 * (j & 7));
     }
     *reinterpret_cast<uint2*>(payload + slot * 64 + 8 * grp) = make_uint2(packed[0], packed[1]);
-    scales[slot * 8 + grp] = (uint8_t)sb;
+    // the key's 8 scale bytes as one 8-byte store from its first lane: each
+    // quad of lanes ORs its bytes into a word, lane 4 hands its word to lane 0
+    uint32_t word = sb << (8 * (grp & 3));
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    const uint32_t hi = __shfl_down(word, 4, 8);
+    if (grp == 0) *reinterpret_cast<uint2*>(scales + slot * 8) = make_uint2(word, hi);
   }
 }
 

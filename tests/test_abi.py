@@ -144,6 +144,7 @@ FP4_REFUSALS = [
     dict(payload=None, code=I.IDX_E_NULL),
     dict(slot_mapping=None, code=I.IDX_E_NULL),
     dict(staging=0x200008, code=I.IDX_E_ALIGN),
+    dict(scales=0x500004, code=I.IDX_E_ALIGN),
 ]
 
 

@@ -23,13 +23,17 @@
 // wave use DPP; waves meet through LDS.
 //
 // Many short rows (at least 1,024 rows of at most 1,024 blocks, as prefill
-// gives) take one wave a row and no LDS instead: lane l holds blocks l,
+// gives, or rows of at most 64 blocks) take one wave a row and no LDS instead: lane l holds blocks l,
 // l + 64, ...; T is found bit by bit, each candidate threshold counted with
 // one ballot per 64 blocks, and ties and output positions come from the same
 // ballot masks.  An LDS-histogram version of that one-wave kernel measured
 // 20 % slower on 32,768 rows of 272 blocks.
 #include "device.h"
 
+
+#ifndef IDX_TOPK_BALLOT_ROWS
+#define IDX_TOPK_BALLOT_ROWS 1024  // rows from which rows of <= 1,024 blocks take one wave each
+#endif
 
 namespace idx {
 
@@ -432,7 +436,10 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   static_assert(IDX_MAX_BLOCKS <= 32 * kTopkThreads, "32 blocks per thread cover the limit");
   // one wave a row once there are enough rows to fill the device four
   // times over with a workgroup each; fewer rows keep four waves a row
-  if (a.max_blocks <= 16 * 64 && grid >= 1024)
+  // one wave a row for many rows of <= 1,024 blocks, and for rows of one
+  // 64-block slot at any count (a workgroup a row measured faster for a few
+  // hundred rows of 1,024 blocks, slower for rows of 12)
+  if (a.max_blocks <= 16 * 64 && (grid >= IDX_TOPK_BALLOT_ROWS || a.max_blocks <= 64))
     launch_ballot<1>(a, grid, stream);
   else if (a.max_blocks <= 16 * kTopkThreads)
     hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);

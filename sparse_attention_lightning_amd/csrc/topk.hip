@@ -379,7 +379,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_ballot_kernel(const StepArg
       T = kmin;
       hi = -1;
     }
-    for (int bit = hi; bit >= 0; --bit) {
+    // unrolled: no loop control among the scalar counting (bits above hi skip)
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+      if (bit > hi) continue;
       const uint32_t c = T | (1u << bit);
       uint32_t n = 0;
 #pragma unroll

@@ -36,6 +36,10 @@
  *    arguments on the host, enqueues its kernels on `stream` and returns
  *    without synchronising.  0 = enqueued; a negative IDX_E_* code = refused,
  *    nothing enqueued (IDX_E_LAUNCH: the runtime rejected a launch).
+ *  - A pointer whose array has no elements (n_req = 0, max_blocks = 0,
+ *    n_pages = 0, n_slot_rows = 0 ...) may be NULL: it is never dereferenced.
+ *    A call over zero rows, or over rows with no blocks, is accepted and
+ *    writes what its outputs hold (sentinels where a row has no block).
  *  - Sizes that live in device memory (row lengths, page ids, slots) cannot be
  *    checked on the host; the kernels clamp or reject them as stated below and
  *    never access memory outside the extents passed in.

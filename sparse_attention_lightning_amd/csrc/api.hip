@@ -56,12 +56,17 @@ int check(const idx_params* p, int need) {
       (int64_t)p->topk < (int64_t)p->init_blocks + p->local_blocks)
     return fail(IDX_E_TOPK, "need topk >= 1, init/local >= 0, topk >= init + local (got %d, %d, %d)",
                 p->topk, p->init_blocks, p->local_blocks);
-  if (!p->req_slot || !p->row_len) return fail(IDX_E_NULL, "req_slot and row_len are required");
-  if (!p->block_scores) return fail(IDX_E_NULL, "block_scores is required");
+  // a pointer is required only where its array has elements; an empty one is
+  // never dereferenced (no K page is valid when n_pages is 0)
+  const int64_t rows = (int64_t)p->n_req * p->packed_queries * p->gqa;
+  if (p->n_req > 0 && (!p->req_slot || !p->row_len))
+    return fail(IDX_E_NULL, "req_slot and row_len are required");
+  if (rows * p->max_blocks > 0 && !p->block_scores) return fail(IDX_E_NULL, "block_scores is required");
   if (need & kScore) {
-    if (!p->q || !p->k || !p->block_table)
+    if ((rows > 0 && !p->q) || (p->n_pages > 0 && !p->k) ||
+        ((int64_t)p->n_slot_rows * p->max_blocks > 0 && !p->block_table))
       return fail(IDX_E_NULL, "q, k and block_table are required for scoring");
-    if (p->k_format == IDX_K_NVFP4 && !p->k_scale)
+    if (p->k_format == IDX_K_NVFP4 && p->n_pages > 0 && !p->k_scale)
       return fail(IDX_E_NULL, "k_scale is required for NVFP4 keys");
     if (!aligned16(p->q) || !aligned16(p->k))
       return fail(IDX_E_ALIGN, "q and k must be 16-byte aligned");
@@ -69,7 +74,7 @@ int check(const idx_params* p, int need) {
       return fail(IDX_E_ALIGN, "k_scale must be 2-byte aligned");
   }
   if (need & kTopk) {
-    if (!p->topk_ids || !p->topk_scores)
+    if (rows > 0 && (!p->topk_ids || !p->topk_scores))
       return fail(IDX_E_NULL, "topk_ids and topk_scores are required for selection");
   }
   return IDX_OK;

@@ -437,11 +437,10 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   static_assert(IDX_MAX_BLOCKS <= 32 * kTopkThreads, "32 blocks per thread cover the limit");
-  // one wave a row once there are enough rows to fill the device four
-  // times over with a workgroup each; fewer rows keep four waves a row
   // one wave a row for many rows of <= 1,024 blocks, and for rows of one
-  // 64-block slot at any count (a workgroup a row measured faster for a few
-  // hundred rows of 1,024 blocks, slower for rows of 12)
+  // 64-block slot at any count; otherwise a workgroup of four waves a row (it
+  // measured faster for a few hundred rows of 1,024 blocks, slower for rows
+  // of 12)
   if (a.max_blocks <= 16 * 64 && (grid >= IDX_TOPK_BALLOT_ROWS || a.max_blocks <= 64))
     launch_ballot<1>(a, grid, stream);
   else if (a.max_blocks <= 16 * kTopkThreads)

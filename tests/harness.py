@@ -174,6 +174,9 @@ def assert_parity(g: dict, o: dict, a: dict) -> int:
     # scores of the selected ids are the GPU's own block scores
     rows = np.arange(g["topk_ids"].shape[0])[:, None]
     sel = g["topk_ids"] >= 0
-    want = np.where(sel, g["block_scores"][rows, np.maximum(g["topk_ids"], 0)], -np.inf)
+    bs = g["block_scores"]
+    if bs.shape[1] == 0:  # no block column: nothing can be selected
+        bs = np.full((bs.shape[0], 1), -np.inf, dtype=np.float32)
+    want = np.where(sel, bs[rows, np.maximum(g["topk_ids"], 0)], -np.inf)
     assert np.array_equal(g["topk_scores"], want, equal_nan=True), "topk_scores != block scores"
     return n

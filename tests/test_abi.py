@@ -136,6 +136,38 @@ def test_entry_specific_requirements(lib):
     assert lib.idx_score_packed(C.byref(p), None) == I.IDX_E_ALIGN
 
 
+EMPTY_NULLS = [  # (sizes that empty some arrays, the pointers that may then be NULL)
+    (dict(n_pages=0), ["k", "k_scale"]),
+    (dict(max_blocks=0), ["block_scores", "block_table"]),
+    (dict(n_slot_rows=0), ["block_table"]),
+    (dict(n_req=0), ["q", "req_slot", "row_len", "block_scores", "topk_ids", "topk_scores"]),
+]
+
+
+@pytest.mark.parametrize("sizes,nulls", EMPTY_NULLS, ids=[next(iter(s)) for s, _ in EMPTY_NULLS])
+def test_empty_arrays_may_be_null(lib, sizes, nulls):
+    """A pointer is required only where its array has elements.  The call is
+    made to fail a later check (a misaligned pointer) so that nothing runs:
+    IDX_E_ALIGN shows that every NULL check passed."""
+    p = good_params()
+    p.k_format = I.IDX_K_NVFP4
+    for f, v in sizes.items():
+        setattr(p, f, v)
+    for f in nulls:
+        setattr(p, f, None)
+    if "q" in nulls:
+        p.k = 0x100004
+    else:
+        p.q = 0x100008
+    assert lib.idx_step(C.byref(p), None) == I.IDX_E_ALIGN, lib.idx_last_error().decode()
+    # the same NULLs with the sizes left non-zero are refused
+    q = good_params()
+    q.k_format = I.IDX_K_NVFP4
+    for f in nulls:
+        setattr(q, f, None)
+    assert lib.idx_step(C.byref(q), None) == I.IDX_E_NULL
+
+
 FP4_REFUSALS = [
     dict(stride=100, code=I.IDX_E_SHAPE),
     dict(stride=130, code=I.IDX_E_SHAPE),

@@ -585,3 +585,75 @@ def test_many_rows_invalid_pages(oracle):
     g, o = Hn.gpu_step(w), oracle.step(**a)
     assert np.isnan(o["block_scores"]).any()
     Hn.assert_parity(g, o, a)
+
+
+# ---------------------------------------------------------------------------
+# degenerate steps: rows with nothing visible, a call with no request, an
+# empty K pool
+# ---------------------------------------------------------------------------
+DEGENERATE = [  # (R, P, H, lens of the requests, pads, pad_len, max_blocks)
+    (3, 1, 4, [0, 0, 0], 0, 0, None),       # every row empty, no block column
+    (3, 1, 4, [0, 0, 0], 0, 0, 6),          # every row empty, six block columns
+    (0, 2, 2, [], 2, 700, None),            # graph pads only
+    (1, 2, 2, [0], 3, 2000, None),          # an empty request beside pads
+    (2, 1, 20, [0, 0], 1, 300, 3),          # many-rows kernel, no row sees a token
+    (1, 32, 1, [0], 1, 500, None),          # many-rows kernel, rows of 0..31 tokens
+    (0, 4, 4, [], 0, 0, None),              # no request at all
+]
+
+
+@pytest.mark.parametrize("fmt", [W.K_BF16, W.K_FP8_E4M3, W.K_NVFP4], ids=["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("shape", range(len(DEGENERATE)))
+def test_degenerate_steps(oracle, fmt, shape):
+    R, P, H, lens, pads, pad_len, mb = DEGENERATE[shape]
+    say("degenerate", fmt, DEGENERATE[shape])
+    w = W.make(name="degenerate", R=R, P=P, H=H, k_format=fmt, req_len=lens, topk=4,
+               init_blocks=1, local_blocks=2, seed=500 + shape, pads=pads, pad_len=pad_len,
+               max_blocks=mb, device="cuda")
+    if fmt == W.K_NVFP4:
+        Hn.gpu_fp4_store(w)
+        a = w.oracle_args(*Hn.oracle_pool(oracle, w))
+    else:
+        a = w.oracle_args()
+    for m in ({}, LSE):
+        a_m = dict(a, **m)
+        g, o = Hn.gpu_step(w, **m), oracle.step(**a_m)
+        for key in g:
+            assert g[key].shape == o[key].shape, key
+        Hn.assert_parity(g, o, a_m)
+        assert np.array_equal(g["topk_ids"], o["topk_ids"])
+
+
+def test_no_request_calls_each_entry_point():
+    """A call over zero requests (every array empty, every pointer NULL) is
+    accepted by all three entry points and launches nothing."""
+    say("no request, each entry point")
+    w = W.make(name="none", R=0, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[], topk=4,
+               init_blocks=1, local_blocks=2, seed=510, device="cuda")
+    outs = Hn.gpu_outputs(w)
+    p = Hn.gpu_params(w, outs)
+    assert p.n_req == 0 and not p.q and not p.req_slot and not p.block_scores
+    for call in (I.idx_score_packed, I.idx_block_topk, I.idx_step):
+        call(p)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("P,H", [(1, 4), (20, 1)], ids=["one_tile", "many_rows"])
+@pytest.mark.parametrize("fmt", [W.K_FP8_E4M3, W.K_NVFP4], ids=["fp8", "nvfp4"])
+def test_empty_k_pool(oracle, fmt, P, H):
+    """n_pages = 0 with NULL pool pointers: nothing is read, every visible
+    block of a real request is NaN and the rest -inf."""
+    say("empty K pool", fmt, P, H)
+    w = W.make(name="no_pages", R=2, P=P, H=H, k_format=fmt, req_len=[300, 1000], topk=4,
+               init_blocks=1, local_blocks=2, seed=511, pads=1, pad_len=500, device="cuda")
+    w.k, w.n_pages = w.k[:0], 0
+    if fmt == W.K_NVFP4:
+        w.k_scale = w.k_scale[:0]
+    assert w.k.data_ptr() == 0
+    a = w.oracle_args()
+    for m in ({}, LSE):
+        a_m = dict(a, **m)
+        g, o = Hn.gpu_step(w, **m), oracle.step(**a_m)
+        assert np.isnan(o["block_scores"]).any() and not np.isfinite(o["block_scores"]).any()
+        Hn.assert_parity(g, o, a_m)
+        assert np.array_equal(g["topk_ids"], o["topk_ids"])

@@ -31,11 +31,18 @@
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
  *    allocates no memory and keeps no state between calls, except a
- *    thread-local copy of the last error message.
+ *    thread-local copy of the last error message and, per device, how many
+ *    workgroups of each kernel fit at once (queried on first use).  Calls
+ *    from several host threads are safe; calls on one stream run in order.
  *  - `stream` is a hipStream_t (NULL = the null stream).  A call checks its
  *    arguments on the host, enqueues its kernels on `stream` and returns
  *    without synchronising.  0 = enqueued; a negative IDX_E_* code = refused,
  *    nothing enqueued (IDX_E_LAUNCH: the runtime rejected a launch).
+ *  - A call makes no allocation, memset, copy or synchronisation, and its
+ *    launch shapes depend only on the host-side sizes, so it may be captured
+ *    into a HIP graph; a replay reads whatever the captured buffers then hold
+ *    (new queries, lengths, slots, page ids: the fixed-shape loop that graph
+ *    pads exist for [P2]).
  *  - A pointer whose array has no elements (n_req = 0, max_blocks = 0,
  *    n_pages = 0, n_slot_rows = 0 ...) may be NULL: it is never dereferenced.
  *    A call over zero rows, or over rows with no blocks, is accepted and

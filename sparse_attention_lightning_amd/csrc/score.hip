@@ -29,6 +29,7 @@
 // tile.h.  Each wave streams its pages as 64-token halves through a ring of
 // register buffers, keeping RING - 1 halves in flight while the matrix cores
 // work on one.
+#include <atomic>
 #include <climits>
 #include <cstddef>
 
@@ -462,10 +463,10 @@ size_t dyn_bytes(int n_req) { return (size_t)(2 * n_req + 1) * sizeof(uint32_t);
 // dynamic LDS limit raised to what the largest request count needs.
 template <int FMT, int MODE>
 int resident_workgroups() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // zero-initialised; calls from several threads store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] > 0) return cache[dev];
+  if (const int n = cache[dev].load(std::memory_order_relaxed); n > 0) return n;
   const size_t smem = dyn_bytes(IDX_MAX_REQ);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_kernel<FMT, MODE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -475,8 +476,8 @@ int resident_workgroups() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(score_kernel<FMT, MODE>),
                                                    kThreads, smem) != hipSuccess || per_cu <= 0)
     per_cu = 1;
-  cache[dev] = cus * per_cu;
-  return cache[dev];
+  cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+  return cus * per_cu;
 }
 
 template <int FMT, int MODE>

@@ -35,6 +35,7 @@
 // row's score of each page straight out; the L2 assembles each row's lines
 // over consecutive pages.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -496,18 +497,18 @@ namespace {
 // Workgroups that fit on the device at once (cached per device).
 template <int FMT, int MODE>
 int rows_resident() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // zero-initialised; calls from several threads store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] > 0) return cache[dev];
+  if (const int n = cache[dev].load(std::memory_order_relaxed); n > 0) return n;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(rows_kernel<FMT, MODE>),
                                                    kRowThreads, 0) != hipSuccess || per_cu <= 0)
     per_cu = 1;
-  cache[dev] = cus * per_cu;
-  return cache[dev];
+  cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+  return cus * per_cu;
 }
 
 template <int FMT, int MODE>

@@ -248,6 +248,8 @@ def main() -> int:
                        "topk": round(float(np.mean(topk_ms)) * 1e3, 2),
                        **({"fp4_store": round(float(np.mean(store_ms)) * 1e3, 2)} if fp4 else {})},
         "kernel_samples": len(ev),
+        # spread of the event-timed score kernel over the sampled steps
+        "score_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(score_ms, [10, 50, 90])],
         "roofline": roofline,
         "cpu_baseline": None,
     }

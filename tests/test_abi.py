@@ -204,3 +204,27 @@ def test_binding_constants_match_header():
     enums = dict((k, int(v)) for k, v in re.findall(r"(IDX_\w+)\s*=\s*(-?\d+)", text))
     for k, v in enums.items():
         assert getattr(I, k) == v, k
+
+
+def test_last_error_is_per_thread(lib):
+    """A refusal on one host thread leaves another thread's message alone."""
+    import threading
+    seen = {}
+
+    def refuse():
+        p = good_params()
+        p.head_dim = 64
+        seen["rc"] = lib.idx_step(C.byref(p), None)
+        seen["msg"] = lib.idx_last_error().decode()
+
+    def fresh():
+        seen["other"] = lib.idx_last_error().decode()
+
+    t = threading.Thread(target=refuse)
+    t.start()
+    t.join()
+    u = threading.Thread(target=fresh)
+    u.start()
+    u.join()
+    assert seen["rc"] == I.IDX_E_SHAPE and "head_dim" in seen["msg"]
+    assert seen["other"] == ""

@@ -705,3 +705,39 @@ def test_graph_replays(oracle, P, H):
     o = oracle.step(**a)
     Hn.assert_parity(got, o, a)
     assert np.array_equal(got["topk_ids"], o["topk_ids"])
+
+
+def test_host_threads_and_streams():
+    """Four host threads, each with its own stream and workload, call
+    idx_step together (ctypes drops the GIL for the call); every output equals
+    the same workload's call made alone."""
+    import threading
+    say("host threads x streams")
+    shapes = [(4, 4, W.K_FP8_E4M3), (20, 2, W.K_BF16), (1, 8, W.K_FP8_E4M3), (64, 1, W.K_BF16)]
+    ws = [W.make(name=f"thr{i}", R=3, P=P, H=H, k_format=f, req_len=[900, 2100, 300], topk=5,
+                 init_blocks=1, local_blocks=2, seed=530 + i, pads=1, pad_len=1000, device="cuda")
+          for i, (P, H, f) in enumerate(shapes)]
+    alone = [Hn.gpu_step(w) for w in ws]
+    outs = [[Hn.gpu_outputs(w) for _ in range(5)] for w in ws]
+    streams = [torch.cuda.Stream() for _ in ws]
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(i):
+        try:
+            for o in outs[i]:
+                I.idx_step(Hn.gpu_params(ws[i], o), streams[i])
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(ws))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, w in enumerate(ws):
+        for o in outs[i]:
+            for key, v in o.items():
+                assert np.array_equal(v.cpu().numpy(), alone[i][key], equal_nan=True), (i, key)

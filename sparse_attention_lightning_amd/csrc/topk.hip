@@ -296,12 +296,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   }
 }
 
-// Rows of at most 1,024 blocks (short contexts, the many query rows of a
-// prefill chunk): the same selection with one wave per row and four rows a
-// workgroup, so the scans and reductions stay inside the wave (DPP) and no
-// workgroup barrier is needed.  Lane l owns the contiguous blocks
-// [l*C, l*C + C), C <= 16, and 16 bins of its wave's 1,024-bin histogram;
-// a pass takes up to 10 bits.
 // Lanes below this one whose bit is set in m.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -741,3 +741,39 @@ def test_host_threads_and_streams():
         for o in outs[i]:
             for key, v in o.items():
                 assert np.array_equal(v.cpu().numpy(), alone[i][key], equal_nan=True), (i, key)
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes: every path (one tile, many rows, both top-k kernels),
+# format and reduction, with lengths from empty to 20,000 tokens
+# ---------------------------------------------------------------------------
+def _random_case(seed: int) -> dict:
+    rng = np.random.default_rng(9000 + seed)
+    P = int(rng.choice([1, 2, 4, 5, 8, 16, 17, 33, 64]))
+    H = int(rng.integers(1, 9)) if P <= 16 else int(rng.integers(1, 3))
+    R = int(rng.integers(1, 6))
+    lens = rng.integers(0, int(rng.choice([600, 6000, 20000])), size=R)  # > 64 blocks: workgroup top-k
+    lens[rng.random(R) < 0.2] = 0
+    topk = int(rng.integers(1, 17))
+    init = int(rng.integers(0, min(3, topk) + 1))
+    local = int(rng.integers(0, topk - init + 1)) if rng.random() < 0.7 else 0
+    return dict(P=P, H=H, R=R, lens=lens.tolist(), topk=topk, init=init, local=min(local, 4),
+                pads=int(rng.integers(0, 3)), fmt=int(rng.integers(0, 3)),
+                lse=bool(rng.random() < 0.4), scale=float(rng.choice([0.02, 1 / np.sqrt(128), 0.5])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(oracle, seed):
+    c = _random_case(seed)
+    say("random", seed, c)
+    w = W.make(name="random", R=c["R"], P=c["P"], H=c["H"], k_format=c["fmt"], req_len=c["lens"],
+               topk=c["topk"], init_blocks=c["init"], local_blocks=c["local"], seed=600 + seed,
+               pads=c["pads"], pad_len=2500, device="cuda")
+    if c["fmt"] == W.K_NVFP4:
+        Hn.gpu_fp4_store(w)
+        a = w.oracle_args(*Hn.oracle_pool(oracle, w))
+    else:
+        a = w.oracle_args()
+    m = dict(score_mode=I.IDX_SCORE_LSE, sm_scale=c["scale"]) if c["lse"] else {}
+    a = dict(a, **m)
+    Hn.assert_parity(Hn.gpu_step(w, **m), oracle.step(**a), a)

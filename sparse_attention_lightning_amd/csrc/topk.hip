@@ -6,8 +6,8 @@
 // nb are always taken and the remaining topk - |forced| slots go to the
 // highest block scores, ties to the lower block id.  Selection is exact.
 //
-// One workgroup of 256 threads per (row, head).  Thread t owns the contiguous
-// blocks [t*C, t*C + C), C = ceil(max_blocks / 256) <= 16 or 32 (rounded up to
+// One workgroup of 512 threads per (row, head).  Thread t owns the contiguous
+// blocks [t*C, t*C + C), C = ceil(max_blocks / 512) <= 8 or 16 (rounded up to
 // a multiple of 4 when rows are 16-byte aligned), and loads their scores into
 // registers first thing; the row's slot and length are fetched before them and
 // the score loads do not wait for them.  Keys are 32-bit integers whose
@@ -15,8 +15,8 @@
 // +0; each thread computes its keys once and marks its competing and forced
 // blocks in two bit masks.  A radix select over the competing keys finds the
 // k-th largest key T, k = topk - |forced|: it starts at the highest bit where
-// those keys differ, takes up to 12 bits a pass into a 4,096-bin LDS histogram
-// (thread t scans and clears 16 bins), and stops once the chosen bin holds
+// those keys differ, takes up to 11 bits a pass into a 2,048-bin LDS histogram
+// (thread t scans and clears 4 bins), and stops once the chosen bin holds
 // exactly the keys still needed.  One packed scan of (taken-for-sure,
 // equal-to-T) counts then gives every thread its output positions, so ids
 // leave in ascending order without a sort.  Reductions and scans inside a
@@ -37,8 +37,10 @@
 
 namespace idx {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 512;  // the workgroup kernel: one row a workgroup
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBallotThreads = 256;  // the one-wave kernel: four rows a workgroup
+constexpr int kBallotWaves = kBallotThreads / 64;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f != f) return 0u;  // NaN
@@ -106,11 +108,11 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
   return combine<OP>(combine<OP>(a, b), combine<OP>(c, d));
 }
 
-// PER: blocks per thread (16 covers max_blocks <= 4096, 32 the full limit).
+// PER: blocks per thread (8 covers max_blocks <= 4096, 16 the full limit).
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   static_assert(PER <= 32, "per-thread block sets are 32-bit masks");
-  constexpr int kBins = 4096, kBinsPerThread = kBins / kTopkThreads;  // 16
+  constexpr int kBins = 2048, kBinsPerThread = kBins / kTopkThreads;  // 4
   __shared__ u32x4 hist4[kBins / 4];
   uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
   __shared__ uint32_t red[3][kTopkWaves];
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     int hi = 31 - __builtin_clz(kmin ^ kmax);
     prefix = (hi == 31) ? 0u : (kmin >> (hi + 1)) << (hi + 1);
     while (hi >= 0) {
-      const int lo = max(hi - 11, 0);
+      const int lo = max(hi - 10, 0);
       const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
@@ -310,11 +312,11 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 // id first, and the output positions (ascending ids) come from the same
 // ballot masks.
 template <int S>
-__global__ __launch_bounds__(kTopkThreads) void topk_ballot_kernel(const StepArgs a) {
+__global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = a.P * a.H;
-  const int64_t o = (int64_t)blockIdx.x * kTopkWaves + wave;
+  const int64_t o = (int64_t)blockIdx.x * kBallotWaves + wave;
   if (o >= (int64_t)a.n_req * rows) return;
   const int r = (int)(o / rows), i = (int)(o - (int64_t)r * rows);
   const int K = a.topk, MB = a.max_blocks;
@@ -421,8 +423,8 @@ void launch_ballot(const StepArgs& a, int64_t rows, hipStream_t stream) {
   } else if (a.max_blocks > 64 * S) {
     launch_ballot<S + 1>(a, rows, stream);
   } else {
-    hipLaunchKernelGGL(topk_ballot_kernel<S>, dim3((unsigned)((rows + kTopkWaves - 1) / kTopkWaves)),
-                       dim3(kTopkThreads), 0, stream, a);
+    hipLaunchKernelGGL(topk_ballot_kernel<S>, dim3((unsigned)((rows + kBallotWaves - 1) / kBallotWaves)),
+                       dim3(kBallotThreads), 0, stream, a);
   }
 }
 
@@ -430,17 +432,17 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.n_req * a.P * a.H;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  static_assert(IDX_MAX_BLOCKS <= 32 * kTopkThreads, "32 blocks per thread cover the limit");
+  static_assert(IDX_MAX_BLOCKS <= 16 * kTopkThreads, "16 blocks per thread cover the limit");
   // one wave a row for many rows of <= 1,024 blocks, and for rows of one
-  // 64-block slot at any count; otherwise a workgroup of four waves a row (it
-  // measured faster for a few hundred rows of 1,024 blocks, slower for rows
-  // of 12)
+  // 64-block slot at any count; otherwise a workgroup of eight waves a row
+  // (it measured faster for a few hundred rows of 1,024 blocks, slower for
+  // rows of 12)
   if (a.max_blocks <= 16 * 64 && (grid >= IDX_TOPK_BALLOT_ROWS || a.max_blocks <= 64))
     launch_ballot<1>(a, grid, stream);
-  else if (a.max_blocks <= 16 * kTopkThreads)
-    hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
+  else if (a.max_blocks <= 8 * kTopkThreads)
+    hipLaunchKernelGGL(topk_kernel<8>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(topk_kernel<32>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
+    hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -25,8 +25,8 @@
 // Many short rows (at least 1,024 rows of at most 1,024 blocks, as prefill
 // gives, or rows of at most 64 blocks) take one wave a row and no LDS instead: lane l holds blocks l,
 // l + 64, ...; T is found bit by bit, each candidate threshold counted with
-// one ballot per 64 blocks, and ties and output positions come from the same
-// ballot masks.  An LDS-histogram version of that one-wave kernel measured
+// one ballot per 64 blocks, stopping once exactly the wanted number reach
+// it; ties and output positions come from the same ballot masks.  An LDS-histogram version of that one-wave kernel measured
 // 20 % slower on 32,768 rows of 272 blocks.
 #include "device.h"
 
@@ -375,7 +375,10 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
       T = kmin;
       hi = -1;
     }
-    // unrolled: no loop control among the scalar counting (bits above hi skip)
+    // unrolled: no loop control among the scalar counting (bits above hi
+    // skip).  Once exactly `want` keys reach c they are the ones to take, and
+    // T = c (a key or not) selects them: keys above T, then all keys equal
+    // to it; the lower bits are not needed.
 #pragma unroll
     for (int bit = 31; bit >= 0; --bit) {
       if (bit > hi) continue;
@@ -384,18 +387,20 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
 #pragma unroll
       for (int j = 0; j < S; ++j) n += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(ckey[j] >= c));
       if (n >= want) T = c;
+      if (n == want) break;
     }
   }
 
   // taken: forced, competing keys above T, and of those equal to T the first
-  // `rem` in id order; written at their rank in id order
+  // `rem` in id order (all of them after an early stop); written at their
+  // rank in id order
   uint32_t above = 0;
   if (want > 0) {
 #pragma unroll
     for (int j = 0; j < S; ++j)
       above += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(((cand >> j) & 1u) && key[j] > T));
   }
-  const uint32_t rem = want - above;  // keys equal to T to take (>= 1 when want > 0)
+  const uint32_t rem = want - above;  // keys equal to T to take
   uint32_t eq_before = 0, sel_before = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) {

@@ -308,8 +308,32 @@ def cpu_baseline(w, n_sample, n_rows, mode) -> dict:
         o.step(**sub)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": round(float(t / frac) * 1e6, 1), "unit": "us", "cores": o.threads(),
-            "kind": "oracle", "sample": f"{what}, median of 3, {scale}"}
+    out = {"value": round(float(t / frac) * 1e6, 1), "unit": "us", "cores": o.threads(),
+           "kind": "oracle", "sample": f"{what}, median of 3, {scale}"}
+    # one thread, on a sixteenth of that sample (one run), scaled the same way
+    if P * H > 16:
+        p1 = max(1, p // 16)
+        frac1 = lw[0, :p1].sum() / lw.sum()
+        sub1 = dict(sub, packed_queries=p1, q=np.ascontiguousarray(q_all[:1, : p1 * H].reshape(-1, H, 128)),
+                    row_len=np.ascontiguousarray(len_all[:1, :p1].reshape(-1)))
+        what1 = f"the first {p1} packed rows of request 0"
+    else:
+        n1 = max(1, n // 16)
+        frac1 = lmax[:n1].sum() / lmax.sum()
+        sub1 = dict(sub, n_req=n1, q=np.ascontiguousarray(q_all[:n1].reshape(-1, H, 128)),
+                    req_slot=np.ascontiguousarray(a["req_slot"][:n1]),
+                    row_len=np.ascontiguousarray(len_all[:n1].reshape(-1)))
+        what1 = f"the first {n1} requests"
+    before = o.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        o.step(**sub1)
+        t1 = time.perf_counter() - t0
+    finally:
+        o.set_threads(before)
+    out["value_1thread"] = round(float(t1 / frac1) * 1e6, 1)
+    out["sample_1thread"] = f"{what1}, one run, {scale}"
+    return out
 
 
 if __name__ == "__main__":

@@ -53,6 +53,8 @@ def load(path: Path | str | None = None) -> C.CDLL:
     lib.oracle_fp4_store.restype = C.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = C.c_int
+    lib.oracle_set_threads.argtypes = [C.c_int]
+    lib.oracle_set_threads.restype = C.c_int
     lib.oracle_fp8_value.argtypes = [C.c_uint8]
     lib.oracle_fp8_value.restype = C.c_double
     lib.oracle_e2m1_value.argtypes = [C.c_uint8]
@@ -87,6 +89,10 @@ class Oracle:
 
     def threads(self) -> int:
         return self.lib.oracle_threads()
+
+    def set_threads(self, n: int) -> int:
+        """Threads for later calls from this thread; returns the count before."""
+        return self.lib.oracle_set_threads(n)
 
     # -- number formats --------------------------------------------------
     def fp8_value(self, code: int) -> float:

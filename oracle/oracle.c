@@ -418,3 +418,14 @@ int oracle_threads(void) {
   return 1;
 #endif
 }
+
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  const int before = omp_get_max_threads();
+  if (n > 0) omp_set_num_threads(n);
+  return before;
+#else
+  (void)n;
+  return 1;
+#endif
+}

@@ -94,6 +94,8 @@ int oracle_fp4_store(const void* staging_bf16, int64_t n_tokens,
 
 /* OpenMP threads the oracle's parallel loops use. */
 int oracle_threads(void);
+/* Threads for the calling thread's later calls (n > 0); returns the count before. */
+int oracle_set_threads(int n);
 
 /* The oracle's own format steps, exported so the tests can pin them. */
 double  oracle_fp8_value(uint8_t code);          /* OCP e4m3fn -> value          */

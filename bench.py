@@ -12,7 +12,8 @@ so back-to-back steps stream K from HBM).
 Prints one JSON line: the metric (us per index step), the dominant kernel's
 roofline against the 8 TB/s HBM peak (algorithmic bytes over its mean duration,
 from HIP events on its launch stream inside the timed region), and the CPU
-oracle timed on the host as a reported baseline.
+oracle timed on the host as a reported baseline (all cores, and one thread on
+a sixteenth of that sample).
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 3]
 """

@@ -662,27 +662,36 @@ def test_empty_k_pool(oracle, fmt, P, H):
 # ---------------------------------------------------------------------------
 # graph capture: one captured step replayed with new device-side data
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", [W.K_FP8_E4M3, W.K_NVFP4], ids=["fp8", "nvfp4"])
 @pytest.mark.parametrize("P,H", [(4, 4), (20, 2)], ids=["one_tile", "many_rows"])
-def test_graph_replays(oracle, P, H):
-    """idx_step captured once in a HIP graph and replayed after new query
-    values, shorter row lengths and a request turned into a graph pad are
-    written into the captured buffers (eager work between replays) equals the
-    eager call on every replay, and the oracle on the last."""
-    say("graph replays", P, H)
-    w = W.make(name="graph", R=3, P=P, H=H, k_format=W.K_FP8_E4M3, req_len=[700, 2500, 40],
+def test_graph_replays(oracle, P, H, fmt):
+    """idx_step (after idx_fp4_store of the keys, for NVFP4) captured once in a
+    HIP graph and replayed after new query values, new keys, shorter row
+    lengths and a request turned into a graph pad are written into the
+    captured buffers (eager work between replays) equals the eager calls on
+    every replay, and the oracle on the last."""
+    say("graph replays", P, H, fmt)
+    w = W.make(name="graph", R=3, P=P, H=H, k_format=fmt, req_len=[700, 2500, 40],
                topk=5, init_blocks=1, local_blocks=2, seed=520 + P, pads=1, pad_len=3000,
                device="cuda")
+    fp4 = fmt == W.K_NVFP4
     outs = Hn.gpu_outputs(w)
     p = Hn.gpu_params(w, outs)
+
+    def step():
+        if fp4:
+            Hn.gpu_fp4_store(w)
+        I.idx_step(p)
+
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        I.idx_step(p)  # first call (launch sizes queried) outside the capture
+        step()  # first call (launch sizes queried) outside the capture
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        I.idx_step(p)
+        step()
     gen = torch.Generator(device="cuda")
     gen.manual_seed(521)
     base_len = w.row_len.clone()
@@ -691,6 +700,8 @@ def test_graph_replays(oracle, P, H):
         outs["topk_scores"].fill_(float("nan"))
         outs["topk_ids"].fill_(-7)
         w.q.copy_(torch.randn(w.q.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        if fp4:
+            w.staging.copy_(torch.randn(w.staging.shape, generator=gen, device="cuda").to(torch.bfloat16))
         w.row_len.copy_(torch.clamp(base_len - 97 * rep, min=0))  # lengths only shrink
         if rep == 3:
             w.req_slot[1] = -1
@@ -698,10 +709,14 @@ def test_graph_replays(oracle, P, H):
         graph.replay()
         torch.cuda.synchronize()
         got = {k: v.cpu().numpy() for k, v in outs.items()}
+        if fp4:
+            Hn.gpu_fp4_store(w)  # the same keys again: the pool is unchanged
         eager = Hn.gpu_step(w)
         for key in got:
             assert np.array_equal(got[key], eager[key], equal_nan=True), f"replay {rep}: {key}"
-    a = w.oracle_args()
+    a = w.oracle_args(*Hn.oracle_pool(oracle, w)) if fp4 else w.oracle_args()
+    if fp4:
+        assert np.array_equal(w.k.cpu().numpy(), a["k"]) and np.array_equal(w.k_scale.cpu().numpy(), a["k_scale"])
     o = oracle.step(**a)
     Hn.assert_parity(got, o, a)
     assert np.array_equal(got["topk_ids"], o["topk_ids"])

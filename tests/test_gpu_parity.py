@@ -496,6 +496,19 @@ def test_max_blocks_limit(oracle):
     Hn.assert_parity(Hn.gpu_step(w), oracle.step(**a), a)
 
 
+def test_max_blocks_limit_many_rows(oracle):
+    """The many-rows kernel at the block limit: 20 rows of one request whose
+    longest row sees 1,048,576 tokens, so its blocks are cut into chunks."""
+    say("max blocks, many rows", I.IDX_MAX_BLOCKS)
+    P, lmax = 20, I.IDX_MAX_BLOCKS * 128
+    w = W.make(name="maxblocks_rows", R=2, P=P, H=1, k_format=W.K_FP8_E4M3,
+               req_len=[lmax - P - 2, 3000], topk=64, init_blocks=1, local_blocks=2, seed=83,
+               device="cuda")
+    assert w.max_blocks == I.IDX_MAX_BLOCKS
+    a = w.oracle_args()
+    Hn.assert_parity(Hn.gpu_step(w), oracle.step(**a), a)
+
+
 def test_max_rows_per_request(oracle):
     """One request at the rows limit: packed_queries x gqa = IDX_MAX_REQ_ROWS
     (16,384 causal query rows x 4 heads); sampled query rows against the

@@ -425,12 +425,14 @@ def test_lse_small_shapes(oracle, fmt, shape):
     Hn.assert_parity(Hn.gpu_step(w, **LSE), oracle.step(**a), a)
 
 
-@pytest.mark.parametrize("scale", [0.01, 1.0, 4.0])
-def test_lse_scales(oracle, scale):
+@pytest.mark.parametrize("P,H", [(4, 4), (20, 2)], ids=["one_tile", "many_rows"])
+@pytest.mark.parametrize("scale", [1e-6, 0.01, 1.0, 4.0, 1000.0])
+def test_lse_scales(oracle, scale, P, H):
     """Small and large softmax scales (a large one makes the block's max term
-    dominate; a small one sums 128 terms of nearly equal size)."""
-    say("lse scale", scale)
-    w = W.make(name="lse_scale", R=3, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[5000, 129, 2000],
+    dominate, far past where exp of the raw terms would overflow; a small one
+    sums 128 terms of nearly equal size)."""
+    say("lse scale", scale, P, H)
+    w = W.make(name="lse_scale", R=3, P=P, H=H, k_format=W.K_FP8_E4M3, req_len=[5000, 129, 2000],
                topk=6, init_blocks=1, local_blocks=2, seed=303, device="cuda")
     mode = dict(score_mode=I.IDX_SCORE_LSE, sm_scale=scale)
     a = dict(w.oracle_args(), **mode)

@@ -204,7 +204,8 @@ def main() -> int:
     digest = source_digest()
     fmt_name = {W.K_BF16: "bf16", W.K_FP8_E4M3: "fp8", W.K_NVFP4: "nvfp4"}[w.k_format]
     # the committed counter profiles are of the max reduction
-    traffic = (traffic_from_profiles(f"score_kernel_{fmt_name}", W.CONFIG_NAMES[args.config], digest)
+    kname = "score_kernel" if P * H <= 16 else "rows_kernel"
+    traffic = (traffic_from_profiles(f"{kname}_{fmt_name}", W.CONFIG_NAMES[args.config], digest)
                if args.score_mode == "max" else None)
 
     if P * H <= 16:
@@ -219,7 +220,7 @@ def main() -> int:
         tflops = flops / score_mean_s / 1e12
         roofline = {"kernel": "rows_kernel", "bound": "mfma", "achieved": round(tflops, 1),
                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                    "traffic": None, "algorithmic_flops": flops, "algorithmic_bytes": score_bytes}
+                    "traffic": traffic, "algorithmic_flops": flops, "algorithmic_bytes": score_bytes}
     line = {
         "metric": METRIC,
         "value": round(ms_per_step * 1e3, 2),

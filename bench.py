@@ -9,13 +9,15 @@ rows x 4 index heads, fp8 e4m3 keys, contexts U[491520, 524285], 3 graph-pad
 requests (about 2.08 GB of K per step, eight times the 256 MB Infinity Cache,
 so back-to-back steps stream K from HBM).
 
-Prints one JSON line: the metric (us per index step), the dominant kernel's
-roofline against the 8 TB/s HBM peak (algorithmic bytes over its mean duration,
-from HIP events on its launch stream inside the timed region), and the CPU
-oracle timed on the host as a reported baseline (all cores, and one thread on
-a sixteenth of that sample).
+Prints one JSON line: the metric (us per index step, wall clock over the
+timed steps), the dominant kernel's roofline against the 8 TB/s HBM peak
+(algorithmic bytes over its mean duration, from HIP events on its launch
+stream in a separate pass of at least 20 steps), the rate at which the part
+reads the same K pages with nothing else to do (``idx_probe_read``), and the
+CPU oracle timed on the host as a reported baseline (all cores, and one
+thread on a sixteenth of that sample).
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 3]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 3] [--k-format fp8]
 """
 from __future__ import annotations
 
@@ -44,6 +46,12 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--config", type=int, default=3,
                     help="workload index 0..5 (default 3; 5 is the prefill scorer)")
     ap.add_argument("--local-blocks", type=int, default=None)
+    ap.add_argument("--k-format", choices=("bf16", "fp8", "nvfp4"), default=None,
+                    help="store the workload's keys in this format instead (same shape)")
+    ap.add_argument("--event-steps", type=int, default=None,
+                    help="steps of the event-timed kernel pass (default max(20, min(steps, 100)))")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain-read measurement of the step's K pages")
     ap.add_argument("--score-mode", choices=("max", "lse"), default="max",
                     help="block reduction: max (default) or lse")
     ap.add_argument("--sm-scale", type=float, default=1 / 128 ** 0.5,
@@ -104,7 +112,8 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w = W.config(args.config, device=dev, local_blocks=args.local_blocks)
+    kf = {None: None, "bf16": W.K_BF16, "fp8": W.K_FP8_E4M3, "nvfp4": W.K_NVFP4}[args.k_format]
+    w = W.config(args.config, device=dev, local_blocks=args.local_blocks, k_format=kf)
     rows, K, MB = w.rows, w.topk, w.max_blocks
     outs = {"block_scores": torch.empty((rows, MB), dtype=torch.float32, device=dev),
             "topk_ids": torch.empty((rows, K), dtype=torch.int32, device=dev),
@@ -175,25 +184,29 @@ def main() -> int:
         one_step()
     torch.cuda.synchronize()
 
-    # Kernel durations come from HIP events on the launch stream.  An event
-    # between two launches costs a few microseconds of its own, so when the
-    # workload streams K from HBM (no flush) only every tenth step carries
-    # events and the step time is the wall clock of all timed steps.  With the
-    # cache flushed between steps every step carries events and the step time
-    # is the mean of the event-timed kernels (the flush is not part of a step).
-    every = 1 if flush is not None else 10
-    sampled = [s for s in range(args.steps) if s % every == 0]
-    evs = {s: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for s in sampled}
+    # 1. wall clock over the timed steps, with no event inside
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         if flush is not None:
             flush.sum()
-        one_step(evs.get(s))
+        one_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ev = [evs[s] for s in sampled]
+    # 2. kernel durations from HIP events on the launch stream, in a pass of
+    # its own (an event between two launches costs a few microseconds, which
+    # the wall-clock pass must not carry).  When the cache is flushed between
+    # steps the step time is the mean of the event-timed kernels, since the
+    # wall clock then includes the flush.
+    n_ev = args.event_steps if args.event_steps else max(20, min(args.steps, 100))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    for e in ev:
+        if flush is not None:
+            flush.sum()
+        one_step(e)
+    torch.cuda.synchronize()
+
     store_ms = [e[0].elapsed_time(e[1]) for e in ev] if fp4 else [0.0] * len(ev)
     score_ms = [e[1].elapsed_time(e[2]) for e in ev]
     topk_ms = [e[2].elapsed_time(e[3]) for e in ev]
@@ -205,7 +218,7 @@ def main() -> int:
     fmt_name = {W.K_BF16: "bf16", W.K_FP8_E4M3: "fp8", W.K_NVFP4: "nvfp4"}[w.k_format]
     # the committed counter profiles are of the max reduction
     kname = "score_kernel" if P * H <= 16 else "rows_kernel"
-    traffic = (traffic_from_profiles(f"{kname}_{fmt_name}", W.CONFIG_NAMES[args.config], digest)
+    traffic = (traffic_from_profiles(f"{kname}_{fmt_name}", w.name, digest)
                if args.score_mode == "max" else None)
 
     if P * H <= 16:
@@ -243,14 +256,15 @@ def main() -> int:
             "context_tokens": [int(w.req_len.min()), int(w.req_len.max() + P - 1)],
             "topk": K, "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
             "k_bytes_per_step": k_bytes, "parallelism": "single GPU",
-            "cache": "flushed between steps" if flush is not None else "K is 8x the 256 MB MALL",
+            "cache": ("flushed between steps" if flush is not None
+                      else f"K is {k_bytes / (256 << 20):.1f}x the 256 MB MALL"),
         },
         "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "kernels_us": {"score": round(score_mean_s * 1e6, 2),
                        "topk": round(float(np.mean(topk_ms)) * 1e3, 2),
                        **({"fp4_store": round(float(np.mean(store_ms)) * 1e3, 2)} if fp4 else {})},
         "kernel_samples": len(ev),
-        # spread of the event-timed score kernel over the sampled steps
+        # spread of the event-timed score kernel over the event pass
         "score_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(score_ms, [10, 50, 90])],
         "roofline": roofline,
         "cpu_baseline": None,
@@ -258,11 +272,80 @@ def main() -> int:
     if fp4:
         line["fp4_store_step_tokens"] = int(step_staging.shape[0])
         line["fp4_store_pool"] = pool_store
+    if not args.no_read_ceiling and P * H <= 16:
+        line["hbm_read_ceiling"] = read_ceiling(w, flush, stream)
+        line["score_frac_of_page_gather"] = round(achieved / line["hbm_read_ceiling"]["page_gather_GBps"], 4)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests, args.cpu_rows, mode)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def read_ceiling(w, flush, stream, reps: int = 10) -> dict:
+    """How fast the part reads the step's K pages with nothing else to do.
+
+    ``idx_probe_read`` streams the pages the score kernel reads (each real
+    request's blocks up to its longest row, in step order, every workgroup
+    an equal contiguous share) and, for comparison, the whole K pool in
+    address order; median of ``reps`` event-timed launches each, with
+    ordinary and with non-temporal loads.  NVFP4 pages are measured on the
+    payload plane (8 KB a page; the score kernel also reads 1 KB of scales)."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_lightning_amd import idx as I
+    from sparse_attention_lightning_amd import workloads as W
+
+    page_bytes = {W.K_BF16: 32768, W.K_FP8_E4M3: 16384, W.K_NVFP4: 8192}[w.k_format]
+    bt = w.block_table.cpu().numpy()
+    slots = w.req_slot.cpu().numpy()
+    nbg = (w.group_len()[: w.n_real].astype(np.int64) + 127) // 128
+    units = np.concatenate([bt[slots[r], : nbg[r]] for r in range(w.n_real)]).astype(np.int32)
+    units_t = torch.as_tensor(units, device=w.k.device)
+    base = w.k.view(torch.uint8)
+    sink = torch.empty(4096, dtype=torch.int32, device=w.k.device)
+    out = {"unit": "GB/s"}
+    for name, u, n in (("page_gather", units_t, len(units)), ("contiguous", None, w.n_pages)):
+        best = 0.0
+        for nt in (False, True):
+            ms = []
+            for _ in range(reps):
+                if flush is not None:
+                    flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                I.idx_probe_read(base, page_bytes, u, n_units=n, nt=nt, sink=sink, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            gbps = n * page_bytes / (float(np.median(ms)) / 1e3) / 1e9
+            out[f"{name}{'_nt' if nt else ''}_GBps"] = round(gbps, 1)
+            best = max(best, gbps)
+        out[f"{name}_GBps"] = round(best, 1)
+    out["bytes"] = {"page_gather": int(len(units)) * page_bytes, "contiguous": int(w.n_pages) * page_bytes}
+    out["method"] = ("idx_probe_read: 16-byte loads only, 16 a thread in flight, a resident grid of "
+                     "512-thread workgroups each on an equal contiguous share of the units; "
+                     "page_gather = the step's K pages in step order, contiguous = the whole K pool in "
+                     "address order; median of %d event-timed launches; best of ordinary and "
+                     "non-temporal loads" % reps)
+    return out
+
+
+def cpu_info() -> dict:
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
 
 
 def cpu_baseline(w, n_sample, n_rows, mode) -> dict:
@@ -311,8 +394,8 @@ def cpu_baseline(w, n_sample, n_rows, mode) -> dict:
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     out = {"value": round(float(t / frac) * 1e6, 1), "unit": "us", "cores": o.threads(),
-           "kind": "oracle", "sample": f"{what}, median of 3, {scale}"}
-    # one thread, on a sixteenth of that sample (one run), scaled the same way
+           "kind": "oracle", "sample": f"{what}, median of 3, {scale}", **cpu_info()}
+    # one thread, on a sixteenth of that sample (median of 3), scaled the same way
     if P * H > 16:
         p1 = max(1, p // 16)
         frac1 = lw[0, :p1].sum() / lw.sum()
@@ -328,13 +411,16 @@ def cpu_baseline(w, n_sample, n_rows, mode) -> dict:
         what1 = f"the first {n1} requests"
     before = o.set_threads(1)
     try:
-        t0 = time.perf_counter()
-        o.step(**sub1)
-        t1 = time.perf_counter() - t0
+        t1s = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            o.step(**sub1)
+            t1s.append(time.perf_counter() - t0)
     finally:
         o.set_threads(before)
+    t1 = float(np.median(t1s))
     out["value_1thread"] = round(float(t1 / frac1) * 1e6, 1)
-    out["sample_1thread"] = f"{what1}, one run, {scale}"
+    out["sample_1thread"] = f"{what1}, median of 3, {scale}"
     return out
 
 

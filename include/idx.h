@@ -36,8 +36,10 @@
  *    from several host threads are safe; calls on one stream run in order.
  *  - `stream` is a hipStream_t (NULL = the null stream).  A call checks its
  *    arguments on the host, enqueues its kernels on `stream` and returns
- *    without synchronising.  0 = enqueued; a negative IDX_E_* code = refused,
- *    nothing enqueued (IDX_E_LAUNCH: the runtime rejected a launch).
+ *    without synchronising.  0 = enqueued; a negative IDX_E_* code other than
+ *    IDX_E_LAUNCH = refused on the host, nothing enqueued.  IDX_E_LAUNCH = the
+ *    runtime rejected a launch; for a call that makes several launches
+ *    (idx_step) the launches before the rejected one stay enqueued.
  *  - A call makes no allocation, memset, copy or synchronisation, and its
  *    launch shapes depend only on the host-side sizes, so it may be captured
  *    into a HIP graph; a replay reads whatever the captured buffers then hold
@@ -191,6 +193,20 @@ int idx_step(const idx_params* p, void* stream);
 
 /* Message describing the last refusal on the calling thread ("" if none). */
 const char* idx_last_error(void);
+
+/*
+ * Measurement aid, not a step of the method: read n_units units of
+ * unit_bytes bytes each from `base` with 16-byte loads and nothing else, to
+ * measure how fast the part streams HBM.  Unit u is base + id * unit_bytes
+ * with id = units[u] (or u when units is NULL); ids outside
+ * [0, n_base_units) read unit 0.  A resident grid of workgroups (at most
+ * n_sink) each take an equal contiguous share of the unit list, as the score
+ * kernel shares its pages, and fold what they read into sink[workgroup].
+ * unit_bytes: a power of two in [1024, 1 << 20]; base 16-byte aligned and
+ * n_base_units * unit_bytes bytes long; nt != 0: non-temporal loads.
+ */
+int idx_probe_read(const void* base, int64_t n_base_units, const int32_t* units, int64_t n_units,
+                   int32_t unit_bytes, int32_t nt, uint32_t* sink, int32_t n_sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -124,7 +124,7 @@ class Oracle:
         rc = self.lib.oracle_fp4_store(_ptr(staging_bits), n_tok, stride, _ptr(slot_mapping),
                                        _ptr(payload), _ptr(scales), n_slots)
         if rc:
-            raise ValueError(f"oracle_fp4_store refused its arguments ({rc})")
+            raise ValueError(f"oracle_fp4_store refused its arguments or ran out of memory ({rc})")
 
     # -- scoring and selection ---------------------------------------------
     def _params(self, a: dict, outs: dict) -> OracleParams:
@@ -180,7 +180,7 @@ class Oracle:
         outs = self._outs(a)
         rc = self.lib.oracle_score_packed(C.byref(self._params(a, outs)))
         if rc:
-            raise ValueError(f"oracle_score_packed refused its arguments ({rc})")
+            raise ValueError(f"oracle_score_packed refused its arguments or ran out of memory ({rc})")
         return {"block_scores": outs["block_scores"]}
 
     def block_topk(self, block_scores: np.ndarray, **a) -> dict:
@@ -188,7 +188,7 @@ class Oracle:
         outs = self._outs(a, block_scores)
         rc = self.lib.oracle_block_topk(C.byref(self._params(a, outs)))
         if rc:
-            raise ValueError(f"oracle_block_topk refused its arguments ({rc})")
+            raise ValueError(f"oracle_block_topk refused its arguments or ran out of memory ({rc})")
         return {"topk_ids": outs["topk_ids"], "topk_scores": outs["topk_scores"]}
 
     def step(self, **a) -> dict:
@@ -196,5 +196,5 @@ class Oracle:
         outs = self._outs(a)
         rc = self.lib.oracle_step(C.byref(self._params(a, outs)))
         if rc:
-            raise ValueError(f"oracle_step refused its arguments ({rc})")
+            raise ValueError(f"oracle_step refused its arguments or ran out of memory ({rc})")
         return outs

@@ -15,7 +15,14 @@ SRC = HERE / "oracle.c"
 DEFAULT_LIB = HERE / "liboracle.so"
 
 
-def build(out: Path | str | None = None, mutant: int = 0, openmp: bool = True) -> Path:
+# AddressSanitizer and UndefinedBehaviorSanitizer, host code only (gcc, no GPU
+# code is involved); a process loading such a build needs libasan preloaded
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out: Path | str | None = None, mutant: int = 0, openmp: bool = True,
+          sanitize: bool = False) -> Path:
     out = Path(out) if out is not None else DEFAULT_LIB
     out.parent.mkdir(parents=True, exist_ok=True)
     tmp = out.with_name(out.name + f".tmp{os.getpid()}")
@@ -23,6 +30,8 @@ def build(out: Path | str | None = None, mutant: int = 0, openmp: bool = True) -
            f"-DORACLE_MUTANT={int(mutant)}", str(SRC), "-o", str(tmp), "-lm"]
     if openmp:
         cmd.insert(1, "-fopenmp")
+    if sanitize:
+        cmd[1:1] = SANITIZE_FLAGS
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -235,7 +235,7 @@ static double k_value(const oracle_params* p, int64_t token, int d) {
 }
 
 int oracle_score_packed(const oracle_params* p) {
-  int P, H, R, MB, rows;
+  int P, H, R, MB, rows, failed = 0;
   int64_t item, n_items;
   if (check_params(p)) return -1;
   P = p->packed_queries;
@@ -262,6 +262,14 @@ int oracle_score_packed(const oracle_params* p) {
     int page_ok = 0, any = 0;
     int lse = p->score_mode == ORACLE_SCORE_LSE;
     double* sv = lse ? (double*)malloc(sizeof(double) * 128 * (size_t)rows) : NULL; /* lse: each row's token scores */
+    if (!best || !end || (lse && !sv)) {
+#pragma omp atomic write
+      failed = 1;
+      free(sv);
+      free(end);
+      free(best);
+      continue;
+    }
 
     /* which tokens of block b each tile row sees */
     for (i = 0; i < rows; i++) {
@@ -308,14 +316,15 @@ int oracle_score_packed(const oracle_params* p) {
         for (t = 0; t < end[i]; t++) sum += exp(c * (sv[i * 128 + t] - best[i]));
         out = (float)(c * best[i] + log(sum));
       }
-      if (end[i] > 0 && !page_ok) out = NAN; /* visible block, page id out of range */
+      if (end[i] > 0 && !page_ok) /* visible block, page id out of range (mutant 15: -inf) */
+        out = MUTANT(15) ? -INFINITY : NAN;
       p->block_scores[((int64_t)r * rows + i) * MB + b] = out;
     }
     free(sv);
     free(end);
     free(best);
   }
-  return 0;
+  return failed ? -1 : 0;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -339,7 +348,7 @@ static int cand_cmp(const void* a, const void* b) {
 }
 
 int oracle_block_topk(const oracle_params* p) {
-  int P, H, R, MB, K, rows;
+  int P, H, R, MB, K, rows, failed = 0;
   int64_t item, n_items;
   if (check_params(p)) return -1;
   P = p->packed_queries;
@@ -375,6 +384,13 @@ int oracle_block_topk(const oracle_params* p) {
 
     sel = (unsigned char*)calloc((size_t)nb, 1);
     c = (cand*)malloc(sizeof(cand) * (size_t)nb);
+    if (!sel || !c) {
+#pragma omp atomic write
+      failed = 1;
+      free(sel);
+      free(c);
+      continue;
+    }
     if (nb <= K) {
       for (b = 0; b < nb; b++) sel[b] = 1;
     } else {
@@ -403,7 +419,7 @@ int oracle_block_topk(const oracle_params* p) {
     free(sel);
     free(c);
   }
-  return 0;
+  return failed ? -1 : 0;
 }
 
 int oracle_step(const oracle_params* p) {

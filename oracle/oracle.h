@@ -78,6 +78,9 @@ typedef struct oracle_params {
   float*   topk_scores;    /* [n_req*P][H][topk]                                 */
 } oracle_params;
 
+/* Every entry point returns 0, or -1 when it refuses its arguments or an
+ * allocation fails (its outputs are then incomplete). */
+
 /* Block max (or lse) of every (row, head, block); -inf past the row's own
  * block count, NaN for a visible block whose page id is outside [0, n_pages). */
 int oracle_score_packed(const oracle_params* p);

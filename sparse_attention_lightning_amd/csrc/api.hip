@@ -3,6 +3,7 @@
 // Every entry point checks its arguments on the host before touching the HIP
 // runtime, so a refused call enqueues nothing and needs no device.
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 
 #include "device.h"
@@ -112,6 +113,10 @@ int launched(hipError_t e, const char* what) {
   return IDX_OK;
 }
 
+// The runtime's last-error slot is per thread and sticky: an earlier failure
+// of some other call would otherwise be reported as this call's launch error.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 }  // namespace
 
 extern "C" {
@@ -121,22 +126,42 @@ const char* idx_last_error(void) { return g_err; }
 int idx_score_packed(const idx_params* p, void* stream) {
   const int rc = check(p, kScore);
   if (rc) return rc;
+  clear_stale_error();
   return launched(idx::launch_score(args_of(p), (hipStream_t)stream), "score");
 }
 
 int idx_block_topk(const idx_params* p, void* stream) {
   const int rc = check(p, kTopk);
   if (rc) return rc;
+  clear_stale_error();
   return launched(idx::launch_topk(args_of(p), (hipStream_t)stream), "top-k");
 }
 
 int idx_step(const idx_params* p, void* stream) {
   const int rc = check(p, kScore | kTopk);
   if (rc) return rc;
+  clear_stale_error();
   const idx::StepArgs a = args_of(p);
   const int r1 = launched(idx::launch_score(a, (hipStream_t)stream), "score");
   if (r1) return r1;
   return launched(idx::launch_topk(a, (hipStream_t)stream), "top-k");
+}
+
+int idx_probe_read(const void* base, int64_t n_base_units, const int32_t* units, int64_t n_units,
+                   int32_t unit_bytes, int32_t nt, uint32_t* sink, int32_t n_sink, void* stream) {
+  if (unit_bytes < 1024 || unit_bytes > (1 << 20) || (unit_bytes & (unit_bytes - 1)))
+    return fail(IDX_E_SHAPE, "unit_bytes %d must be a power of two in [1024, 1 << 20]", unit_bytes);
+  if (n_units < 0 || n_base_units < 1 || n_sink < 1 || n_units > ((int64_t)1 << 40))
+    return fail(IDX_E_SHAPE, "need n_units >= 0, n_base_units >= 1, n_sink >= 1");
+  if (n_base_units > (INT64_MAX >> 21))
+    return fail(IDX_E_SHAPE, "n_base_units %lld too large", (long long)n_base_units);
+  if (!base || !sink)
+    return fail(IDX_E_NULL, "base and sink are required");
+  if (!aligned16(base)) return fail(IDX_E_ALIGN, "base must be 16-byte aligned");
+  clear_stale_error();
+  return launched(idx::launch_read_probe(base, n_base_units, units, n_units, unit_bytes, nt != 0, sink, n_sink,
+                                         (hipStream_t)stream),
+                  "read probe");
 }
 
 int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_row_stride,
@@ -160,6 +185,7 @@ int idx_fp4_store(const void* staging_bf16, int64_t n_tokens, int64_t staging_ro
     return fail(IDX_E_ALIGN, "staging and payload must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(scales) & 7u) != 0)
     return fail(IDX_E_ALIGN, "scales must be 8-byte aligned");
+  clear_stale_error();
   return launched(idx::launch_fp4_store(static_cast<const uint16_t*>(staging_bf16), n_tokens,
                                         staging_row_stride, slot_mapping, payload, scales, n_slots,
                                         (hipStream_t)stream),

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     for (int j = 0; j < PER; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
   }
 
-  // this thread's 16 bins, highest digits first: bins [kBins - 16(t+1), kBins - 16 t)
+  // this thread's 4 bins, highest digits first: bins [kBins - 4(t+1), kBins - 4 t)
   const int bin0 = kBins - kBinsPerThread * (tid + 1);
 #pragma unroll
   for (int q = 0; q < kBinsPerThread / 4; ++q) hist4[bin0 / 4 + q] = u32x4{0u, 0u, 0u, 0u};
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
         if (((cand >> j) & 1u) && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1u);
       }
       __syncthreads();
-      // this thread's 16 bins (descending digits) into registers, then clear them
+      // this thread's 4 bins (descending digits) into registers, then clear them
       uint32_t h[kBinsPerThread];
 #pragma unroll
       for (int q = 0; q < kBinsPerThread / 4; ++q) {

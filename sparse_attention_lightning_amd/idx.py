@@ -25,7 +25,8 @@ IDX_MAX_BLOCKS = 8192
 IDX_MAX_REQ = 8192
 IDX_MAX_REQ_ROWS = 65536
 IDX_MAX_ROWS = 1 << 24
-EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error")
+EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error",
+           "idx_probe_read")
 
 
 class IdxError(RuntimeError):
@@ -70,6 +71,9 @@ def load(path: Path | str | None = None) -> C.CDLL:
     lib.idx_fp4_store.restype = C.c_int
     lib.idx_last_error.argtypes = []
     lib.idx_last_error.restype = C.c_char_p
+    lib.idx_probe_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int32, C.c_int32,
+                                   C.c_void_p, C.c_int32, C.c_void_p]
+    lib.idx_probe_read.restype = C.c_int
     if path is None:
         _lib = lib
     return lib
@@ -119,8 +123,8 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
                 n_slot_rows: int | None = None, n_pages: int | None = None,
                 score_mode: int = IDX_SCORE_MAX, sm_scale: float = 0.0) -> IdxParams:
     """Build the parameter block from tensors (sizes read from their shapes
-    unless given).  ``score_mode`` IDX_SCORE_LSE takes ``sm_scale``.  The
-    returned object keeps the tensors alive."""
+    unless given).  ``score_mode`` IDX_SCORE_LSE takes ``sm_scale``.
+    The returned object keeps the tensors alive."""
     if k_format not in _K_DTYPES:
         raise ValueError(f"unknown k_format {k_format}")
     p = IdxParams()
@@ -145,8 +149,12 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
     p.topk_scores = _dev(topk_scores, "topk_scores", (torch.float32,), optional=True)
     p.n_req = req_slot.numel()
     if max_blocks is None:
-        max_blocks = block_table.shape[-1] if block_table is not None else (
-            block_scores.numel() // max(1, p.n_req * packed_queries * gqa))
+        if block_table is not None:
+            max_blocks = block_table.shape[-1]
+        elif block_scores is not None:
+            max_blocks = block_scores.numel() // max(1, p.n_req * packed_queries * gqa)
+        else:
+            raise ValueError("max_blocks is needed when neither block_table nor block_scores is given")
     p.max_blocks = max_blocks
     if n_slot_rows is None:
         n_slot_rows = block_table.shape[0] if block_table is not None else 0
@@ -157,7 +165,7 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
     rows = p.n_req * packed_queries * gqa
     if row_len.numel() != p.n_req * packed_queries:
         raise ValueError("row_len must have n_req * packed_queries entries")
-    if block_scores.numel() < rows * max_blocks:
+    if block_scores is not None and block_scores.numel() < rows * max_blocks:
         raise ValueError("block_scores is smaller than n_req * P * H * max_blocks")
     if q is not None and q.numel() < rows * 128:
         raise ValueError("q is smaller than n_req * P * H * 128")
@@ -187,6 +195,30 @@ def idx_block_topk(p: IdxParams, stream=None) -> None:
 def idx_step(p: IdxParams, stream=None) -> None:
     lib = load()
     _check(lib.idx_step(C.byref(p), _stream(stream)), lib)
+
+
+def idx_probe_read(base: torch.Tensor, unit_bytes: int, units: torch.Tensor | None = None,
+                   n_units: int | None = None, nt: bool = False, sink: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Measurement aid: stream ``base`` (a contiguous GPU tensor viewed as
+    units of ``unit_bytes``) unit by unit, in the order of ``units`` (int32
+    unit ids) or in address order.  Returns the sink words."""
+    lib = load()
+    if base.device.type != "cuda" or not base.is_contiguous():
+        raise ValueError("base must be a contiguous GPU tensor")
+    n_base = base.numel() * base.element_size() // unit_bytes
+    up = None
+    if units is not None:
+        up = _dev(units, "units", (torch.int32,))
+        n_units = units.numel() if n_units is None else n_units
+    elif n_units is None:
+        n_units = n_base
+    if sink is None:
+        sink = torch.empty(4096, dtype=torch.int32, device=base.device)
+    rc = lib.idx_probe_read(base.data_ptr(), n_base, up, n_units, unit_bytes, int(nt), sink.data_ptr(),
+                            sink.numel(), _stream(stream))
+    _check(rc, lib)
+    return sink
 
 
 def idx_fp4_store(staging: torch.Tensor, slot_mapping: torch.Tensor, payload: torch.Tensor,

@@ -263,13 +263,15 @@ CONFIG_NAMES = {
 
 
 def config(idx: int, device: str | torch.device = "cpu", local_blocks: int | None = None,
-           n_real: int | None = None) -> Workload:
+           n_real: int | None = None, k_format: int | None = None) -> Workload:
     """Workload ``idx`` (0..5) with seed 1000 + idx.
 
     ``local_blocks`` overrides the forced local window (the 0 variant of the
     straddling fp8 workload).  ``n_real`` keeps the first ``n_real`` request
     lengths of the same draw (slot and page tables are drawn for the smaller
-    table); it makes bounded samples for CPU timing."""
+    table); it makes bounded samples for CPU timing.  ``k_format`` stores the
+    keys in another format at the same shape (the name says which), e.g. the
+    64-request ~150K workload with fp8 keys beside its NVFP4 ones."""
     seed = 1000 + idx
     rng = np.random.default_rng(seed)
     if idx == 0:
@@ -302,4 +304,9 @@ def config(idx: int, device: str | torch.device = "cpu", local_blocks: int | Non
     if n_real is not None:
         lens = lens[:n_real]
         kw["R"] = n_real
-    return make(name=CONFIG_NAMES[idx], req_len=lens, seed=seed, device=device, rng=rng, **kw)
+    name = CONFIG_NAMES[idx]
+    if k_format is not None and k_format != kw["k_format"]:
+        short = {K_BF16: "bf16", K_FP8_E4M3: "fp8", K_NVFP4: "nvfp4"}
+        name = name.replace(short[kw["k_format"]], short[k_format], 1)
+        kw["k_format"] = k_format
+    return make(name=name, req_len=lens, seed=seed, device=device, rng=rng, **kw)

@@ -611,12 +611,55 @@ def pin_graph_pads(o) -> None:
     assert (full["topk_ids"][n:] == -1).all() and np.isneginf(full["topk_scores"][n:]).all()
 
 
+def pin_bad_page_ids(o) -> None:
+    """A visible block whose page id lies outside [0, n_pages) (negative, one
+    past the pool, far past it) is not read: every row that sees it scores
+    NaN, rows that do not see it keep -inf, every other block is bit-equal to
+    the run with valid ids, and selection ranks the NaN below every number.
+    This is the library's stated rule for bad tables (the pages give none);
+    it is checked against the brute force and against the valid-table run,
+    for the max and the lse."""
+    for fmt, mode in ((W.K_BF16, {}), (W.K_FP8_E4M3, {}),
+                      (W.K_FP8_E4M3, {"score_mode": 1, "sm_scale": 0.2})):
+        # request 2's rows see 3070..3073 tokens: 24, 24, 24 and 25 blocks
+        w = small_workload(fmt, seed=95, R_lens=(300, 1022, 3070), topk=6, local=1)
+        a = dict(w.oracle_args(), **mode)
+        base = o.step(**a)
+        bt = a["block_table"].copy()
+        s1, s2 = int(a["req_slot"][1]), int(a["req_slot"][2])
+        bad = {(1, 2): a["n_pages"] + 5, (1, 7): a["n_pages"],   # block 7: the last of request 1
+               (2, 0): -3, (2, 10): 1 << 30, (2, 24): a["n_pages"]}  # block 24: seen by row 3 only
+        for (r, b), pg in bad.items():
+            bt[(s1, s2)[r - 1], b] = pg
+        a2 = dict(a, block_table=bt)
+        got = o.step(**a2)
+        compare_step(got, brute.step(a2, brute.pool_values(fmt, a["k"])), f"bad pages {fmt} {mode}")
+        bs, bs0 = got["block_scores"], base["block_scores"]
+        P, H = 4, 4
+        want = bs0.copy()
+        for (r, b), _ in bad.items():
+            for i in range(P * H):
+                L = int(a["row_len"][r * P + i // H])
+                if b < (L + 127) // 128:
+                    want[r * P * H + i, b] = np.nan
+        assert same(bs, want), f"bad pages {fmt} {mode}: block scores are not NaN exactly where seen"
+        # row 3 of request 2 sees block 24 (NaN); rows 0..2 do not (-inf)
+        assert np.isnan(bs[2 * 16 + 12: 2 * 16 + 16, 24]).all()
+        assert np.isneginf(bs[2 * 16: 2 * 16 + 12, 24]).all()
+        # a NaN block is taken only when forced (block 0, block 24 as row 3's local window)
+        for o_ in range(bs.shape[0]):
+            for b in got["topk_ids"][o_][got["topk_ids"][o_] >= 0]:
+                if np.isnan(bs[o_, b]):
+                    nb = int(np.isfinite(bs0[o_]).sum())
+                    assert b < 1 or b >= nb - 1 or nb <= 6, f"row {o_} selected NaN block {b}"
+
+
 PINS = [
     pin_fp8_decode, pin_e2m1_decode, pin_golden_store, pin_fp4_roundtrip,
     pin_bruteforce_bf16, pin_bruteforce_fp8, pin_bruteforce_fp4, pin_fp4_equals_bf16_of_dequant,
     pin_bruteforce_lse, pin_lse_closed_form, pin_lse_bounds,
     pin_topk_textbook, pin_topk_bruteforce, pin_topk_invariants, pin_exact_tie, pin_straddle,
     pin_packed_equals_per_row, pin_many_rows_equal_per_row, pin_masking, pin_slot_permutation,
-    pin_graph_pads,
+    pin_graph_pads, pin_bad_page_ids,
     pin_scale_rounding, pin_code_rounding,
 ]

@@ -206,6 +206,28 @@ def test_binding_constants_match_header():
         assert getattr(I, k) == v, k
 
 
+PROBE_REFUSALS = [
+    dict(unit_bytes=512, code=I.IDX_E_SHAPE),
+    dict(unit_bytes=3072, code=I.IDX_E_SHAPE),
+    dict(unit_bytes=1 << 21, code=I.IDX_E_SHAPE),
+    dict(n_units=-1, code=I.IDX_E_SHAPE),
+    dict(n_base=0, code=I.IDX_E_SHAPE),
+    dict(n_sink=0, code=I.IDX_E_SHAPE),
+    dict(base=None, code=I.IDX_E_NULL),
+    dict(sink=None, code=I.IDX_E_NULL),
+    dict(base=0x200008, code=I.IDX_E_ALIGN),
+]
+
+
+@pytest.mark.parametrize("case", PROBE_REFUSALS, ids=lambda c: ",".join(f"{k}={v}" for k, v in c.items() if k != "code"))
+def test_probe_refusals(lib, case):
+    a = dict(base=0x200000, n_base=64, units=None, n_units=64, unit_bytes=16384, nt=0, sink=0x300000, n_sink=256)
+    a.update({k: v for k, v in case.items() if k != "code"})
+    rc = lib.idx_probe_read(a["base"], a["n_base"], a["units"], a["n_units"], a["unit_bytes"], a["nt"],
+                            a["sink"], a["n_sink"], None)
+    assert rc == case["code"]
+
+
 def test_last_error_is_per_thread(lib):
     """A refusal on one host thread leaves another thread's message alone."""
     import threading

@@ -1,8 +1,10 @@
 """HIP path vs the CPU oracle on an MI355X (through the C-ABI).
 
-Small cases are compared in full; the five workloads run at full size in the
-launch configuration the benchmark times, compared on sampled requests (the
-oracle computes them one by one) and on properties that hold at any size.
+Small cases are compared in full.  The five decode workloads run at full size
+in the launch configuration the benchmark times and are compared in full too:
+every row of every request, graph pads included, and every byte of the NVFP4
+planes.  The prefill workload (32,768 rows) is compared on sampled query rows
+and on properties that hold at any size.
 """
 from __future__ import annotations
 
@@ -336,53 +338,53 @@ def test_shares_longer_than_a_round(oracle):
 
 
 # ---------------------------------------------------------------------------
-# the five workloads at full size, in the benchmark's launch configuration
+# the five workloads at full size, in the benchmark's launch configuration:
+# every row of every request (graph pads included) against the oracle, and
+# for NVFP4 every byte of both planes
 # ---------------------------------------------------------------------------
-def _full(oracle, idx, sample, local_blocks=None, **mode):
-    say("workload", W.CONFIG_NAMES[idx], "local", local_blocks, "sample", sample, mode)
+_POOLS: dict = {}
+
+
+def _oracle_pool_full(oracle, w):
+    """The oracle's NVFP4 planes for all of the workload's staging keys (one
+    store per workload and session: the max and lse tests share it)."""
+    key = (w.name, w.seed)
+    if key not in _POOLS:
+        _POOLS.clear()
+        _POOLS[key] = Hn.oracle_pool(oracle, w)
+    return _POOLS[key]
+
+
+def _full(oracle, idx, local_blocks=None, **mode):
+    say("workload", W.CONFIG_NAMES[idx], "local", local_blocks, mode, "every row")
     w = W.config(idx, device="cuda", local_blocks=local_blocks)
-    P, H = w.packed_queries, w.gqa
     if w.k_format == W.K_NVFP4:
         Hn.gpu_fp4_store(w)
-        # oracle store of the sampled requests' keys only
-        starts = np.concatenate([[0], np.cumsum(w.req_len + P - 1)])
-        toks = np.concatenate([np.arange(starts[r], starts[r + 1]) for r in sample if r < w.n_real])
-        payload, scales = Hn.oracle_pool(oracle, w, toks)
-        slots = w.slot_mapping.cpu().numpy()[toks]
-        assert np.array_equal(w.k.cpu().numpy()[slots], payload[slots]), "fp4 payload differs"
-        assert np.array_equal(w.k_scale.cpu().numpy()[slots], scales[slots]), "fp4 scales differ"
+        payload, scales = _oracle_pool_full(oracle, w)
+        # every slot: written ones bit-exact, the rest still hold their fill
+        assert np.array_equal(w.k.cpu().numpy(), payload), "fp4 payload bytes differ"
+        assert np.array_equal(w.k_scale.cpu().numpy(), scales), "fp4 scale bytes differ"
+        say("fp4 store: all", w.slot_mapping.numel(), "keys identical")
         a = w.oracle_args(payload, scales)
     else:
         a = w.oracle_args()
     a = dict(a, **mode)
     g = Hn.gpu_step(w, **mode)
-    sub = Hn.subset_args(a, sample, P, H)
-    o = oracle.step(**sub)
-    rows = Hn.rows_of(sample, P * H)
-    gs = {k: v[rows] for k, v in g.items()}
-    relaxed = Hn.assert_parity(gs, o, sub)
-    # properties at full size: every row's selection is valid
+    o = oracle.step(**a)
+    relaxed = Hn.assert_parity(g, o, a)
     nbs = Hn.row_blocks(a)
-    ids = g["topk_ids"]
-    for r in range(ids.shape[0]):
-        nb = int(nbs[r])
-        sel = ids[r][ids[r] >= 0]
-        assert np.all(np.diff(sel) > 0)
-        if nb <= w.topk:
-            assert np.array_equal(sel, np.arange(nb))
-        else:
-            assert len(sel) == w.topk and Hn._forced(nb, w.init_blocks, w.local_blocks) <= set(sel.tolist())
+    say(W.CONFIG_NAMES[idx], "rows compared:", g["topk_ids"].shape[0], "near-tie rows:", relaxed)
     assert np.isneginf(g["block_scores"][nbs == 0]).all()
     return g, relaxed
 
 
 def test_workload_1_bf16_131k(oracle):
-    _full(oracle, 1, sample=[0, 5, 15])
+    _full(oracle, 1)
 
 
 @pytest.mark.parametrize("local", [2, 0])
 def test_workload_2_fp8_straddle(oracle, local):
-    g, _ = _full(oracle, 2, sample=[0, 1, 2, 3, 9], local_blocks=local)
+    g, _ = _full(oracle, 2, local_blocks=local)
     # the straddling requests: rows end at 32767..32770 -> 256/256/257/257 blocks
     for r in range(4):
         for j, nb in enumerate([256, 256, 257, 257]):
@@ -392,13 +394,13 @@ def test_workload_2_fp8_straddle(oracle, local):
 
 
 def test_workload_3_fp8_524k_pads(oracle):
-    g, _ = _full(oracle, 3, sample=[0, 17, 31, 32, 33, 34])
+    g, _ = _full(oracle, 3)
     pads = g["topk_ids"][32 * 16:]
     assert (pads == -1).all() and np.isneginf(g["block_scores"][32 * 16:]).all()
 
 
 def test_workload_4_nvfp4_150k(oracle):
-    _full(oracle, 4, sample=[0, 33, 63])
+    _full(oracle, 4)
 
 
 # ---------------------------------------------------------------------------
@@ -452,12 +454,12 @@ def test_lse_invalid_page_ids(oracle):
 
 
 def test_lse_workload_3_fp8_524k_pads(oracle):
-    g, _ = _full(oracle, 3, sample=[0, 31, 33], **LSE)
+    g, _ = _full(oracle, 3, **LSE)
     assert (g["topk_ids"][32 * 16:] == -1).all() and np.isneginf(g["block_scores"][32 * 16:]).all()
 
 
 def test_lse_workload_4_nvfp4_150k(oracle):
-    _full(oracle, 4, sample=[5, 60], **LSE)
+    _full(oracle, 4, **LSE)
 
 
 def _full_prefill(oracle, req, qrows, **mode):
@@ -735,6 +737,80 @@ def test_graph_replays(oracle, P, H, fmt):
     o = oracle.step(**a)
     Hn.assert_parity(got, o, a)
     assert np.array_equal(got["topk_ids"], o["topk_ids"])
+
+
+def _graph_kernel_nodes(fn) -> int:
+    """Kernel nodes of a HIP graph captured from ``fn()`` (the calls are
+    made once outside the capture first, so launch sizes are known)."""
+    import ctypes as C
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph(keep_graph=True)
+    with torch.cuda.graph(graph):
+        fn()
+    hip = C.CDLL("libamdhip64.so.7")  # the runtime torch has loaded (same soname)
+    h = C.c_void_p(graph.raw_cuda_graph())
+    n = C.c_size_t(0)
+    assert hip.hipGraphGetNodes(h, None, C.byref(n)) == 0
+    nodes = (C.c_void_p * max(1, n.value))()
+    assert hip.hipGraphGetNodes(h, nodes, C.byref(n)) == 0
+    kernels = 0
+    for i in range(n.value):
+        t = C.c_int(-1)
+        assert hip.hipGraphNodeGetType(C.c_void_p(nodes[i]), C.byref(t)) == 0
+        kernels += t.value == 0  # hipGraphNodeTypeKernel
+    return kernels
+
+
+@pytest.mark.parametrize("P,H", [(4, 4), (24, 4)], ids=["packed", "many_rows"])
+def test_launch_count(P, H):
+    """One packed scoring launch per step (the analogue of sglang PR 45451's
+    verify test, which counts one packed launch per verify forward): scoring
+    is one kernel, selection one, the step two, whatever the request count,
+    formats and graph pads; the NVFP4 store is one."""
+    say("launch count", P, H)
+    for fmt in (W.K_BF16, W.K_FP8_E4M3, W.K_NVFP4):
+        w = W.make(name="launches", R=6, P=P, H=H, k_format=fmt, req_len=[700, 2500, 40, 0, 9000, 131],
+                   topk=5, init_blocks=1, local_blocks=2, seed=530, pads=2, pad_len=3000, device="cuda")
+        outs = Hn.gpu_outputs(w)
+        p = Hn.gpu_params(w, outs)
+        assert _graph_kernel_nodes(lambda: I.idx_score_packed(p)) == 1
+        assert _graph_kernel_nodes(lambda: I.idx_block_topk(p)) == 1
+        assert _graph_kernel_nodes(lambda: I.idx_step(p)) == 2
+        if fmt == W.K_NVFP4:
+            assert _graph_kernel_nodes(lambda: Hn.gpu_fp4_store(w)) == 1
+
+
+@pytest.mark.parametrize("unit_bytes", [1024, 16384, 32768])
+def test_read_probe_reads_every_unit(unit_bytes):
+    """The plain-read probe the benchmark's read ceiling comes from loads
+    every byte of the units it is given: the XOR of its per-workgroup words
+    equals the XOR of those units' 32-bit words (a unit listed twice
+    cancels); ids outside the buffer read unit 0."""
+    say("read probe", unit_bytes)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    n_base = (64 << 20) // unit_bytes
+    base = torch.randint(-2**31, 2**31 - 1, (n_base * unit_bytes // 4,), generator=gen,
+                         dtype=torch.int32, device="cuda")
+    words = base.view(n_base, unit_bytes // 4).cpu().numpy().view(np.uint32)
+    rng = np.random.default_rng(78)
+    units = rng.integers(0, n_base, size=3 * n_base // 2).astype(np.int32)
+    units[::97] = n_base + 5  # out of range: unit 0
+    for ids in (None, units):
+        sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        I.idx_probe_read(base, unit_bytes, None if ids is None else torch.as_tensor(ids, device="cuda"),
+                         sink=sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        eff = np.arange(n_base) if ids is None else np.where(ids >= n_base, 0, ids)
+        counts = np.bincount(eff, minlength=n_base) % 2
+        want = np.bitwise_xor.reduce(words[counts == 1].reshape(-1)) if counts.any() else np.uint32(0)
+        assert got == want, (unit_bytes, ids is None)
 
 
 def test_host_threads_and_streams():

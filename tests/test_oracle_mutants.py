@@ -7,7 +7,7 @@ the fp8-to-bf16 cast dropped, K addressed by group index instead of through
 the slot table) plus ones of this build's own (ties to the higher id, the
 partial-block mask dropped, the sign of zero codes dropped, e2m1 ties away
 from zero, the scale rounded toward zero, nibble order swapped, the init block
-not forced, the lse computed without the softmax scale).  Each is compiled into its own copy of the oracle (ORACLE_MUTANT).
+not forced, the lse computed without the softmax scale, a bad page scored -inf).  Each is compiled into its own copy of the oracle (ORACLE_MUTANT).
 """
 import pytest
 
@@ -30,6 +30,7 @@ MUTANTS = {
     12: "nibble order swapped",
     13: "init block not forced",
     14: "lse without the softmax scale",
+    15: "a visible block on a bad page scored -inf, not NaN",
 }
 
 

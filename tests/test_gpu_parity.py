@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import conftest
 import harness as Hn
 import pins
 from sparse_attention_lightning_amd import idx as I
@@ -373,7 +374,10 @@ def _full(oracle, idx, local_blocks=None, **mode):
     o = oracle.step(**a)
     relaxed = Hn.assert_parity(g, o, a)
     nbs = Hn.row_blocks(a)
-    say(W.CONFIG_NAMES[idx], "rows compared:", g["topk_ids"].shape[0], "near-tie rows:", relaxed)
+    msg = (f"{w.name} local={w.local_blocks} {mode.get('score_mode', 0) and 'lse' or 'max'}: "
+           f"{g['topk_ids'].shape[0]} rows compared, {relaxed} near-tie rows")
+    say(msg)
+    conftest.REPORT.append(msg)
     assert np.isneginf(g["block_scores"][nbs == 0]).all()
     return g, relaxed
 

@@ -194,6 +194,27 @@ int idx_step(const idx_params* p, void* stream);
 /* Message describing the last refusal on the calling thread ("" if none). */
 const char* idx_last_error(void);
 
+/* Largest n_req * packed_queries * gqa * max_blocks of idx_step_noalloc: the
+ * block scores of one step it can hold (16 MiB of fp32 per device). */
+#define IDX_NOALLOC_MAX_SCORES (4 << 20)
+
+/*
+ * idx_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * same kernels as idx_step; the block scores they hand from scoring to
+ * selection live in a library-owned device array of IDX_NOALLOC_MAX_SCORES
+ * floats (16 MiB, one per device, held until the process ends), so
+ * p->block_scores must be NULL and no block scores are returned.  The call
+ * makes no allocation of any kind.  Refusals as for idx_step, and
+ * IDX_E_SHAPE when n_req * packed_queries * gqa * max_blocks exceeds
+ * IDX_NOALLOC_MAX_SCORES.  Every call on a device shares that device's array:
+ * calls whose kernels overlap on one device (several streams, or several
+ * host threads without ordering) race and may select from each other's
+ * scores; order them on one stream.  The array needs no clearing between
+ * calls (the score kernel writes every entry the top-k kernel reads).
+ */
+int idx_step_noalloc(const idx_params* p, void* stream);
+
 /*
  * Measurement aid, not a step of the method: read n_units units of
  * unit_bytes bytes each from `base` with 16-byte loads and nothing else, to

@@ -147,6 +147,32 @@ int idx_step(const idx_params* p, void* stream) {
   return launched(idx::launch_topk(a, (hipStream_t)stream), "top-k");
 }
 
+int idx_step_noalloc(const idx_params* p, void* stream) {
+  if (p && p->block_scores)
+    return fail(IDX_E_SHAPE, "idx_step_noalloc keeps the block scores itself: block_scores must be NULL");
+  if (!p) return fail(IDX_E_NULL, "params is NULL");
+  // the checks of idx_step, with the library's array standing in for block_scores
+  idx_params q = *p;
+  q.block_scores = reinterpret_cast<float*>(uintptr_t{16});  // non-NULL placeholder, never used
+  const int rc = check(&q, kScore | kTopk);
+  if (rc) return rc;
+  const int64_t n = (int64_t)p->n_req * p->packed_queries * p->gqa * p->max_blocks;
+  if (n > IDX_NOALLOC_MAX_SCORES)
+    return fail(IDX_E_SHAPE, "n_req * packed_queries * gqa * max_blocks = %lld exceeds the %d block scores "
+                "idx_step_noalloc holds", (long long)n, IDX_NOALLOC_MAX_SCORES);
+  clear_stale_error();
+  idx::StepArgs a = args_of(p);
+  a.block_scores = nullptr;
+  if (n > 0) {
+    const hipError_t e = idx::noalloc_scores(&a.block_scores);
+    if (e != hipSuccess)
+      return fail(IDX_E_LAUNCH, "device address of the block-score array: %s", hipGetErrorString(e));
+  }
+  const int r1 = launched(idx::launch_score(a, (hipStream_t)stream), "score");
+  if (r1) return r1;
+  return launched(idx::launch_topk(a, (hipStream_t)stream), "top-k");
+}
+
 int idx_probe_read(const void* base, int64_t n_base_units, const int32_t* units, int64_t n_units,
                    int32_t unit_bytes, int32_t nt, uint32_t* sink, int32_t n_sink, void* stream) {
   if (unit_bytes < 1024 || unit_bytes > (1 << 20) || (unit_bytes & (unit_bytes - 1)))

@@ -45,6 +45,9 @@ hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t s
                             int64_t n_slots, hipStream_t stream);
 hipError_t launch_read_probe(const void* base, int64_t n_base_units, const int32_t* units, int64_t n_units,
                              int unit_bytes, bool nt, uint32_t* sink, int n_sink, hipStream_t stream);
+// The device address of this device's block-score array of idx_step_noalloc
+// (looked up on the first call per device).
+hipError_t noalloc_scores(float** out);
 
 __device__ __forceinline__ int clamp_len(int32_t len, int max_blocks) {
   const int cap = max_blocks * kBlock;

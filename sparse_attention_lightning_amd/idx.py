@@ -25,8 +25,9 @@ IDX_MAX_BLOCKS = 8192
 IDX_MAX_REQ = 8192
 IDX_MAX_REQ_ROWS = 65536
 IDX_MAX_ROWS = 1 << 24
+IDX_NOALLOC_MAX_SCORES = 4 << 20
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error",
-           "idx_probe_read")
+           "idx_step_noalloc", "idx_probe_read")
 
 
 class IdxError(RuntimeError):
@@ -62,7 +63,7 @@ def load(path: Path | str | None = None) -> C.CDLL:
     if not p.exists():
         raise RuntimeError(f"HIP library {p} is missing: build it with __graft_entry__.build()")
     lib = C.CDLL(str(p))
-    for name in ("idx_score_packed", "idx_block_topk", "idx_step"):
+    for name in ("idx_score_packed", "idx_block_topk", "idx_step", "idx_step_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = [C.POINTER(IdxParams), C.c_void_p]
         fn.restype = C.c_int
@@ -117,14 +118,16 @@ _ROW_BYTES = {IDX_K_BF16: 256, IDX_K_FP8_E4M3: 128, IDX_K_NVFP4: 64}
 def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
                 k_scale: torch.Tensor | None, req_slot: torch.Tensor,
                 block_table: torch.Tensor | None, row_len: torch.Tensor,
-                block_scores: torch.Tensor, topk_ids: torch.Tensor | None,
+                block_scores: torch.Tensor | None, topk_ids: torch.Tensor | None,
                 topk_scores: torch.Tensor | None, packed_queries: int, gqa: int, topk: int,
                 init_blocks: int, local_blocks: int, max_blocks: int | None = None,
                 n_slot_rows: int | None = None, n_pages: int | None = None,
                 score_mode: int = IDX_SCORE_MAX, sm_scale: float = 0.0) -> IdxParams:
     """Build the parameter block from tensors (sizes read from their shapes
     unless given).  ``score_mode`` IDX_SCORE_LSE takes ``sm_scale``.
-    The returned object keeps the tensors alive."""
+    ``block_scores`` may be None for :func:`idx_step_noalloc` (which keeps
+    them itself; then ``max_blocks`` comes from ``block_table`` or must be
+    given).  The returned object keeps the tensors alive."""
     if k_format not in _K_DTYPES:
         raise ValueError(f"unknown k_format {k_format}")
     p = IdxParams()
@@ -144,7 +147,7 @@ def make_params(*, k_format: int, q: torch.Tensor, k: torch.Tensor | None,
     p.req_slot = _dev(req_slot, "req_slot", (torch.int32,))
     p.block_table = _dev(block_table, "block_table", (torch.int32,), optional=True)
     p.row_len = _dev(row_len, "row_len", (torch.int32,))
-    p.block_scores = _dev(block_scores, "block_scores", (torch.float32,))
+    p.block_scores = _dev(block_scores, "block_scores", (torch.float32,), optional=True)
     p.topk_ids = _dev(topk_ids, "topk_ids", (torch.int32,), optional=True)
     p.topk_scores = _dev(topk_scores, "topk_scores", (torch.float32,), optional=True)
     p.n_req = req_slot.numel()
@@ -195,6 +198,13 @@ def idx_block_topk(p: IdxParams, stream=None) -> None:
 def idx_step(p: IdxParams, stream=None) -> None:
     lib = load()
     _check(lib.idx_step(C.byref(p), _stream(stream)), lib)
+
+
+def idx_step_noalloc(p: IdxParams, stream=None) -> None:
+    """idx_step with the block scores kept in the library's own device array
+    (``p`` built with ``block_scores=None``); allocates nothing."""
+    lib = load()
+    _check(lib.idx_step_noalloc(C.byref(p), _stream(stream)), lib)
 
 
 def idx_probe_read(base: torch.Tensor, unit_bytes: int, units: torch.Tensor | None = None,

@@ -201,9 +201,34 @@ def test_binding_constants_match_header():
         assert m and int(m.group(1)) == getattr(I, name), name
     m = re.search(r"#define\s+IDX_MAX_ROWS\s+\(1 << (\d+)\)", text)
     assert m and (1 << int(m.group(1))) == I.IDX_MAX_ROWS
+    m = re.search(r"#define\s+IDX_NOALLOC_MAX_SCORES\s+\((\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == I.IDX_NOALLOC_MAX_SCORES
     enums = dict((k, int(v)) for k, v in re.findall(r"(IDX_\w+)\s*=\s*(-?\d+)", text))
     for k, v in enums.items():
         assert getattr(I, k) == v, k
+
+
+def test_noalloc_refusals(lib):
+    """idx_step_noalloc keeps the block scores itself: a caller buffer is
+    refused, as is a step whose block scores exceed its array; the other
+    checks are idx_step's."""
+    p = good_params()
+    assert lib.idx_step_noalloc(C.byref(p), None) == I.IDX_E_SHAPE     # block_scores given
+    assert "NULL" in lib.idx_last_error().decode()
+    p.block_scores = None
+    p.head_dim = 64
+    assert lib.idx_step_noalloc(C.byref(p), None) == I.IDX_E_SHAPE     # idx_step's checks apply
+    p = good_params()
+    p.block_scores = None
+    p.topk_ids = None
+    assert lib.idx_step_noalloc(C.byref(p), None) == I.IDX_E_NULL
+    p = good_params()
+    p.block_scores = None
+    p.max_blocks = I.IDX_MAX_BLOCKS
+    p.n_req = I.IDX_NOALLOC_MAX_SCORES // (16 * I.IDX_MAX_BLOCKS) + 1  # one request too many
+    assert lib.idx_step_noalloc(C.byref(p), None) == I.IDX_E_SHAPE
+    assert "exceeds" in lib.idx_last_error().decode()
+    assert lib.idx_step_noalloc(None, None) == I.IDX_E_NULL
 
 
 PROBE_REFUSALS = [

@@ -32,6 +32,18 @@ class OracleParams(C.Structure):
     ]
 
 
+class OracleAttnParams(C.Structure):
+    _fields_ = [
+        ("n_req", C.c_int32), ("n_slot_rows", C.c_int32), ("packed_queries", C.c_int32),
+        ("kv_heads", C.c_int32), ("q_per_kv", C.c_int32), ("head_dim", C.c_int32),
+        ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
+        ("sm_scale", C.c_float), ("n_pages", C.c_int64),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+        ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
+        ("topk_ids", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p), ("out_abs", C.c_void_p),
+    ]
+
+
 _LIBS: dict[str, C.CDLL] = {}
 
 
@@ -48,6 +60,8 @@ def load(path: Path | str | None = None) -> C.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [C.POINTER(OracleParams)]
         fn.restype = C.c_int
+    lib.oracle_sparse_attn.argtypes = [C.POINTER(OracleAttnParams)]
+    lib.oracle_sparse_attn.restype = C.c_int
     lib.oracle_fp4_store.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_int64]
     lib.oracle_fp4_store.restype = C.c_int
@@ -198,3 +212,36 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_step refused its arguments or ran out of memory ({rc})")
         return outs
+
+    # -- sparse attention over the selected blocks ---------------------------
+    def sparse_attn(self, **a) -> dict:
+        """out [rows, H, G, 128], lse [rows, H, G] and out_abs (the weighted
+        |V| that scales out's rounding error) as float32 arrays."""
+        R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
+        MB, K, n_pages = a["max_blocks"], a["topk"], a["n_pages"]
+        q = _arr(a["q"], np.uint16)
+        k = _arr(a["k"], np.uint16)
+        v = _arr(a["v"], np.uint16)
+        req_slot = _arr(a["req_slot"], np.int32)
+        bt = _arr(a["block_table"], np.int32)
+        row_len = _arr(a["row_len"], np.int32)
+        ids = _arr(a["topk_ids"], np.int32)
+        assert q.size == R * P * H * G * 128 and row_len.size == R * P and req_slot.size == R
+        assert bt.size == a["n_slot_rows"] * MB and ids.size == R * P * H * K
+        assert k.size == n_pages * H * 128 * 128 and v.size == k.size
+        out = np.full((R * P, H, G, 128), np.nan, np.float32)
+        lse = np.full((R * P, H, G), np.nan, np.float32)
+        oabs = np.full_like(out, np.nan)
+        pr = OracleAttnParams()
+        for f in ("n_req", "n_slot_rows", "packed_queries", "kv_heads", "q_per_kv", "max_blocks", "topk",
+                  "n_pages"):
+            setattr(pr, f, int(a[f]))
+        pr.head_dim, pr.block_size = 128, 128
+        pr.sm_scale = float(a["sm_scale"])
+        pr.q, pr.k, pr.v = _ptr(q), _ptr(k), _ptr(v)
+        pr.req_slot, pr.block_table, pr.row_len, pr.topk_ids = _ptr(req_slot), _ptr(bt), _ptr(row_len), _ptr(ids)
+        pr.out, pr.lse, pr.out_abs = _ptr(out), _ptr(lse), _ptr(oabs)
+        rc = self.lib.oracle_sparse_attn(C.byref(pr))
+        if rc:
+            raise ValueError(f"oracle_sparse_attn refused its arguments or ran out of memory ({rc})")
+        return {"out": out, "lse": lse, "out_abs": oabs}

@@ -427,6 +427,137 @@ int oracle_step(const oracle_params* p) {
   return rc ? rc : oracle_block_topk(p);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Sparse attention over the selected blocks (readings in oracle.h)         */
+/* ------------------------------------------------------------------------ */
+
+int oracle_sparse_attn(const oracle_attn_params* p) {
+  int P, H, G, MB, K, failed = 0;
+  int64_t item, n_items;
+  if (!p || p->head_dim != 128 || p->block_size != 128 || p->n_req < 0 || p->packed_queries < 1 ||
+      p->kv_heads < 1 || p->q_per_kv < 1 || p->max_blocks < 0 || p->topk < 0 || p->n_slot_rows < 0 ||
+      p->n_pages < 0 || !(p->sm_scale > 0.0f && isfinite(p->sm_scale)))
+    return -1;
+  P = p->packed_queries;
+  H = p->kv_heads;
+  G = p->q_per_kv;
+  MB = p->max_blocks;
+  K = p->topk;
+  n_items = (int64_t)p->n_req * P * H * G;
+  if (n_items == 0) return 0;
+  if (!p->q || !p->req_slot || !p->row_len || !p->out || !p->lse ||
+      (K > 0 && !p->topk_ids) || (MB > 0 && p->n_slot_rows > 0 && !p->block_table) ||
+      (p->n_pages > 0 && (!p->k || !p->v)))
+    return -1;
+
+#pragma omp parallel for schedule(dynamic, 4)
+  for (item = 0; item < n_items; item++) {
+    /* item = ((row * H + h) * G + g), row = r * P + j */
+    int64_t row = item / ((int64_t)H * G);
+    int h = (int)((item / G) % H);
+    int g = (int)(item % G);
+    int r = (int)(row / P);
+    int hs = MUTANT(19) ? (h + 1) % H : h; /* mutant 19: another head's selection */
+    const uint16_t* q = (const uint16_t*)p->q;
+    const uint16_t* kp = (const uint16_t*)p->k;
+    const uint16_t* vp = (const uint16_t*)p->v;
+    int64_t qrow = MUTANT(22) ? (row * G + g) * H + h : item; /* mutant 22: heads in the wrong order */
+    float* out = p->out + item * 128;
+    float* oabs = p->out_abs ? p->out_abs + item * 128 : NULL;
+    unsigned char* sel;
+    double* sc;
+    int64_t* tok; /* (page * H + h) * 128 + t of each visible token */
+    int slot, len, nb, b, t, d, e, n = 0, bad = 0;
+    double m = -INFINITY, l = 0.0, o[128], oa[128];
+
+    for (d = 0; d < 128; d++) {
+      out[d] = 0.0f;
+      if (oabs) oabs[d] = 0.0f;
+    }
+    p->lse[item] = -INFINITY;
+    slot = p->req_slot[r];
+    if (slot < 0 || slot >= p->n_slot_rows) continue; /* graph pad */
+    {
+      int64_t cap = (int64_t)MB * 128;
+      int32_t raw = p->row_len[row];
+      len = raw < 0 ? 0 : (int)((int64_t)raw > cap ? cap : raw);
+    }
+    nb = (len + 127) / 128;
+    if (nb == 0) continue;
+
+    sel = (unsigned char*)calloc((size_t)nb, 1);
+    sc = (double*)malloc(sizeof(double) * (size_t)nb * 128);
+    tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)nb * 128);
+    if (!sel || !sc || !tok) {
+#pragma omp atomic write
+      failed = 1;
+      free(sel);
+      free(sc);
+      free(tok);
+      continue;
+    }
+    /* the selected set (only blocks the row can see matter) */
+    if (MUTANT(18)) {
+      for (b = 0; b < nb; b++) sel[b] = 1; /* mutant 18: selection ignored */
+    } else {
+      const int32_t* ids = p->topk_ids + (row * H + hs) * K;
+      for (e = 0; e < K; e++)
+        if (ids[e] >= 0 && ids[e] < nb) sel[ids[e]] = 1;
+    }
+    /* scaled scores of the visible tokens of the selected blocks */
+    for (b = 0; b < nb; b++) {
+      int64_t page;
+      if (!sel[b]) continue;
+      page = p->block_table[(int64_t)slot * MB + b];
+      if (page < 0 || page >= p->n_pages) {
+        bad = 1; /* the row sees at least token 128 b of this block */
+        continue;
+      }
+      for (t = 0; t < 128; t++) {
+        double s = 0.0;
+        int64_t kt = (page * H + h) * 128 + t;
+        if (128 * b + t >= len && !MUTANT(17)) break; /* mutant 17: length mask dropped */
+        for (d = 0; d < 128; d++) s += bf16_value(q[qrow * 128 + d]) * bf16_value(kp[kt * 128 + d]);
+        sc[n] = MUTANT(16) ? s : (double)p->sm_scale * s; /* mutant 16: scale dropped */
+        tok[n] = kt;
+        n++;
+      }
+    }
+    if (bad) {
+      for (d = 0; d < 128; d++) {
+        out[d] = NAN;
+        if (oabs) oabs[d] = NAN;
+      }
+      p->lse[item] = NAN;
+    } else if (n > 0) {
+      for (e = 0; e < n; e++)
+        if (sc[e] > m) m = sc[e];
+      for (d = 0; d < 128; d++) o[d] = oa[d] = 0.0;
+      for (e = 0; e < n; e++) {
+        double w = exp(sc[e] - m);
+        int64_t page_h = tok[e] / 128; /* (page * H + h) */
+        int tt = (int)(tok[e] % 128);
+        l += w;
+        for (d = 0; d < 128; d++) {
+          /* V is [page][h][dim][token]; mutant 21 reads it as [token][dim] */
+          double v = bf16_value(vp[MUTANT(21) ? tok[e] * 128 + d : (page_h * 128 + d) * 128 + tt]);
+          o[d] += w * v;
+          oa[d] += w * fabs(v);
+        }
+      }
+      for (d = 0; d < 128; d++) {
+        out[d] = (float)(MUTANT(20) ? o[d] : o[d] / l); /* mutant 20: not normalized */
+        if (oabs) oabs[d] = (float)(oa[d] / l);
+      }
+      p->lse[item] = (float)(m + log(l));
+    }
+    free(sel);
+    free(sc);
+    free(tok);
+  }
+  return failed ? -1 : 0;
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

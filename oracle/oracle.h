@@ -95,6 +95,54 @@ int oracle_fp4_store(const void* staging_bf16, int64_t n_tokens,
                      int64_t staging_row_stride, const int64_t* slot_mapping,
                      uint8_t* payload, uint8_t* scales, int64_t n_slots);
 
+/*
+ * Sparse attention over the selected blocks (the step after selection: the
+ * sparse kernel whose tests the sglang PR 45451 Accuracy Tests run beside the
+ * packed scorer, and the fused verify kernel timed in the ROCm/ATOM PR 2745
+ * Validation).  The pages fix none of its shapes; the readings taken:
+ *  - grouped-query attention with kv_heads = the indexer's gqa index heads
+ *    (index head h selects the blocks of KV head h) and q_per_kv query heads
+ *    per KV head, head dimension 128;
+ *  - query head g of KV head h of draft row j attends over the tokens of the
+ *    blocks in topk_ids[row][h][.] (ids outside [0, max_blocks) ignored, an id
+ *    listed twice counts once) that the row sees: position 128 b + t < the
+ *    row's length, the same causal length as the indexer;
+ *  - K and V are paged like the index K (page = block = 128 tokens, the same
+ *    request slots and block table), bf16, K as [n_pages][kv_heads][128
+ *    tokens][128] and V as [n_pages][kv_heads][128 dims][128 tokens];
+ *  - out = sum_t softmax_t(sm_scale * q.k_t) v_t and lse = ln sum_t
+ *    exp(sm_scale * q.k_t); a row that sees no selected token gets out = 0 and
+ *    lse = -inf, as do graph pads; a row that sees a token of a block whose
+ *    page id is outside [0, n_pages) gets NaN in both.
+ * Everything in double, rounded once to float at the end.
+ */
+typedef struct oracle_attn_params {
+  int32_t n_req;          /* requests, graph pads included                      */
+  int32_t n_slot_rows;
+  int32_t packed_queries; /* P: draft rows per request                          */
+  int32_t kv_heads;       /* H: KV heads = index heads                          */
+  int32_t q_per_kv;       /* G: query heads per KV head                         */
+  int32_t head_dim;       /* 128                                                 */
+  int32_t block_size;     /* 128                                                 */
+  int32_t max_blocks;
+  int32_t topk;           /* ids per (draft row, KV head)                       */
+  float   sm_scale;
+  int64_t n_pages;
+  const void*    q;        /* bf16 [n_req*P][H][G][128]                          */
+  const void*    k;        /* bf16 [n_pages][H][128 tokens][128]                 */
+  const void*    v;        /* bf16 [n_pages][H][128 dims][128 tokens]            */
+  const int32_t* req_slot;    /* [n_req]                                         */
+  const int32_t* block_table; /* [n_slot_rows][max_blocks]                       */
+  const int32_t* row_len;     /* [n_req*P]                                       */
+  const int32_t* topk_ids;    /* [n_req*P][H][topk]                              */
+  float* out;              /* [n_req*P][H][G][128]                               */
+  float* lse;              /* [n_req*P][H][G]                                    */
+  float* out_abs;          /* optional, like out: sum_t softmax_t |v_t|, the
+                              scale of out's rounding error                      */
+} oracle_attn_params;
+
+int oracle_sparse_attn(const oracle_attn_params* p);
+
 /* OpenMP threads the oracle's parallel loops use. */
 int oracle_threads(void);
 /* Threads for the calling thread's later calls (n > 0); returns the count before. */

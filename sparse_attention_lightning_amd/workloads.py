@@ -310,3 +310,63 @@ def config(idx: int, device: str | torch.device = "cpu", local_blocks: int | Non
         name = name.replace(short[kw["k_format"]], short[k_format], 1)
         kw["k_format"] = k_format
     return make(name=name, req_len=lens, seed=seed, device=device, rng=rng, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the sparse attention that follows selection
+# ---------------------------------------------------------------------------
+POISON_ATTN_V = 1.0e4   # V where no row may look: a leaked token moves its row's output by ~1e4 / n
+
+
+@dataclass
+class AttnInputs:
+    q_per_kv: int
+    q: torch.Tensor     # bf16 [n_req*P, H, G, 128]: query head g of KV head h of each draft row
+    k: torch.Tensor     # bf16 [n_pages, H, 128 tokens, 128]
+    v: torch.Tensor     # bf16 [n_pages, H, 128 dims, 128 tokens] (each page-head's V transposed)
+    seed: int
+
+
+def make_attn(w: Workload, q_per_kv: int, seed: int | None = None, poison: bool = True) -> AttnInputs:
+    """Seeded N(0,1) attention queries, keys and values over the workload's
+    page pool (the same pages, slots and row lengths as its index K; the KV
+    heads are the workload's gqa index heads).  Gap pages and the tail of
+    each request's last page get K = 0 and V = POISON_ATTN_V, so a token no
+    row may see would move that row's output by far more than any tolerance."""
+    seed = w.seed + 500 if seed is None else seed
+    dev = w.q.device
+    H, n_pages = w.gqa, w.n_pages
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    q = torch.empty((w.n_req * w.packed_queries, H, q_per_kv, D), dtype=torch.bfloat16, device=dev)
+    _randn_into(q.view(-1, D), gen)
+    k = torch.empty((n_pages, H, BLOCK, D), dtype=torch.bfloat16, device=dev)
+    _randn_into(k.view(-1, D), gen)
+    v = torch.empty((n_pages, H, D, BLOCK), dtype=torch.bfloat16, device=dev)
+    _randn_into(v.view(-1, BLOCK), gen)
+    if poison:
+        gap = w.extra["gap_pages"]
+        if len(gap):
+            gi = torch.as_tensor(gap, device=dev)
+            k[gi] = 0
+            v[gi] = POISON_ATTN_V
+        for pg, off in w.extra["tails"]:
+            k[pg, :, off:, :] = 0
+            v[pg, :, :, off:] = POISON_ATTN_V
+    return AttnInputs(q_per_kv=q_per_kv, q=q, k=k, v=v, seed=seed)
+
+
+def attn_oracle_args(w: Workload, at: AttnInputs, topk_ids, sm_scale: float) -> dict:
+    """Keyword arguments of the oracle's sparse attention (numpy, host) for
+    the selection ``topk_ids`` ([n_req*P*H, topk] int32, numpy or torch)."""
+    def u16(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    ids = topk_ids.detach().cpu().numpy() if isinstance(topk_ids, torch.Tensor) else np.asarray(topk_ids)
+    ids = np.ascontiguousarray(ids.astype(np.int32).reshape(w.n_req * w.packed_queries * w.gqa, -1))
+    return dict(n_req=w.n_req, n_slot_rows=w.n_slot_rows, packed_queries=w.packed_queries,
+                kv_heads=w.gqa, q_per_kv=at.q_per_kv, max_blocks=w.max_blocks, topk=ids.shape[1],
+                sm_scale=sm_scale, n_pages=w.n_pages, q=u16(at.q), k=u16(at.k), v=u16(at.v),
+                req_slot=w.req_slot.cpu().numpy().astype(np.int32),
+                block_table=w.block_table.cpu().numpy().astype(np.int32),
+                row_len=w.row_len.cpu().numpy().astype(np.int32), topk_ids=ids)

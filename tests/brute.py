@@ -96,3 +96,88 @@ def select(block_scores: np.ndarray, nb: np.ndarray, topk: int, init: int, local
         ids[o, : len(chosen)] = chosen
         sc[o, : len(chosen)] = block_scores[o, chosen]
     return ids, sc
+
+
+# ---------------------------------------------------------------------------
+# sparse attention over the selected blocks
+# ---------------------------------------------------------------------------
+def _attn_rows(a: dict):
+    """Yield (row, h, g, visible token list as (page, t), bad) per query head."""
+    R, P, H, G, MB, K = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"], a["max_blocks"], a["topk"]
+    bt = a["block_table"].reshape(a["n_slot_rows"], MB)
+    ids = a["topk_ids"].reshape(R * P, H, K)
+    for row in range(R * P):
+        r = row // P
+        slot = int(a["req_slot"][r])
+        pad = not (0 <= slot < a["n_slot_rows"])
+        n = int(min(max(int(a["row_len"][row]), 0), MB * 128))
+        for h in range(H):
+            toks, bad = [], False
+            if not pad:
+                chosen = sorted({int(b) for b in ids[row, h] if 0 <= b < math.ceil(n / 128)})
+                for b in chosen:
+                    page = int(bt[slot, b])
+                    if not (0 <= page < a["n_pages"]):
+                        bad = True
+                        continue
+                    toks += [(page, t) for t in range(min(128, n - 128 * b))]
+            for g in range(G):
+                yield row, h, g, toks, bad
+
+
+def sparse_attn(a: dict) -> dict:
+    """fp64 reference: for each query head, scipy's softmax and logsumexp over
+    the scaled dots with the visible tokens of its selected blocks (numpy
+    gathers and matmuls), then the weighted sum of their V columns."""
+    from scipy.special import logsumexp, softmax
+    R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
+    q = bf16_values(a["q"]).reshape(R * P, H, G, 128)
+    k = bf16_values(a["k"]).reshape(a["n_pages"], H, 128, 128)
+    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 128, 128)   # [page][h][dim][token]
+    scale = float(np.float32(a["sm_scale"]))  # the softmax scale crosses the interface as fp32
+    out = np.zeros((R * P, H, G, 128))
+    lse = np.full((R * P, H, G), -np.inf)
+    for row, h, g, toks, bad in _attn_rows(a):
+        if bad:
+            out[row, h, g], lse[row, h, g] = np.nan, np.nan
+            continue
+        if not toks:
+            continue
+        pg = np.array([p for p, _ in toks])
+        tt = np.array([t for _, t in toks])
+        s = scale * (k[pg, h, tt, :] @ q[row, h, g])
+        out[row, h, g] = softmax(s) @ v[pg, h, :, tt]
+        lse[row, h, g] = logsumexp(s)
+    return {"out": out, "lse": lse}
+
+
+def sparse_attn_loops(a: dict) -> dict:
+    """The same in plain Python loops and math.exp (tiny inputs only)."""
+    R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
+    q = bf16_values(a["q"]).reshape(R * P, H, G, 128).tolist()
+    k = bf16_values(a["k"]).reshape(a["n_pages"], H, 128, 128)
+    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 128, 128)
+    out = [[[[0.0] * 128 for _ in range(G)] for _ in range(H)] for _ in range(R * P)]
+    lse = [[[-math.inf] * G for _ in range(H)] for _ in range(R * P)]
+    for row, h, g, toks, bad in _attn_rows(a):
+        if bad:
+            out[row][h][g] = [math.nan] * 128
+            lse[row][h][g] = math.nan
+            continue
+        if not toks:
+            continue
+        s = []
+        for p_, t in toks:
+            kr = k[p_, h, t].tolist()
+            s.append(float(np.float32(a["sm_scale"])) * sum(x * y for x, y in zip(q[row][h][g], kr)))
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        tot = sum(w)
+        o = [0.0] * 128
+        for wi, (p_, t) in zip(w, toks):
+            col = v[p_, h, :, t].tolist()
+            for d in range(128):
+                o[d] += wi * col[d]
+        out[row][h][g] = [x / tot for x in o]
+        lse[row][h][g] = m + math.log(tot)
+    return {"out": np.array(out), "lse": np.array(lse)}

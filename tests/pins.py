@@ -654,6 +654,220 @@ def pin_bad_page_ids(o) -> None:
                     assert b < 1 or b >= nb - 1 or nb <= 6, f"row {o_} selected NaN block {b}"
 
 
+# ---------------------------------------------------------------------------
+# sparse attention over the selected blocks
+# ---------------------------------------------------------------------------
+ATTN_SCALE = float(np.float32(128 ** -0.5))  # an fp32 number, as the interface carries it
+
+
+def attn_workload(seed: int, lens=(0, 130, 700, 1500), P: int = 3, H: int = 2, G: int = 3, pads: int = 1):
+    w = W.make(name="attn", R=len(lens), P=P, H=H, k_format=W.K_BF16, req_len=list(lens), topk=4,
+                init_blocks=1, local_blocks=1, seed=seed, pads=pads, pad_len=900)
+    return w, W.make_attn(w, G, seed=seed + 1)
+
+
+def random_selection(w, rng, topk: int, messy: bool = True) -> np.ndarray:
+    """Per (draft row, KV head) a random set of the row's blocks, ascending,
+    padded with -1; with ``messy`` some rows also list an id twice, an id
+    past the row's blocks and one past max_blocks (all to be ignored)."""
+    rows = w.n_req * w.packed_queries
+    lens = w.row_len.numpy()
+    ids = np.full((rows, w.gqa, topk), -1, np.int32)
+    for row in range(rows):
+        nb = (int(lens[row]) + 127) // 128
+        for h in range(w.gqa):
+            n = int(min(nb, rng.integers(1, topk - 2))) if nb else 0
+            chosen = np.sort(rng.choice(nb, size=n, replace=False)) if n else np.zeros(0, int)
+            ids[row, h, :n] = chosen
+            if messy and n and rng.random() < 0.6:
+                ids[row, h, n:n + 3] = [chosen[0], nb + 1, w.max_blocks + 7][: topk - n]
+    return ids
+
+
+def assert_attn_close(got: dict, want: dict, what: str, rtol: float = 1e-6) -> None:
+    for key in ("out", "lse"):
+        g = np.asarray(got[key], np.float64)
+        x = np.asarray(want[key], np.float64)
+        assert g.shape == x.shape, (what, key, g.shape, x.shape)
+        assert np.array_equal(np.isnan(g), np.isnan(x)), f"{what} {key}: NaN layout differs"
+        assert np.array_equal(np.isinf(g), np.isinf(x)), f"{what} {key}: inf layout differs"
+        f = np.isfinite(x)
+        err = np.abs(g[f] - x[f]) / np.maximum(np.abs(x[f]), 1e-3)
+        assert err.size == 0 or err.max() <= rtol, f"{what} {key}: max rel err {err.max():.3g}"
+
+
+def pin_attn_bruteforce(o) -> None:
+    """Oracle against scipy's softmax / logsumexp and numpy gathers over the
+    visible tokens of each row's selected blocks: random selections (with
+    duplicates, ids past the row and past max_blocks), partial last blocks,
+    several KV heads and query heads a KV head, a graph pad."""
+    w, at = attn_workload(611)
+    ids = random_selection(w, np.random.default_rng(612), topk=6)
+    a = W.attn_oracle_args(w, at, ids, ATTN_SCALE)
+    assert_attn_close(o.sparse_attn(**a), brute.sparse_attn(a), "attn brute force")
+
+
+def pin_attn_loops(o) -> None:
+    """The same against plain Python loops and math.exp on a tiny case."""
+    w, at = attn_workload(621, lens=(40, 200), P=2, H=2, G=2, pads=0)
+    ids = random_selection(w, np.random.default_rng(622), topk=4)
+    a = W.attn_oracle_args(w, at, ids, 0.3)
+    assert_attn_close(o.sparse_attn(**a), brute.sparse_attn_loops(a), "attn loops")
+
+
+def pin_attn_dense(o) -> None:
+    """Every block selected: causal attention over the whole visible context,
+    from torch's scaled_dot_product_attention in float64 with each row's
+    length mask (and torch.logsumexp for the lse)."""
+    w, at = attn_workload(631, lens=(129, 300, 1022), P=4, H=2, G=2, pads=0)
+    R, P, H, G = w.n_req, 4, 2, 2
+    lens = w.row_len.numpy()
+    nbmax = int((lens.max() + 127) // 128)
+    ids = np.full((R * P, H, nbmax), -1, np.int32)
+    for row in range(R * P):
+        nb = (int(lens[row]) + 127) // 128
+        ids[row, :, :nb] = np.arange(nb)
+    a = W.attn_oracle_args(w, at, ids, ATTN_SCALE)
+    got = o.sparse_attn(**a)
+    k64 = at.k.to(torch.float64)
+    v64 = at.v.to(torch.float64)
+    q64 = at.q.to(torch.float64)
+    bt = w.block_table.numpy()
+    for r in range(R):
+        slot = int(w.req_slot[r])
+        L = int(lens[r * P: r * P + P].max())
+        pages = torch.as_tensor(bt[slot, : (L + 127) // 128].astype(np.int64))
+        for h in range(H):
+            kc = k64[pages, h].reshape(-1, 128)[:L]                       # [L, 128] in position order
+            vc = v64[pages, h].permute(0, 2, 1).reshape(-1, 128)[:L]      # [L, 128]
+            for j in range(P):
+                row = r * P + j
+                mask = torch.arange(L) < int(lens[row])
+                qq = q64[row, h][None, :, None, :]                        # [1, G, 1, 128]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qq, kc[None, None].expand(1, G, L, 128), vc[None, None].expand(1, G, L, 128),
+                    attn_mask=mask[None, None, None, :], scale=ATTN_SCALE)[0, :, 0, :]
+                s = ATTN_SCALE * (q64[row, h] @ kc.T)
+                lse = torch.logsumexp(s.masked_fill(~mask[None, :], -math.inf), dim=1)
+                assert_attn_close({"out": got["out"][row, h], "lse": got["lse"][row, h]},
+                                  {"out": ref.numpy(), "lse": lse.numpy()}, f"dense row {row} head {h}")
+
+
+def pin_attn_closed_forms(o) -> None:
+    """(1) The same V column for every token: the output is that column,
+    exactly, whatever the weights.  (2) The same key for every token: the
+    weights are uniform, so the output is the mean of the visible selected V
+    columns and lse = c q.k0 + ln n.  (3) A row of one token: its V column,
+    lse = c q.k."""
+    rng = np.random.default_rng(641)
+    w, at = attn_workload(641)
+    ids = random_selection(w, rng, topk=6, messy=False)
+    R, P, H, G = w.n_req, w.packed_queries, w.gqa, at.q_per_kv
+    col = torch.randn(128, generator=torch.Generator().manual_seed(642)).to(torch.bfloat16)
+    v_const = at.v.clone()
+    v_const[:] = col[None, None, :, None]
+    res = o.sparse_attn(**W.attn_oracle_args(w, W.AttnInputs(G, at.q, at.k, v_const, at.seed), ids, ATTN_SCALE))
+    lens = w.row_len.numpy()
+    for row in range(R * P):
+        r = row // P
+        real = r < w.n_real and lens[row] > 0
+        for h in range(H):
+            if real and (ids[row, h] >= 0).any():
+                assert np.array_equal(res["out"][row, h], np.broadcast_to(col.float().numpy(), (G, 128))), \
+                    f"constant V: row {row} head {h}"
+            else:
+                assert (res["out"][row, h] == 0).all() and np.isneginf(res["lse"][row, h]).all()
+    # (2) equal keys
+    k0 = torch.randn(128, generator=torch.Generator().manual_seed(643)).to(torch.bfloat16)
+    k_eq = at.k.clone()
+    k_eq[:] = k0
+    res = o.sparse_attn(**W.attn_oracle_args(w, W.AttnInputs(G, at.q, k_eq, at.v, at.seed), ids, ATTN_SCALE))
+    v64 = at.v.to(torch.float64).numpy()
+    bt = w.block_table.numpy()
+    q64 = at.q.to(torch.float64).numpy()
+    for row in range(R * P):
+        r = row // P
+        if r >= w.n_real or lens[row] == 0:
+            continue
+        for h in range(H):
+            cols = []
+            for b in sorted(set(ids[row, h][ids[row, h] >= 0].tolist())):
+                page = bt[int(w.req_slot[r]), b]
+                cols += [v64[page, h, :, t] for t in range(min(128, int(lens[row]) - 128 * b))]
+            n = len(cols)
+            s0 = ATTN_SCALE * (q64[row, h] @ k0.double().numpy())
+            assert_attn_close({"out": res["out"][row, h], "lse": res["lse"][row, h]},
+                              {"out": np.broadcast_to(np.mean(cols, axis=0), (G, 128)), "lse": s0 + math.log(n)},
+                              f"equal keys row {row} head {h}", rtol=1e-5)
+    # (3) one visible token
+    w1, at1 = attn_workload(644, lens=(1, 1), P=1, H=2, G=3, pads=0)
+    ids1 = np.zeros((2, 2, 1), np.int32)
+    res = o.sparse_attn(**W.attn_oracle_args(w1, at1, ids1, ATTN_SCALE))
+    bt1 = w1.block_table.numpy()
+    for r in range(2):
+        page = bt1[int(w1.req_slot[r]), 0]
+        for h in range(2):
+            want = at1.v[page, h, :, 0].float().numpy()
+            assert np.array_equal(res["out"][r, h], np.broadcast_to(want, (3, 128))), "one token: V column"
+            s = ATTN_SCALE * (at1.q[r, h].double().numpy() @ at1.k[page, h, 0].double().numpy())
+            assert np.allclose(res["lse"][r, h], s, rtol=1e-6, atol=1e-6), "one token: lse"
+
+
+def pin_attn_invariants(o) -> None:
+    """Reordered, duplicated and ignored ids change nothing; neither do the
+    K and V of unselected blocks and of tokens past a row's length; graph
+    pads give 0 and -inf; a selected block on a page outside the pool makes
+    exactly the rows that see it NaN."""
+    rng = np.random.default_rng(651)
+    w, at = attn_workload(651)
+    ids = random_selection(w, rng, topk=7, messy=False)
+    a = W.attn_oracle_args(w, at, ids, ATTN_SCALE)
+    base = o.sparse_attn(**a)
+    shuffled = ids.copy()
+    for row in range(ids.shape[0]):
+        for h in range(ids.shape[1]):
+            sel = ids[row, h][ids[row, h] >= 0]
+            extra = [-1, w.max_blocks, 99999] + (list(sel[:1]) if len(sel) else [])
+            lst = list(rng.permutation(sel)) + extra
+            shuffled[row, h] = (lst + [-1] * 7)[:7]
+    got = o.sparse_attn(**dict(a, topk_ids=shuffled))
+    for key in base:
+        assert same(got[key], base[key]), f"id order / duplicates / ignored ids changed {key}"
+    # poison what no row of that head may use: unselected blocks, tokens past each row
+    k2, v2 = at.k.clone(), at.v.clone()
+    bt = w.block_table.numpy()
+    lens = w.row_len.numpy()
+    P = w.packed_queries
+    for r in range(w.n_real):
+        slot = int(w.req_slot[r])
+        nbg = (int(lens[r * P: r * P + P].max()) + 127) // 128
+        for h in range(w.gqa):
+            used = set(ids[r * P: r * P + P, h][ids[r * P: r * P + P, h] >= 0].tolist())
+            for b in range(nbg):
+                if b not in used:
+                    k2[bt[slot, b], h] = 7
+                    v2[bt[slot, b], h] = -5000
+    res = o.sparse_attn(**W.attn_oracle_args(w, W.AttnInputs(at.q_per_kv, at.q, k2, v2, at.seed), ids, ATTN_SCALE))
+    for key in base:
+        assert same(res[key], base[key]), f"unselected blocks changed {key}"
+    n_real_rows = w.n_real * P
+    assert (base["out"][n_real_rows:] == 0).all() and np.isneginf(base["lse"][n_real_rows:]).all(), "pads"
+    # a selected block on a bad page
+    bt_bad = bt.copy()
+    row, h = 3 * P - 1, 1            # request 2's longest row, head 1
+    b = int(ids[row, h][0])
+    bt_bad[int(w.req_slot[2]), b] = w.n_pages + 3
+    res = o.sparse_attn(**dict(a, block_table=np.ascontiguousarray(bt_bad)))
+    for rr in range(ids.shape[0]):
+        for hh in range(w.gqa):
+            sees = (rr // P == 2 and b in ids[rr, hh].tolist() and 128 * b < lens[rr])
+            if sees:
+                assert np.isnan(res["out"][rr, hh]).all() and np.isnan(res["lse"][rr, hh]).all(), (rr, hh)
+            else:
+                assert same(res["out"][rr, hh], base["out"][rr, hh]), (rr, hh)
+    assert np.isnan(res["lse"][row, h]).all()
+
+
 PINS = [
     pin_fp8_decode, pin_e2m1_decode, pin_golden_store, pin_fp4_roundtrip,
     pin_bruteforce_bf16, pin_bruteforce_fp8, pin_bruteforce_fp4, pin_fp4_equals_bf16_of_dequant,
@@ -661,5 +875,6 @@ PINS = [
     pin_topk_textbook, pin_topk_bruteforce, pin_topk_invariants, pin_exact_tie, pin_straddle,
     pin_packed_equals_per_row, pin_many_rows_equal_per_row, pin_masking, pin_slot_permutation,
     pin_graph_pads, pin_bad_page_ids,
+    pin_attn_bruteforce, pin_attn_loops, pin_attn_dense, pin_attn_closed_forms, pin_attn_invariants,
     pin_scale_rounding, pin_code_rounding,
 ]

@@ -7,7 +7,10 @@ the fp8-to-bf16 cast dropped, K addressed by group index instead of through
 the slot table) plus ones of this build's own (ties to the higher id, the
 partial-block mask dropped, the sign of zero codes dropped, e2m1 ties away
 from zero, the scale rounded toward zero, nibble order swapped, the init block
-not forced, the lse computed without the softmax scale, a bad page scored -inf).  Each is compiled into its own copy of the oracle (ORACLE_MUTANT).
+not forced, the lse computed without the softmax scale, a bad page scored -inf) and, for the
+sparse attention over the selected blocks, the scale dropped, the length mask dropped, the
+selection ignored, another head's selection, no normalization, V read untransposed and query heads
+out of order.  Each is compiled into its own copy of the oracle (ORACLE_MUTANT).
 """
 import pytest
 
@@ -31,6 +34,13 @@ MUTANTS = {
     13: "init block not forced",
     14: "lse without the softmax scale",
     15: "a visible block on a bad page scored -inf, not NaN",
+    16: "attention: softmax scale dropped",
+    17: "attention: length mask dropped",
+    18: "attention: selection ignored (every block attended)",
+    19: "attention: another KV head's selection",
+    20: "attention: output not normalized",
+    21: "attention: V read untransposed",
+    22: "attention: query heads in the wrong order",
 }
 
 

@@ -52,6 +52,9 @@ def parse() -> argparse.Namespace:
                     help="steps of the event-timed kernel pass (default max(20, min(steps, 100)))")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the plain-read measurement of the step's K pages")
+    ap.add_argument("--attn-q-per-kv", type=int, default=4,
+                    help="query heads per KV head of the sparse attention measured after the step "
+                         "(0: skip it; packed_queries * this must be <= 16)")
     ap.add_argument("--score-mode", choices=("max", "lse"), default="max",
                     help="block reduction: max (default) or lse")
     ap.add_argument("--sm-scale", type=float, default=1 / 128 ** 0.5,
@@ -272,6 +275,9 @@ def main() -> int:
     if fp4:
         line["fp4_store_step_tokens"] = int(step_staging.shape[0])
         line["fp4_store_pool"] = pool_store
+    if args.attn_q_per_kv and P * args.attn_q_per_kv <= 16:
+        line["sparse_attn"] = bench_attn(w, outs["topk_ids"], args.attn_q_per_kv, flush, stream,
+                                         n_ev=max(10, min(args.steps, 50)))
     if not args.no_read_ceiling and P * H <= 16:
         line["hbm_read_ceiling"] = read_ceiling(w, flush, stream)
         line["score_frac_of_page_gather"] = round(achieved / line["hbm_read_ceiling"]["page_gather_GBps"], 4)
@@ -280,6 +286,70 @@ def main() -> int:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests, args.cpu_rows, mode)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def bench_attn(w, topk_ids, G: int, flush, stream, n_ev: int) -> dict:
+    """The sparse attention over the blocks the step just selected: bf16 K
+    and V pools of the workload's page count, G query heads per KV head,
+    softmax scale 1/sqrt(128).  Timed with HIP events around each call (its
+    two launches), mean of ``n_ev`` calls after 3 warm-ups.  Algorithmic bytes:
+    for every (request, KV head), the K and V of each block in the union of
+    its draft rows' selections, up to the longest of those rows' visible
+    tokens in it (256 + 256 B a token), plus queries, ids and outputs."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_lightning_amd import idx as I
+    from sparse_attention_lightning_amd import workloads as W
+
+    at = W.make_attn(w, G)
+    P, H, R = w.packed_queries, w.gqa, w.n_req
+    out = torch.empty_like(at.q)
+    lse = torch.empty(at.q.shape[:3], dtype=torch.float32, device=at.q.device)
+    p = I.make_attn_params(q=at.q, k=at.k, v=at.v, req_slot=w.req_slot, block_table=w.block_table,
+                           row_len=w.row_len, topk_ids=topk_ids, out=out, lse=lse, sm_scale=128 ** -0.5)
+    for _ in range(3):
+        I.idx_sparse_attn(p, stream)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(n_ev):
+        if flush is not None:
+            flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        I.idx_sparse_attn(p, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    # algorithmic bytes from the selection
+    ids = topk_ids.cpu().numpy().reshape(R, P, H, -1)
+    lens = w.row_len.cpu().numpy().reshape(R, P).astype(np.int64)
+    slots = w.req_slot.cpu().numpy()
+    tokens = union = selected = 0
+    for r in range(R):
+        if not (0 <= slots[r] < w.n_slot_rows):
+            continue
+        nb = (lens[r] + 127) // 128
+        for h in range(H):
+            best = {}
+            for j in range(P):
+                for b in ids[r, j, h]:
+                    if 0 <= b < nb[j]:
+                        selected += 1
+                        best[int(b)] = max(best.get(int(b), 0), int(min(128, lens[r, j] - 128 * b)))
+            union += len(best)
+            tokens += sum(best.values())
+    rows = R * P * H * G
+    nbytes = tokens * 512 + rows * 256 * 2 + rows * 4 + ids.size * 4
+    us = float(np.mean(ms)) * 1e3
+    gbps = nbytes / (us / 1e6) / 1e9
+    del at, out, lse, p
+    torch.cuda.empty_cache()
+    return {"us": round(us, 2), "us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(ms, [10, 50, 90])],
+            "q_per_kv": G, "kv_heads": H, "query_heads": rows, "selected_blocks": int(selected),
+            "union_blocks": int(union), "kv_bytes": int(tokens * 512), "algorithmic_bytes": int(nbytes),
+            "achieved_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "calls": n_ev}
 
 
 def read_ceiling(w, flush, stream, reps: int = 10) -> dict:

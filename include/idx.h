@@ -194,6 +194,83 @@ int idx_step(const idx_params* p, void* stream);
 /* Message describing the last refusal on the calling thread ("" if none). */
 const char* idx_last_error(void);
 
+/*
+ * Sparse attention over the selected blocks: the step after selection.  The
+ * pages name it ([P1] Accuracy Tests run the sparse kernel's tests beside the
+ * packed scorer; [P3] Validation times the fused verify kernel on MI355X) but
+ * fix none of its shapes; the readings taken:
+ *  - grouped-query attention: kv_heads = the indexer's gqa index heads, index
+ *    head h choosing the blocks of KV head h; q_per_kv query heads per KV
+ *    head; head dimension 128;
+ *  - query head g of KV head h of draft row j attends over the tokens of the
+ *    blocks listed in topk_ids[row j][h][.] (the output of idx_block_topk, or
+ *    any int32 list: ids < 0, ids past the row's blocks and repeats are
+ *    ignored) that the row sees: position 128 b + t < row_len[row j];
+ *  - K and V are paged like the index K (page = block = 128 tokens, the same
+ *    req_slot and block_table), bf16;
+ *  - out = sum_t softmax_t(sm_scale q.k_t) v_t (fp32 accumulation, stored as
+ *    bf16), lse = ln sum_t exp(sm_scale q.k_t) (fp32).  A row that sees no
+ *    selected token (length 0, nothing selected, graph pad) gets out = 0 and
+ *    lse = -inf; a row that sees a token of a selected block whose page id is
+ *    outside [0, n_pages) gets NaN in both.
+ *
+ * Shapes, with P = packed_queries, H = kv_heads, G = q_per_kv, R = n_req:
+ *   q        bf16 [R*P][H][G][128]
+ *   k        bf16 [n_pages][H][128 tokens][128]: token t of page p, head h is
+ *            k[p][h][t]
+ *   v        bf16 [n_pages][H][128 dims][128 tokens]: each page-head's V
+ *            transposed, v[p][h][d][t] (16 consecutive tokens of a dimension
+ *            are one load for the PV product)
+ *   req_slot, block_table, row_len: as idx_params
+ *   topk_ids int32 [R*P][H][topk]
+ *   out      bf16 [R*P][H][G][128];  lse fp32 [R*P][H][G]
+ *   workspace  at least idx_sparse_attn_workspace(p) bytes, 16-byte aligned,
+ *            caller-owned; its contents are scratch (partial results of the
+ *            splits of each (request, KV head)), needing no initialisation.
+ * Limits: P * G <= IDX_ATTN_MAX_ROWS (the rows of one request and KV head
+ * share one 16-row MFMA tile and read each selected K/V page once), P * topk
+ * <= IDX_ATTN_MAX_IDS.  q, k, v, out 16-byte aligned.
+ */
+#define IDX_ATTN_MAX_ROWS 16
+#define IDX_ATTN_MAX_IDS 1024
+#define IDX_ATTN_MAX_SPLITS 64
+
+typedef struct idx_attn_params {
+  int32_t n_req;          /* requests, graph pads included, <= IDX_MAX_REQ  */
+  int32_t n_slot_rows;    /* rows of block_table                             */
+  int32_t packed_queries; /* draft rows per request, >= 1                    */
+  int32_t kv_heads;       /* >= 1 (the indexer's gqa)                        */
+  int32_t q_per_kv;       /* query heads per KV head, >= 1                   */
+  int32_t head_dim;       /* must be 128                                     */
+  int32_t block_size;     /* must be 128                                     */
+  int32_t max_blocks;     /* columns of block_table, 0..IDX_MAX_BLOCKS       */
+  int32_t topk;           /* ids per (draft row, KV head), >= 1              */
+  float sm_scale;         /* softmax scale, finite and > 0                   */
+  int64_t n_pages;        /* pages in the K and V pools, >= 0                */
+  int64_t workspace_bytes;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* req_slot;
+  const int32_t* block_table;
+  const int32_t* row_len;
+  const int32_t* topk_ids;
+  void* out;
+  float* lse;
+  void* workspace;
+} idx_attn_params;
+
+/* Bytes of workspace idx_sparse_attn needs for these sizes on the current
+ * device, or a negative IDX_E_* code when the sizes are refused. */
+int64_t idx_sparse_attn_workspace(const idx_attn_params* p);
+
+/* Sparse attention over the selected blocks (two launches on `stream`: the
+ * splits' partials, then their merge).  Refusals as the other calls, plus
+ * IDX_E_PACK for P * G > IDX_ATTN_MAX_ROWS, IDX_E_TOPK for P * topk >
+ * IDX_ATTN_MAX_IDS, IDX_E_MODE for a bad sm_scale and IDX_E_SHAPE for a
+ * workspace below idx_sparse_attn_workspace(p). */
+int idx_sparse_attn(const idx_attn_params* p, void* stream);
+
 /* Largest n_req * packed_queries * gqa * max_blocks of idx_step_noalloc: the
  * block scores of one step it can hold (16 MiB of fp32 per device). */
 #define IDX_NOALLOC_MAX_SCORES (4 << 20)

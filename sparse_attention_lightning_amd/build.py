@@ -10,7 +10,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libidx.so"
 SOURCES = ["api.hip", "score.hip", "score_rows.hip", "topk.hip", "fp4_store.hip", "noalloc.hip",
-           "probe.hip"]
+           "probe.hip", "attn.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

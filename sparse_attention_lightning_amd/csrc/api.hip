@@ -117,9 +117,96 @@ int launched(hipError_t e, const char* what) {
 // of some other call would otherwise be reported as this call's launch error.
 void clear_stale_error() { (void)hipGetLastError(); }
 
+int check_attn(const idx_attn_params* p) {
+  if (!p) return fail(IDX_E_NULL, "params is NULL");
+  if (p->head_dim != 128 || p->block_size != 128)
+    return fail(IDX_E_SHAPE, "head_dim and block_size must be 128 (got %d, %d)", p->head_dim, p->block_size);
+  if (p->packed_queries < 1 || p->kv_heads < 1 || p->q_per_kv < 1)
+    return fail(IDX_E_SHAPE, "packed_queries, kv_heads and q_per_kv must be >= 1 (got %d, %d, %d)",
+                p->packed_queries, p->kv_heads, p->q_per_kv);
+  if ((int64_t)p->packed_queries * p->q_per_kv > IDX_ATTN_MAX_ROWS)
+    return fail(IDX_E_PACK, "packed_queries * q_per_kv = %lld exceeds %d rows a tile",
+                (long long)p->packed_queries * p->q_per_kv, IDX_ATTN_MAX_ROWS);
+  if (p->n_req < 0 || p->n_slot_rows < 0 || p->n_pages < 0)
+    return fail(IDX_E_SHAPE, "negative count (n_req %d, n_slot_rows %d, n_pages %lld)", p->n_req, p->n_slot_rows,
+                (long long)p->n_pages);
+  if (p->n_req > IDX_MAX_REQ) return fail(IDX_E_SHAPE, "n_req %d exceeds %d", p->n_req, IDX_MAX_REQ);
+  if (p->kv_heads > 1024) return fail(IDX_E_SHAPE, "kv_heads %d exceeds 1024", p->kv_heads);
+  if (p->max_blocks < 0 || p->max_blocks > IDX_MAX_BLOCKS)
+    return fail(IDX_E_SHAPE, "max_blocks %d outside [0, %d]", p->max_blocks, IDX_MAX_BLOCKS);
+  if (p->n_pages > ((int64_t)1 << 40) / p->kv_heads)
+    return fail(IDX_E_SHAPE, "n_pages %lld too large", (long long)p->n_pages);
+  if (p->topk < 1 || (int64_t)p->packed_queries * p->topk > IDX_ATTN_MAX_IDS)
+    return fail(IDX_E_TOPK, "need topk >= 1 and packed_queries * topk <= %d (got %d, %d)", IDX_ATTN_MAX_IDS,
+                p->topk, p->packed_queries);
+  if (!(p->sm_scale > 0.0f && p->sm_scale <= 3.402823466e38f))
+    return fail(IDX_E_MODE, "sm_scale must be finite and > 0 (got %g)", (double)p->sm_scale);
+  return IDX_OK;
+}
+
+int64_t attn_workspace_bytes(const idx_attn_params* p, int* splits) {
+  const int64_t items = (int64_t)p->n_req * p->kv_heads;
+  const int s = idx::attn_splits(items);
+  if (splits) *splits = s;
+  return items * s * 16 * 132 * (int64_t)sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t idx_sparse_attn_workspace(const idx_attn_params* p) {
+  const int rc = check_attn(p);
+  if (rc) return rc;
+  g_err[0] = '\0';
+  return attn_workspace_bytes(p, nullptr);
+}
+
+int idx_sparse_attn(const idx_attn_params* p, void* stream) {
+  const int rc = check_attn(p);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)p->n_req * p->packed_queries;
+  if (rows > 0 && (!p->q || !p->req_slot || !p->row_len || !p->topk_ids || !p->out || !p->lse))
+    return fail(IDX_E_NULL, "q, req_slot, row_len, topk_ids, out and lse are required");
+  if (p->n_pages > 0 && (!p->k || !p->v)) return fail(IDX_E_NULL, "k and v are required");
+  if ((int64_t)p->n_slot_rows * p->max_blocks > 0 && !p->block_table)
+    return fail(IDX_E_NULL, "block_table is required");
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->out) || !aligned16(p->workspace))
+    return fail(IDX_E_ALIGN, "q, k, v, out and workspace must be 16-byte aligned");
+  int splits = 1;
+  const int64_t need = attn_workspace_bytes(p, &splits);
+  if (rows > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(IDX_E_SHAPE, "workspace of %lld bytes is below the %lld needed", (long long)p->workspace_bytes,
+                (long long)need);
+  clear_stale_error();
+  if (rows == 0) {
+    g_err[0] = '\0';
+    return IDX_OK;
+  }
+  idx::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.k = static_cast<const uint8_t*>(p->k);
+  a.v = static_cast<const uint8_t*>(p->v);
+  a.req_slot = p->req_slot;
+  a.block_table = p->block_table;
+  a.row_len = p->row_len;
+  a.topk_ids = p->topk_ids;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.lse = p->lse;
+  a.ws = static_cast<float*>(p->workspace);
+  a.n_pages = p->n_pages;
+  a.n_req = p->n_req;
+  a.n_slot_rows = p->n_slot_rows;
+  a.P = p->packed_queries;
+  a.H = p->kv_heads;
+  a.G = p->q_per_kv;
+  a.max_blocks = p->max_blocks;
+  a.topk = p->topk;
+  a.splits = splits;
+  a.c2 = p->sm_scale * 1.44269504088896341f;
+  return launched(idx::launch_attn(a, (hipStream_t)stream), "sparse attention");
+}
+
 
 const char* idx_last_error(void) { return g_err; }
 

@@ -1,0 +1,349 @@
+// attn.hip -- sparse attention over the selected blocks, for gfx950 (MI355X).
+//
+// The step after selection: each query head of KV head h of a draft row
+// attends over the tokens of the blocks index head h selected for that row,
+// under the row's own length (sglang PR 45451, Accuracy Tests, runs the sparse
+// kernel's tests beside the packed scorer; ROCm/ATOM PR 2745, Validation,
+// times the fused verify kernel on MI355X).
+//
+// Work item = (request, KV head).  Its P draft rows x G query heads (P G <= 16)
+// form one 16-row MFMA tile, and the item walks the union of its P rows'
+// selections, each block carrying the mask of the rows that chose it: a block
+// chosen by several draft rows is read from HBM once for all of them, as the
+// indexer reads each K page once for all rows of a request.  An item's union
+// is cut into `splits` contiguous shares, one workgroup of four waves each; a
+// wave takes every fourth block of its workgroup's share and keeps its own
+// online-softmax state, the four are merged in LDS, and the workgroup writes
+// its partial (max, sum, unnormalized output) per row.  A second kernel merges
+// the splits of an item.
+//
+// Per 32-token unit of a block, per wave:
+//   S^T = K Q^T   MFMA 16x16x32 bf16 with K as the A operand: lane (m, gq)
+//                 loads 16 bytes of token pi_c(m)'s row, so lane (n, gq) ends
+//                 with row n's scores of tokens 8 gq .. 8 gq + 7 (two 16-token
+//                 halves c = 0, 1, pi_c(m) = 8 (m / 4) + 4 c + m % 4);
+//   O^T += V^T P^T  with P^T as the B operand, which is exactly what each lane
+//                 holds (its row's probabilities of those 8 tokens, in bf16),
+//                 and V^T as the A operand, read as 16 contiguous bytes (8
+//                 tokens of one dimension) from the page's transposed V.
+// So K and V go from HBM straight into operand registers, and the rescale of
+// the running output is local to each lane (lane n holds row n's output
+// dimensions 16 dt + 4 gq + i).  Loads go through per-page buffer descriptors;
+// a page outside the pool gets an empty one (reads nothing) and makes every
+// row that sees it NaN.
+#include <atomic>
+
+#include "device.h"
+
+namespace idx {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnBitWords = IDX_MAX_BLOCKS / 32;
+constexpr int kAttnRing = 2;       // 32-token units in registers per wave (64 VGPRs each)
+constexpr int kPartFloats = 132;  // per row of a partial: output [0, 128), max (log2 units), sum, pad
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const uint8_t* pool, int64_t page_head, bool ok) {
+  const uint8_t* base = ok ? pool + page_head * 32768 : pool;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, ok ? 32768 : 0, 0x00020000);
+}
+
+struct AttnUnit {
+  u32x4 k[2][4];  // [half c][k-step s]
+  u32x4 v[8];     // [dim tile dt]
+};
+
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const AttnArgs a) {
+  __shared__ int32_t list_id[IDX_ATTN_MAX_IDS];
+  __shared__ int32_t list_page[IDX_ATTN_MAX_IDS];
+  __shared__ uint16_t list_mask[IDX_ATTN_MAX_IDS];
+  __shared__ union {
+    uint32_t bits[IDX_ATTN_MAX_ROWS][kAttnBitWords];  // each draft row's selected blocks
+    struct {
+      float o[kAttnWaves][16][128];
+      float m[kAttnWaves][16];
+      float l[kAttnWaves][16];
+    } comb;
+  } U;
+  __shared__ uint32_t wave_tot[kAttnWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)__builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.splits;
+  const int item = blockIdx.x / S, split = blockIdx.x - item * S;
+  const int H = a.H, P = a.P, G = a.G, MB = a.max_blocks, K = a.topk;
+  const int r = item / H, h = item - r * H;
+  const int nw = (MB + 31) >> 5;
+  const int slot = a.req_slot[r];
+  const bool pad = slot < 0 || slot >= a.n_slot_rows;
+
+  // 1. each draft row's selected blocks it can see, as bitmaps
+  for (int x = tid; x < P * kAttnBitWords; x += kAttnThreads) U.bits[x / kAttnBitWords][x % kAttnBitWords] = 0u;
+  __syncthreads();
+  if (!pad) {
+    for (int e = tid; e < P * K; e += kAttnThreads) {
+      const int j = e / K;
+      const int nb = blocks_of(clamp_len(a.row_len[r * P + j], MB));
+      const int id = a.topk_ids[((int64_t)(r * P + j) * H + h) * K + (e - j * K)];
+      if (id >= 0 && id < nb) atomicOr(&U.bits[j][id >> 5], 1u << (id & 31));
+    }
+  }
+  __syncthreads();
+  // 2. their union in ascending id order, each block with its row mask
+  uint32_t u = 0;
+  if (tid < nw)
+    for (int j = 0; j < P; ++j) u |= U.bits[j][tid];
+  uint32_t nu;
+  uint32_t pos = block_exclusive_scan<kAttnThreads>((uint32_t)__builtin_popcount(u), wave_tot, &nu);
+  for (uint32_t x = u; x; x &= x - 1) {
+    const int bit = __builtin_ctz(x);
+    uint32_t mask = 0;
+    for (int j = 0; j < P; ++j) mask |= ((U.bits[j][tid] >> bit) & 1u) << j;
+    list_id[pos] = tid * 32 + bit;
+    list_mask[pos] = (uint16_t)mask;
+    ++pos;
+  }
+  __syncthreads();
+  // 3. this workgroup's share of the union and its page ids
+  const int lo = (int)((int64_t)split * nu / S), hi = (int)((int64_t)(split + 1) * nu / S);
+  for (int x = lo + tid; x < hi; x += kAttnThreads) list_page[x] = a.block_table[(int64_t)slot * MB + list_id[x]];
+  __syncthreads();
+
+  // 4. the wave's blocks: lo + wave, lo + wave + 4, ...
+  const int n = lane & 15, gq = lane >> 4;
+  const bool row_ok = n < P * G;
+  const int j = row_ok ? n / G : 0, g = row_ok ? n - j * G : 0;
+  const int64_t qrow = (((int64_t)(r * P + j)) * H + h) * G + g;
+  const int my_len = row_ok && !pad ? clamp_len(a.row_len[r * P + j], MB) : 0;
+  const uint32_t jbit = row_ok ? (1u << j) : 0u;
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + 32 * s + 8 * gq);
+    qf[s] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  const int my_blocks = (hi - lo - wave + kAttnWaves - 1) / kAttnWaves;  // may be <= 0
+  const int n_units = my_blocks > 0 ? 4 * my_blocks : 0;
+
+  float m = -INFINITY, l = 0.f;
+  bool bad = false;
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // token of K row this lane loads for half c: pi_c(n)
+  const int tk0 = 8 * (n >> 2) + (n & 3);
+
+  auto issue = [&](AttnUnit& w, int U_) {
+    const int x = lo + wave + kAttnWaves * (U_ >> 2);
+    const bool exists = U_ < n_units;
+    const int page = exists ? (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]) : -1;
+    const bool ok = exists && page >= 0 && page < a.n_pages;
+    const int64_t ph = (int64_t)(ok ? page : 0) * H + h;
+    const __amdgpu_buffer_rsrc_t rk = attn_rsrc(a.k, ph, ok);
+    const __amdgpu_buffer_rsrc_t rv = attn_rsrc(a.v, ph, ok);
+    const int sub = U_ & 3;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        w.k[c][s] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (32 * sub + tk0 + 4 * c) * 256 + 64 * s + 16 * gq, 0, 0));
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      w.v[dt] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * dt + n) * 256 + (32 * sub + 8 * gq) * 2, 0, 0));
+  };
+
+  auto compute = [&](const AttnUnit& w, int U_) {
+    if (U_ >= n_units) return;
+    const int x = lo + wave + kAttnWaves * (U_ >> 2);
+    const int b = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_id[x]);
+    const uint32_t mask = __builtin_amdgcn_readfirstlane((uint32_t)list_mask[x]);
+    const int page = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]);
+    const bool ok = page >= 0 && page < a.n_pages;
+    const bool sel = (mask & jbit) != 0u;
+    bad |= sel && !ok;
+    f32x4 acc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w.k[c][s]), qf[s], acc[c], 0, 0, 0);
+    }
+    // this lane: row n, tokens 8 gq + 4 c + i of the unit
+    const int pos0 = 128 * b + 32 * (U_ & 3) + 8 * gq;
+    float xv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = sel && ok && pos0 + 4 * c + i < my_len;
+        xv[4 * c + i] = vis ? acc[c][i] * a.c2 : -INFINITY;
+        mt = fmaxf(mt, xv[4 * c + i]);
+      }
+    mt = fmaxf(mt, x16(mt, gq));
+    mt = fmaxf(mt, x32(mt, gq));
+    const float mn = fmaxf(m, mt);
+    const bool live = mn != -INFINITY;  // some token of this row seen so far
+    const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+    float sum = 0.f;
+    bf16x8_t pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = live ? __builtin_amdgcn_exp2f(xv[e] - mn) : 0.f;
+      sum += pe;
+      pb[e] = (__bf16)pe;
+    }
+    l = l * alpha + sum;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      o[dt] *= alpha;
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w.v[dt]), pb, o[dt], 0, 0, 0);
+    }
+  };
+
+  {
+    AttnUnit ring[kAttnRing];
+#pragma unroll
+    for (int k = 0; k < kAttnRing - 1; ++k) issue(ring[k], k);
+    for (int U0 = 0; U0 < n_units; U0 += kAttnRing) {
+#pragma unroll
+      for (int k = 0; k < kAttnRing; ++k) {
+        issue(ring[(k + kAttnRing - 1) % kAttnRing], U0 + k + kAttnRing - 1);
+        compute(ring[k], U0 + k);
+      }
+    }
+  }
+
+  // 5. merge the four waves in LDS (the bitmaps are dead), write the partial
+  l += x16(l, gq);
+  l += x32(l, gq);
+  __syncthreads();
+  if (gq == 0) {
+    U.comb.m[wave][n] = m;
+    U.comb.l[wave][n] = bad ? __builtin_nanf("") : l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<f32x4*>(&U.comb.o[wave][n][16 * dt + 4 * gq]) = o[dt];
+  __syncthreads();
+  {
+    const int row = tid >> 4, c8 = tid & 15;
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
+      M = fmaxf(M, U.comb.m[w2][row]);
+      nan |= U.comb.l[w2][row] != U.comb.l[w2][row];
+    }
+    float L = 0.f, acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w2 = 0; w2 < kAttnWaves; ++w2) {
+      const float mw = U.comb.m[w2][row];
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += f * U.comb.l[w2][row];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc8[d] += f * U.comb.o[w2][row][8 * c8 + d];
+    }
+    if (nan) L = __builtin_nanf("");
+    float* part = a.ws + ((int64_t)item * S + split) * 16 * kPartFloats + row * kPartFloats;
+    if (c8 == 0) {
+      part[128] = M;
+      part[129] = L;
+    }
+    *reinterpret_cast<f32x4*>(part + 8 * c8) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
+    *reinterpret_cast<f32x4*>(part + 8 * c8 + 4) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
+  }
+}
+
+// Merge the splits of each item: row n = tid / 16 writes output dimensions
+// 8 (tid % 16) .. + 8 (and its lse).
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnArgs a) {
+  const int item = blockIdx.x, tid = threadIdx.x;
+  const int row = tid >> 4, c8 = tid & 15;
+  const int H = a.H, P = a.P, G = a.G, S = a.splits;
+  if (row >= P * G) return;
+  const int r = item / H, h = item - r * H;
+  const int j = row / G, g = row - j * G;
+  const float* part = a.ws + (int64_t)item * S * 16 * kPartFloats + row * kPartFloats;
+  float M = -INFINITY;
+  bool nan = false;
+  for (int s = 0; s < S; ++s) {
+    const float* ps = part + (int64_t)s * 16 * kPartFloats;
+    M = fmaxf(M, ps[128]);
+    nan |= ps[129] != ps[129];
+  }
+  float L = 0.f, acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float* ps = part + (int64_t)s * 16 * kPartFloats;
+      const float f = (ps[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[128] - M);
+      L += f * ps[129];
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(ps + 8 * c8);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(ps + 8 * c8 + 4);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc8[d] += f * v0[d];
+        acc8[4 + d] += f * v1[d];
+      }
+    }
+  }
+  const int64_t orow = (((int64_t)(r * P + j)) * H + h) * G + g;
+  bf16x8_t ob;
+  float lse;
+  if (nan) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)__builtin_nanf("");
+    lse = __builtin_nanf("");
+  } else if (M == -INFINITY) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)0.f;
+    lse = -INFINITY;
+  } else {
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)(acc8[d] * inv);
+    lse = (M + __builtin_amdgcn_logf(L)) * 0.693147180559945309f;
+  }
+  *reinterpret_cast<bf16x8_t*>(a.out + orow * 128 + 8 * c8) = ob;
+  if (c8 == 0) a.lse[orow] = lse;
+}
+
+namespace {
+int attn_resident_workgroups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (const int nwg = cache[dev].load(std::memory_order_relaxed); nwg > 0) return nwg;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(attn_partial_kernel),
+                                                   kAttnThreads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+  return cus * per_cu;
+}
+}  // namespace
+
+int attn_splits(int64_t items) {
+  if (items <= 0) return 1;
+  const int64_t s = (attn_resident_workgroups() + items - 1) / items;
+  return (int)(s < 1 ? 1 : (s > IDX_ATTN_MAX_SPLITS ? IDX_ATTN_MAX_SPLITS : s));
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.n_req * a.H;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0, stream, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)items), dim3(kAttnThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace idx

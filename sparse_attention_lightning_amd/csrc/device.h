@@ -37,6 +37,27 @@ struct StepArgs {
   float sm_scale;      // lse only
 };
 
+// Sparse attention over the selected blocks (one launch of partials, one of
+// the merge).
+struct AttnArgs {
+  const uint16_t* q;          // bf16 [R*P][H][G][128]
+  const uint8_t* k;           // bf16 [n_pages][H][128 tokens][128]
+  const uint8_t* v;           // bf16 [n_pages][H][128 dims][128 tokens]
+  const int32_t* req_slot;
+  const int32_t* block_table;
+  const int32_t* row_len;
+  const int32_t* topk_ids;    // [R*P][H][topk]
+  uint16_t* out;              // bf16 [R*P][H][G][128]
+  float* lse;                 // [R*P][H][G]
+  float* ws;                  // partials: [R*H][splits][16 rows][132]
+  int64_t n_pages;
+  int32_t n_req, n_slot_rows, P, H, G, max_blocks, topk, splits;
+  float c2;                   // sm_scale * log2(e)
+};
+// Workgroups of the partial kernel per (request, KV head) item.
+int attn_splits(int64_t items);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
 hipError_t launch_score(const StepArgs& a, hipStream_t stream);       // any rows per request
 hipError_t launch_score_rows(const StepArgs& a, hipStream_t stream);  // more than 16 rows per request
 hipError_t launch_topk(const StepArgs& a, hipStream_t stream);
@@ -83,6 +104,19 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_mov<0x124>(x);  // row_ror:4
   x += dpp_mov<0x128>(x);  // row_ror:8
   return x;
+}
+
+// The value lane l ^ 16 (x16) or l ^ 32 (x32) holds, for a lane of lane group
+// g = l / 16, through the gfx950 lane swaps (VALU, no LDS round trip): a swap
+// of v with itself leaves the partner row's copy in the second result on
+// lanes 0-15 and 32-47 (x16) or 0-31 (x32), and in the first on the others.
+__device__ __forceinline__ float x16(float v, int g) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((g & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float x32(float v, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((g & 2) ? r[0] : r[1]);
 }
 
 // Exclusive prefix sum over a workgroup of THREADS threads (all must call);

@@ -232,19 +232,6 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
-// The value lane l ^ 16 (x16) or l ^ 32 (x32) holds, through the gfx950 lane
-// swaps (VALU, no LDS round trip): a swap of v with itself leaves the partner
-// row's copy in the second result on lanes 0-15 and 32-47 (x16) or 0-31
-// (x32), and in the first on the others.
-__device__ __forceinline__ float x16(float v, int g) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((g & 1) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float x32(float v, int g) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((g & 2) ? r[0] : r[1]);
-}
-
 // Reduce the values of tiles Q .. Q+3 over the four lane groups (lanes n,
 // n + 16, n + 32, n + 48) so that lane group g ends with tile Q + g's: two
 // exchange steps, each lane keeping half of what it holds and receiving the

@@ -26,8 +26,11 @@ IDX_MAX_REQ = 8192
 IDX_MAX_REQ_ROWS = 65536
 IDX_MAX_ROWS = 1 << 24
 IDX_NOALLOC_MAX_SCORES = 4 << 20
+IDX_ATTN_MAX_ROWS = 16
+IDX_ATTN_MAX_IDS = 1024
+IDX_ATTN_MAX_SPLITS = 64
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error",
-           "idx_step_noalloc", "idx_probe_read")
+           "idx_step_noalloc", "idx_probe_read", "idx_sparse_attn", "idx_sparse_attn_workspace")
 
 
 class IdxError(RuntimeError):
@@ -48,6 +51,19 @@ class IdxParams(C.Structure):
         ("q", C.c_void_p), ("k", C.c_void_p), ("k_scale", C.c_void_p),
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
         ("block_scores", C.c_void_p), ("topk_ids", C.c_void_p), ("topk_scores", C.c_void_p),
+    ]
+
+
+class IdxAttnParams(C.Structure):
+    """Mirror of ``idx_attn_params``."""
+    _fields_ = [
+        ("n_req", C.c_int32), ("n_slot_rows", C.c_int32), ("packed_queries", C.c_int32),
+        ("kv_heads", C.c_int32), ("q_per_kv", C.c_int32), ("head_dim", C.c_int32),
+        ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
+        ("sm_scale", C.c_float), ("n_pages", C.c_int64), ("workspace_bytes", C.c_int64),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+        ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
+        ("topk_ids", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p), ("workspace", C.c_void_p),
     ]
 
 
@@ -75,6 +91,10 @@ def load(path: Path | str | None = None) -> C.CDLL:
     lib.idx_probe_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int32, C.c_int32,
                                    C.c_void_p, C.c_int32, C.c_void_p]
     lib.idx_probe_read.restype = C.c_int
+    lib.idx_sparse_attn.argtypes = [C.POINTER(IdxAttnParams), C.c_void_p]
+    lib.idx_sparse_attn.restype = C.c_int
+    lib.idx_sparse_attn_workspace.argtypes = [C.POINTER(IdxAttnParams)]
+    lib.idx_sparse_attn_workspace.restype = C.c_int64
     if path is None:
         _lib = lib
     return lib
@@ -253,3 +273,64 @@ def idx_fp4_store(staging: torch.Tensor, slot_mapping: torch.Tensor, payload: to
                            slot_mapping.data_ptr(), payload.data_ptr(), scales.data_ptr(),
                            n_slots, _stream(stream))
     _check(rc, lib)
+
+
+def make_attn_params(*, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, req_slot: torch.Tensor,
+                     block_table: torch.Tensor, row_len: torch.Tensor, topk_ids: torch.Tensor,
+                     out: torch.Tensor, lse: torch.Tensor, sm_scale: float,
+                     workspace: torch.Tensor | None = None) -> IdxAttnParams:
+    """Parameter block of the sparse attention from tensors: q [R*P, H, G,
+    128] bf16, k [n_pages, H, 128, 128] bf16, v [n_pages, H, 128 dims, 128
+    tokens] bf16, topk_ids [R*P*H, topk] (or [R*P, H, topk]) int32, out like
+    q, lse [R*P, H, G] fp32.  Without ``workspace`` one of the size the
+    library asks for is allocated here (kept alive by the returned object)."""
+    if q.dim() != 4 or q.shape[-1] != 128:
+        raise ValueError("q must be [R*P, H, G, 128]")
+    if k.dim() != 4 or k.shape[2:] != (128, 128) or v.shape != k.shape:
+        raise ValueError("k and v must be [n_pages, H, 128, 128]")
+    p = IdxAttnParams()
+    n_req = req_slot.numel()
+    rows, H, G = q.shape[0], q.shape[1], q.shape[2]
+    if n_req == 0 or rows % n_req:
+        raise ValueError("q rows must be n_req * packed_queries")
+    P = rows // n_req
+    if k.shape[1] != H:
+        raise ValueError("k and q disagree on kv_heads")
+    if row_len.numel() != rows:
+        raise ValueError("row_len must have n_req * packed_queries entries")
+    topk = topk_ids.numel() // max(1, rows * H)
+    if topk_ids.numel() != rows * H * topk or out.shape != q.shape or lse.shape != q.shape[:3]:
+        raise ValueError("topk_ids, out or lse has the wrong shape")
+    p.n_req, p.packed_queries, p.kv_heads, p.q_per_kv = n_req, P, H, G
+    p.head_dim = p.block_size = 128
+    p.n_slot_rows, p.max_blocks = block_table.shape[0], block_table.shape[1]
+    p.topk, p.sm_scale, p.n_pages = topk, sm_scale, k.shape[0]
+    p.q = _dev(q, "q", (torch.bfloat16,))
+    p.k = _dev(k, "k", (torch.bfloat16,))
+    p.v = _dev(v, "v", (torch.bfloat16,))
+    p.req_slot = _dev(req_slot, "req_slot", (torch.int32,))
+    p.block_table = _dev(block_table, "block_table", (torch.int32,))
+    p.row_len = _dev(row_len, "row_len", (torch.int32,))
+    p.topk_ids = _dev(topk_ids, "topk_ids", (torch.int32,))
+    p.out = _dev(out, "out", (torch.bfloat16,))
+    p.lse = _dev(lse, "lse", (torch.float32,))
+    if workspace is None:
+        need = idx_sparse_attn_workspace(p)
+        workspace = torch.empty(max(1, (need + 15) // 16) * 4, dtype=torch.float32, device=q.device)
+    p.workspace = _dev(workspace, "workspace", (torch.float32, torch.uint8))
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    p._keep = (q, k, v, req_slot, block_table, row_len, topk_ids, out, lse, workspace)
+    return p
+
+
+def idx_sparse_attn_workspace(p: IdxAttnParams) -> int:
+    lib = load()
+    n = lib.idx_sparse_attn_workspace(C.byref(p))
+    if n < 0:
+        raise IdxError(int(n), lib.idx_last_error().decode())
+    return int(n)
+
+
+def idx_sparse_attn(p: IdxAttnParams, stream=None) -> None:
+    lib = load()
+    _check(lib.idx_sparse_attn(C.byref(p), _stream(stream)), lib)

@@ -24,7 +24,7 @@ def lib():
 
 def declared_functions() -> list[str]:
     text = (ROOT / "include" / "idx.h").read_text()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(idx_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\s*\*)\s*(idx_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -116,10 +116,80 @@ def test_params_layout_matches_header(tmp_path):
     assert got[1:] == [getattr(I.IdxParams, n).offset for n in names]
 
 
+def test_attn_params_layout_matches_header(tmp_path):
+    names = [f for f, _ in I.IdxAttnParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "idx.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(idx_attn_params));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(idx_attn_params, {n}));\n' for n in names)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", f"-I{ROOT / 'include'}", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == C.sizeof(I.IdxAttnParams)
+    assert got[1:] == [getattr(I.IdxAttnParams, n).offset for n in names]
+
+
+def good_attn_params() -> I.IdxAttnParams:
+    p = I.IdxAttnParams()
+    p.n_req, p.n_slot_rows, p.packed_queries, p.kv_heads, p.q_per_kv = 2, 4, 4, 2, 4
+    p.head_dim = p.block_size = 128
+    p.max_blocks, p.topk, p.sm_scale, p.n_pages = 16, 8, 0.125, 64
+    p.workspace_bytes = 1 << 30
+    for i, f in enumerate(["q", "k", "v", "req_slot", "block_table", "row_len", "topk_ids", "out", "lse",
+                           "workspace"]):
+        setattr(p, f, 0x100000 * (i + 1))
+    return p
+
+
+ATTN_REFUSALS = [
+    ("head_dim", 64, I.IDX_E_SHAPE),
+    ("block_size", 256, I.IDX_E_SHAPE),
+    ("packed_queries", 0, I.IDX_E_SHAPE),
+    ("kv_heads", 0, I.IDX_E_SHAPE),
+    ("q_per_kv", 0, I.IDX_E_SHAPE),
+    ("q_per_kv", 5, I.IDX_E_PACK),           # 4 * 5 rows > 16
+    ("n_req", -1, I.IDX_E_SHAPE),
+    ("n_req", I.IDX_MAX_REQ + 1, I.IDX_E_SHAPE),
+    ("max_blocks", I.IDX_MAX_BLOCKS + 1, I.IDX_E_SHAPE),
+    ("n_pages", -1, I.IDX_E_SHAPE),
+    ("topk", 0, I.IDX_E_TOPK),
+    ("topk", I.IDX_ATTN_MAX_IDS // 4 + 1, I.IDX_E_TOPK),
+    ("sm_scale", 0.0, I.IDX_E_MODE),
+    ("sm_scale", float("inf"), I.IDX_E_MODE),
+    ("sm_scale", float("nan"), I.IDX_E_MODE),
+    ("q", None, I.IDX_E_NULL),
+    ("v", None, I.IDX_E_NULL),
+    ("topk_ids", None, I.IDX_E_NULL),
+    ("lse", None, I.IDX_E_NULL),
+    ("block_table", None, I.IDX_E_NULL),
+    ("v", 0x100008, I.IDX_E_ALIGN),
+    ("workspace", 0x100004, I.IDX_E_ALIGN),
+    ("workspace_bytes", 16, I.IDX_E_SHAPE),
+]
+
+
+@pytest.mark.parametrize("field,value,code", ATTN_REFUSALS, ids=[f"{f}={v}" for f, v, _ in ATTN_REFUSALS])
+def test_attn_refusals(lib, field, value, code):
+    p = good_attn_params()
+    setattr(p, field, value)
+    assert lib.idx_sparse_attn(C.byref(p), None) == code, lib.idx_last_error().decode()
+    assert lib.idx_last_error().decode() != ""
+
+
+def test_attn_workspace_query(lib):
+    p = good_attn_params()
+    assert lib.idx_sparse_attn_workspace(C.byref(p)) > 0
+    p.q_per_kv = 5
+    assert lib.idx_sparse_attn_workspace(C.byref(p)) == I.IDX_E_PACK
+    assert lib.idx_sparse_attn_workspace(None) == I.IDX_E_NULL
+
+
 def test_null_params(lib):
     assert lib.idx_step(None, None) == I.IDX_E_NULL
     assert lib.idx_score_packed(None, None) == I.IDX_E_NULL
     assert lib.idx_block_topk(None, None) == I.IDX_E_NULL
+    assert lib.idx_sparse_attn(None, None) == I.IDX_E_NULL
 
 
 def test_entry_specific_requirements(lib):
@@ -201,6 +271,9 @@ def test_binding_constants_match_header():
         assert m and int(m.group(1)) == getattr(I, name), name
     m = re.search(r"#define\s+IDX_MAX_ROWS\s+\(1 << (\d+)\)", text)
     assert m and (1 << int(m.group(1))) == I.IDX_MAX_ROWS
+    for name in ("IDX_ATTN_MAX_ROWS", "IDX_ATTN_MAX_IDS", "IDX_ATTN_MAX_SPLITS"):
+        m = re.search(rf"#define\s+{name}\s+(\d+)", text)
+        assert m and int(m.group(1)) == getattr(I, name), name
     m = re.search(r"#define\s+IDX_NOALLOC_MAX_SCORES\s+\((\d+) << (\d+)\)", text)
     assert m and (int(m.group(1)) << int(m.group(2))) == I.IDX_NOALLOC_MAX_SCORES
     enums = dict((k, int(v)) for k, v in re.findall(r"(IDX_\w+)\s*=\s*(-?\d+)", text))

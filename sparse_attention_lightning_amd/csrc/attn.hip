@@ -11,9 +11,9 @@
 // selections, each block carrying the mask of the rows that chose it: a block
 // chosen by several draft rows is read from HBM once for all of them, as the
 // indexer reads each K page once for all rows of a request.  An item's union
-// is cut into `splits` contiguous shares, one workgroup of four waves each; a
-// wave takes every fourth block of its workgroup's share and keeps its own
-// online-softmax state, the four are merged in LDS, and the workgroup writes
+// is cut into `splits` contiguous shares, one workgroup of four waves each; the
+// waves take the share's blocks one at a time from an LDS counter and each
+// keeps its own online-softmax state, the four are merged in LDS, and the workgroup writes
 // its partial (max, sum, unnormalized output) per row.  A second kernel merges
 // the splits of an item.
 //
@@ -37,10 +37,18 @@
 
 namespace idx {
 
+// Tuning knobs (compile-time; neither changes what is computed).
+#ifndef IDX_ATTN_RING
+#define IDX_ATTN_RING 3      // 32-token units in registers per wave (64 registers each)
+#endif
+#ifndef IDX_ATTN_MIN_WGS
+#define IDX_ATTN_MIN_WGS 1   // workgroups a CU must hold at once (sets each wave's register budget)
+#endif
+
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnBitWords = IDX_MAX_BLOCKS / 32;
-constexpr int kAttnRing = 2;       // 32-token units in registers per wave (64 VGPRs each)
+constexpr int kAttnRing = IDX_ATTN_RING;
 constexpr int kPartFloats = 132;  // per row of a partial: output [0, 128), max (log2 units), sum, pad
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -55,7 +63,7 @@ struct AttnUnit {
   u32x4 v[8];     // [dim tile dt]
 };
 
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_kernel(const AttnArgs a) {
   __shared__ int32_t list_id[IDX_ATTN_MAX_IDS];
   __shared__ int32_t list_page[IDX_ATTN_MAX_IDS];
   __shared__ uint16_t list_mask[IDX_ATTN_MAX_IDS];
@@ -68,6 +76,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const Att
     } comb;
   } U;
   __shared__ uint32_t wave_tot[kAttnWaves];
+  __shared__ uint32_t next_block;  // blocks of the share handed out to the waves
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)__builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,9 +118,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const Att
   // 3. this workgroup's share of the union and its page ids
   const int lo = (int)((int64_t)split * nu / S), hi = (int)((int64_t)(split + 1) * nu / S);
   for (int x = lo + tid; x < hi; x += kAttnThreads) list_page[x] = a.block_table[(int64_t)slot * MB + list_id[x]];
+  if (tid == 0) next_block = 0;
   __syncthreads();
 
-  // 4. the wave's blocks: lo + wave, lo + wave + 4, ...
+  // 4. the share's blocks, one at a time to whichever wave asks next (the
+  // waves of a SIMD are not served equally by the memory system, so fixed
+  // per-wave shares would end on the slower one)
   const int n = lane & 15, gq = lane >> 4;
   const bool row_ok = n < P * G;
   const int j = row_ok ? n / G : 0, g = row_ok ? n - j * G : 0;
@@ -125,8 +137,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const Att
     if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + 32 * s + 8 * gq);
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
   }
-  const int my_blocks = (hi - lo - wave + kAttnWaves - 1) / kAttnWaves;  // may be <= 0
-  const int n_units = my_blocks > 0 ? 4 * my_blocks : 0;
+  const uint32_t n_share = (uint32_t)(hi - lo);
+  int vm_x = -1;      // lane bi % 64 holds the share position of the wave's block bi (-1: none)
+  bool done = false;  // the share is exhausted
+  int last = -1;      // the wave's last block that holds a block
 
   float m = -INFINITY, l = 0.f;
   bool bad = false;
@@ -137,8 +151,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const Att
   const int tk0 = 8 * (n >> 2) + (n & 3);
 
   auto issue = [&](AttnUnit& w, int U_) {
-    const int x = lo + wave + kAttnWaves * (U_ >> 2);
-    const bool exists = U_ < n_units;
+    const int bi = U_ >> 2;
+    if ((U_ & 3) == 0) {  // a new block: the next one of the share
+      int xn = -1;
+      if (!done) {
+        uint32_t k = 0;
+        if (lane == 0) k = atomicAdd(&next_block, 1u);
+        k = __builtin_amdgcn_readfirstlane(k);
+        if (k < n_share) {
+          xn = lo + (int)k;
+          last = bi;
+        } else {
+          done = true;
+        }
+      }
+      if (lane == (bi & 63)) vm_x = xn;
+    }
+    const int x = __builtin_amdgcn_readlane(vm_x, bi & 63);
+    const bool exists = x >= 0;
     const int page = exists ? (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]) : -1;
     const bool ok = exists && page >= 0 && page < a.n_pages;
     const int64_t ph = (int64_t)(ok ? page : 0) * H + h;
@@ -158,8 +188,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const Att
   };
 
   auto compute = [&](const AttnUnit& w, int U_) {
-    if (U_ >= n_units) return;
-    const int x = lo + wave + kAttnWaves * (U_ >> 2);
+    const int x = __builtin_amdgcn_readlane(vm_x, (U_ >> 2) & 63);
+    if (x < 0) return;
     const int b = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_id[x]);
     const uint32_t mask = __builtin_amdgcn_readfirstlane((uint32_t)list_mask[x]);
     const int page = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]);
@@ -212,12 +242,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(const Att
     AttnUnit ring[kAttnRing];
 #pragma unroll
     for (int k = 0; k < kAttnRing - 1; ++k) issue(ring[k], k);
-    for (int U0 = 0; U0 < n_units; U0 += kAttnRing) {
+    for (int U0 = 0;; U0 += kAttnRing) {
 #pragma unroll
       for (int k = 0; k < kAttnRing; ++k) {
         issue(ring[(k + kAttnRing - 1) % kAttnRing], U0 + k + kAttnRing - 1);
         compute(ring[k], U0 + k);
       }
+      if (done && 4 * (last + 1) <= U0 + kAttnRing) break;  // every unit of a held block is computed
     }
   }
 

@@ -46,8 +46,13 @@ namespace idx {
 #ifndef IDX_SCORE_NT_OUT
 #define IDX_SCORE_NT_OUT 0       // 1: non-temporal block-score stores
 #endif
-constexpr int kWaves = 8;
+#ifndef IDX_SCORE_WAVES
+#define IDX_SCORE_WAVES 8        // waves of a workgroup (one workgroup a CU)
+#endif
+constexpr int kWaves = IDX_SCORE_WAVES;
 constexpr int kThreads = kWaves * 64;
+constexpr int kPagesPerThread = (768 + kThreads - 1) / kThreads;  // round pages a thread stages
+constexpr int kQPiecesPerThread = (8 * 16 * 16) / kThreads;       // query-tile pieces a thread loads
 constexpr int kRoundPages = 768;   // pages a workgroup stages at once
 constexpr int kRoundReqs = 8;      // requests a round may touch
 constexpr int kQStride = 136;      // 16-bit values per query row in LDS (272 B: rows change banks)
@@ -79,7 +84,9 @@ static_assert(offsetof(RoundLds, q) % 16 == 0 && offsetof(RoundLds, req) % 16 ==
 // with the per-request arrays for the largest request count, one workgroup
 // still fits in the 160 KB of LDS of a CU
 static_assert(sizeof(RoundLds) + 64 + (2 * IDX_MAX_REQ + 1) * 4 <= 160 * 1024, "LDS budget");
-static_assert(kRoundPages <= 2 * kThreads && kRoundPages <= 1024 && kRoundReqs <= 8, "round page fields");
+static_assert(kRoundPages <= kPagesPerThread * kThreads && kRoundPages <= 1024 && kRoundReqs <= 8,
+              "round page fields");
+static_assert(kQPiecesPerThread * kThreads == kRoundReqs * kTileRows * 16, "query pieces");
 static_assert(IDX_SCORE_SORT_BUCKETS <= kTileRows * kRoundPages, "the bucket histogram fits the stage");
 
 
@@ -105,9 +112,9 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     const int j = tid / kTileRows, i = tid % kTileRows;
     L.req[j].len[i] = (i < rows) ? clamp_len(a.row_len[(r0 + j) * P + i / H], MB) : 0;
   }
-  int pk[2], jk[2];
+  int pk[kPagesPerThread], jk[kPagesPerThread];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < kPagesPerThread; ++m) {
     const int k = tid + kThreads * m;
     pk[m] = -1;
     jk[m] = 0;
@@ -122,7 +129,9 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
       L.ridx[k] = (uint8_t)j;
     }
   }
-  int pos[2] = {tid, tid + kThreads};  // hand-out position of each page
+  int pos[kPagesPerThread];  // hand-out position of each page
+#pragma unroll
+  for (int m = 0; m < kPagesPerThread; ++m) pos[m] = tid + kThreads * m;
 #if IDX_SCORE_SORT_BUCKETS > 0
   if (np >= IDX_SCORE_SORT_MIN) {
     // by page id: a counting sort into NB equal buckets of the pool, so that
@@ -132,10 +141,11 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     uint32_t* hist = reinterpret_cast<uint32_t*>(&L.stage[0][0]);
     for (int b = tid; b < NB; b += kThreads) hist[b] = 0;
     __syncthreads();
-    int bk[2];
-    uint32_t rank[2] = {0, 0};
+    int bk[kPagesPerThread];
+    uint32_t rank[kPagesPerThread];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < kPagesPerThread; ++m) {
+      rank[m] = 0;
       const int k = tid + kThreads * m;
       const int pid = pk[m];
       bk[m] = (pid >= 0 && pid < a.n_pages) ? (int)((uint64_t)pid * NB / (uint64_t)a.n_pages) : NB - 1;
@@ -158,21 +168,21 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 2; ++m) pos[m] = (int)(hist[bk[m]] + rank[m]);
+    for (int m = 0; m < kPagesPerThread; ++m) pos[m] = (int)(hist[bk[m]] + rank[m]);
   }
 #endif
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < kPagesPerThread; ++m) {
     const int k = tid + kThreads * m;
     if (k < np) {
       L.pid[pos[m]] = pk[m];
       L.sk[pos[m]] = (uint16_t)(k | (jk[m] << 10));
     }
   }
-  // query tiles: piece e = (request j, row, group of 8 values); 4 per thread
-  u32x4 pc[4];
+  // query tiles: piece e = (request j, row, group of 8 values); kQPiecesPerThread per thread
+  u32x4 pc[kQPiecesPerThread];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kQPiecesPerThread; ++i) {
     const int e = tid + kThreads * i, j = e >> 8, row = (e >> 4) & 15, col = (e & 15) * 8;
     pc[i] = u32x4{0u, 0u, 0u, 0u};
     if (j < nreq && row < rows)
@@ -182,7 +192,7 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
   if constexpr (FMT == IDX_K_NVFP4) {
     __syncthreads();  // amax cleared
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kQPiecesPerThread; ++i) {
       const int e = tid + kThreads * i, j = e >> 8;
       float m = 0.f;
 #pragma unroll
@@ -192,7 +202,7 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kQPiecesPerThread; ++i) {
       const int e = tid + kThreads * i, j = e >> 8;
       if (j >= nreq) continue;
       const float amax = __uint_as_float(L.amax[j]);
@@ -212,7 +222,7 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kQPiecesPerThread; ++i) {
     const int e = tid + kThreads * i, j = e >> 8, row = (e >> 4) & 15, col = (e & 15) * 8;
     if (j < nreq) *reinterpret_cast<u32x4*>(&L.q[j][row][col]) = pc[i];
   }

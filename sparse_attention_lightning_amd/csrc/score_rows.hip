@@ -31,9 +31,9 @@
 // p + 1 tokens, items above the diagonal exit at once) and the C chunks of a
 // row group split that extent evenly, so the chunks of a row group are equal
 // however long its rows are.  Each XCD takes a contiguous run of items, so
-// the workgroups that read the same K pages share an L2.  Each lane writes its
-// row's score of each page straight out; the L2 assembles each row's lines
-// over consecutive pages.
+// the workgroups that read the same K pages share an L2.  Each lane keeps its
+// row's scores of four consecutive pages and writes them as one 16-byte store
+// (max mode; lse writes each page's score at once).
 #include <algorithm>
 #include <atomic>
 #include <climits>
@@ -57,6 +57,18 @@ namespace idx {
                               // lse: after the page (its half-page accumulators leave no registers)
 #endif
 
+// Block scores a lane keeps before one store (4: an aligned 16-byte store; 1:
+// each alone).  Per-value stores leave each 128-byte output line to be
+// assembled over 32 pages, and the streaming K evicts the partly written
+// lines: 10.4x the block-score bytes reach HBM on the prefill workload, 3.3x
+// with 4 values a store, 2.0x with 8.  4 costs nothing in max mode; lse mode
+// has no registers to spare (4 measured 3 % slower), 8 cost max mode 4.5 %.
+#ifndef IDX_ROWS_OUT_VEC_MAX
+#define IDX_ROWS_OUT_VEC_MAX 4
+#endif
+#ifndef IDX_ROWS_OUT_VEC_LSE
+#define IDX_ROWS_OUT_VEC_LSE 1
+#endif
 #ifndef IDX_ROWS_ITEMS
 #define IDX_ROWS_ITEMS 1      // items per resident workgroup the block chunks aim at
 #endif
@@ -349,6 +361,14 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
     }
   }
   const float c2 = (MODE == IDX_SCORE_LSE) ? a.sm_scale * 1.44269504088896341f : 0.f;
+  // the lane's row's scores of the current group of IDX_ROWS_OUT_VEC blocks
+  // (block b in slot b % IDX_ROWS_OUT_VEC), written as one store when the
+  // group is complete; a group cut by the item's ends goes out value by value
+  constexpr int kOutVec = (MODE == IDX_SCORE_MAX) ? IDX_ROWS_OUT_VEC_MAX : IDX_ROWS_OUT_VEC_LSE;
+  static_assert(kOutVec == 1 || kOutVec % 4 == 0, "whole 16-byte stores");
+  float obuf[kWaveTiles / 4][kOutVec];
+  const bool vec_rows = kOutVec > 1 && (MB % kOutVec) == 0 &&
+                        (reinterpret_cast<uintptr_t>(a.block_scores) & (4 * kOutVec - 1)) == 0;
 
   // page j of the item: its id (-1 past the item) and descriptors
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k);
@@ -433,7 +453,33 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
         o = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(s)) * 0.693147180559945309f;
       if (!ok) o = (b * kBlock < my_len[q]) ? __builtin_nanf("") : -INFINITY;
       const int row = wrow0 + kTileRows * (4 * q + g) + n;
-      if (row < PH) a.block_scores[((int64_t)r * PH + row) * MB + b] = o;
+      float* dst = a.block_scores + ((int64_t)r * PH + row) * MB;
+      if constexpr (kOutVec == 1) {
+        if (row < PH) dst[b] = o;
+      } else {
+        constexpr int V = kOutVec;
+        const int sl = b % V;
+#pragma unroll
+        for (int e = 0; e < V; ++e) obuf[q][e] = (sl == e) ? o : obuf[q][e];
+        if (sl == V - 1 || k == nblk - 1) {  // the group is complete, or the item ends
+          const int g0 = b - sl;
+          if (row < PH) {
+            if (vec_rows && sl == V - 1 && g0 >= b0) {
+              if constexpr (V == 4) {
+                *reinterpret_cast<f32x4*>(dst + g0) = f32x4{obuf[q][0], obuf[q][1], obuf[q][2], obuf[q][3]};
+              } else {
+#pragma unroll
+                for (int e = 0; e < V; e += 4)
+                  *reinterpret_cast<f32x4*>(dst + g0 + e) = f32x4{obuf[q][e], obuf[q][e + 1], obuf[q][e + 2], obuf[q][e + 3]};
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < V; ++e)
+                if (e <= sl && g0 + e >= b0) dst[g0 + e] = obuf[q][e];
+            }
+          }
+        }
+      }
     };
     out(std::integral_constant<int, 0>{});
     if constexpr (kWaveTiles > 4) out(std::integral_constant<int, 1>{});

@@ -41,7 +41,7 @@ namespace idx {
 #define IDX_SCORE_SORT_BUCKETS 256  // page-id buckets of the pool for the hand-out order (0: round order)
 #endif
 #ifndef IDX_SCORE_SORT_MIN
-#define IDX_SCORE_SORT_MIN 64       // rounds with fewer pages keep round order
+#define IDX_SCORE_SORT_MIN 32       // rounds with fewer pages keep round order
 #endif
 #ifndef IDX_SCORE_NT_OUT
 #define IDX_SCORE_NT_OUT 0       // 1: non-temporal block-score stores

@@ -31,6 +31,9 @@
 #include "device.h"
 
 
+#ifndef IDX_TOPK_VALU_COUNT
+#define IDX_TOPK_VALU_COUNT 1  // 1: the one-wave kernel counts keys per lane and sums them with DPP
+#endif                         // (vector work); 0: a ballot and a scalar popcount per slot
 #ifndef IDX_TOPK_BALLOT_ROWS
 #define IDX_TOPK_BALLOT_ROWS 1024  // rows from which rows of <= 1,024 blocks take one wave each
 #endif
@@ -375,17 +378,27 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
       T = kmin;
       hi = -1;
     }
-    // unrolled: no loop control among the scalar counting (bits above hi
-    // skip).  Once exactly `want` keys reach c they are the ones to take, and
-    // T = c (a key or not) selects them: keys above T, then all keys equal
-    // to it; the lower bits are not needed.
+    // unrolled: no loop control among the counting (bits above hi skip).
+    // Once exactly `want` keys reach c they are the ones to take, and T = c
+    // (a key or not) selects them: keys above T, then all keys equal to it;
+    // the lower bits are not needed.  The count runs on the vector unit (per
+    // lane, then a DPP sum across the wave): the scalar unit is one a CU,
+    // shared by its four SIMDs, and a ballot with a scalar popcount per slot
+    // made it the bottleneck.
 #pragma unroll
     for (int bit = 31; bit >= 0; --bit) {
       if (bit > hi) continue;
       const uint32_t c = T | (1u << bit);
+#if IDX_TOPK_VALU_COUNT
+      uint32_t cl = 0;
+#pragma unroll
+      for (int j = 0; j < S; ++j) cl += (ckey[j] >= c) ? 1u : 0u;
+      const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(cl), 63);
+#else
       uint32_t n = 0;
 #pragma unroll
       for (int j = 0; j < S; ++j) n += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(ckey[j] >= c));
+#endif
       if (n >= want) T = c;
       if (n == want) break;
     }

@@ -15,7 +15,15 @@
 
 namespace idx {
 
+#ifndef IDX_STORE_UNROLL
+#define IDX_STORE_UNROLL 1  // 16-element groups a thread loads before it quantizes them
+#endif
+#ifndef IDX_STORE_NT
+#define IDX_STORE_NT 0      // 1: non-temporal staging loads and payload / scale stores
+#endif
+
 constexpr int kStoreThreads = 256;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t e4m3_rne_satfinite(float t) {
   if (!(t < 448.0f)) return 0x7Eu;  // clamp (NaN too: unspecified)
@@ -31,57 +39,93 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// Quantize one 16-element group (this lane's) of a key and store it; the
+// key's eight lanes call this together.
+__device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot, int grp, uint8_t* payload,
+                                               uint8_t* scales) {
+  const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float x[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[2 * j] = __uint_as_float(wd[j] << 16);
+    x[2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
+  }
+  const uint32_t sb = e4m3_rne_satfinite(amax / 6.0f);
+  const float s = e4m3_value(sb);
+  // midpoints of the e2m1 grid 0 .5 1 1.5 2 3 4 6, times s (exact)
+  const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
+  const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float a = fabsf(x[j]);
+    // ties: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    const uint32_t b2 = a >= m3;
+    const uint32_t b1 = a >= (b2 ? m5 : m1);
+    const float t3 = b2 ? (b1 ? m6 : m4) : (b1 ? m2 : m0);
+    const uint32_t b0 = a > t3;
+    uint32_t mag = (b2 << 2) | (b1 << 1) | b0;
+    mag = (s > 0.0f) ? mag : 0u;
+    const uint32_t code = mag | ((__float_as_uint(x[j]) >> 28) & 8u);
+    packed[j >> 3] |= code << (4 * (j & 7));
+  }
+  u32x2* pdst = reinterpret_cast<u32x2*>(payload + slot * 64 + 8 * grp);
+  // the key's 8 scale bytes as one 8-byte store from its first lane: each
+  // quad of lanes ORs its bytes into a word, lane 4 hands its word to lane 0
+  uint32_t word = sb << (8 * (grp & 3));
+  word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  const uint32_t hi = __shfl_down(word, 4, 8);
+  u32x2* sdst = reinterpret_cast<u32x2*>(scales + slot * 8);
+  if constexpr (IDX_STORE_NT) {
+    __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, pdst);
+    if (grp == 0) __builtin_nontemporal_store(u32x2{word, hi}, sdst);
+  } else {
+    *pdst = u32x2{packed[0], packed[1]};
+    if (grp == 0) *sdst = u32x2{word, hi};
+  }
+}
+
+// Eight lanes a key, one per group; a thread takes IDX_STORE_UNROLL items a
+// grid-stride step and issues all their loads before quantizing any.
 __global__ __launch_bounds__(kStoreThreads) void fp4_store_kernel(
     const uint16_t* __restrict__ staging, int64_t n_tokens, int64_t stride,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ payload,
     uint8_t* __restrict__ scales, int64_t n_slots) {
+  constexpr int U = IDX_STORE_UNROLL;
   const int64_t n_items = n_tokens * 8;
-  for (int64_t item = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x; item < n_items;
-       item += (int64_t)gridDim.x * kStoreThreads) {
-    const int64_t t = item >> 3;
-    const int grp = (int)(item & 7);
-    // the key's row is read whether or not its slot is valid, so the two
-    // loads overlap (the row is in range either way)
-    const uint4* src = reinterpret_cast<const uint4*>(staging + t * stride + 16 * grp);
-    const uint4 w0 = src[0], w1 = src[1];
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0 || slot >= n_slots) continue;  // the key's 8 lanes skip together
-    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float x[16];
-    float amax = 0.0f;
+  const int64_t step = (int64_t)gridDim.x * kStoreThreads;
+  for (int64_t item0 = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x; item0 < n_items; item0 += step * U) {
+    u32x4 w0[U], w1[U];
+    int64_t slot[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[2 * j] = __uint_as_float(wd[j] << 16);
-      x[2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
-      amax = fmaxf(amax, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
+    for (int u = 0; u < U; ++u) {
+      const int64_t item = item0 + u * step;
+      slot[u] = -1;
+      if (item < n_items) {  // a key's 8 items are all in range or all out (n_items is a multiple of 8)
+        const int64_t t = item >> 3;
+        const int grp = (int)(item & 7);
+        // the key's row is read whether or not its slot is valid, so the
+        // loads overlap (the row is in range either way)
+        const u32x4* src = reinterpret_cast<const u32x4*>(staging + t * stride + 16 * grp);
+        if constexpr (IDX_STORE_NT) {
+          w0[u] = __builtin_nontemporal_load(src);
+          w1[u] = __builtin_nontemporal_load(src + 1);
+        } else {
+          w0[u] = src[0];
+          w1[u] = src[1];
+        }
+        slot[u] = slot_mapping[t];
+      }
     }
-    const uint32_t sb = e4m3_rne_satfinite(amax / 6.0f);
-    const float s = e4m3_value(sb);
-    // midpoints of the e2m1 grid 0 .5 1 1.5 2 3 4 6, times s (exact)
-    const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
-    const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
-    uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float a = fabsf(x[j]);
-      // ties: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
-      const uint32_t b2 = a >= m3;
-      const uint32_t b1 = a >= (b2 ? m5 : m1);
-      const float t3 = b2 ? (b1 ? m6 : m4) : (b1 ? m2 : m0);
-      const uint32_t b0 = a > t3;
-      uint32_t mag = (b2 << 2) | (b1 << 1) | b0;
-      mag = (s > 0.0f) ? mag : 0u;
-      const uint32_t code = mag | ((__float_as_uint(x[j]) >> 28) & 8u);
-      packed[j >> 3] |= code << (4 * (j & 7));
+    for (int u = 0; u < U; ++u) {
+      const int64_t item = item0 + u * step;
+      if (item < n_items && slot[u] >= 0 && slot[u] < n_slots)  // the key's 8 lanes take this together
+        quantize_group(w0[u], w1[u], slot[u], (int)(item & 7), payload, scales);
     }
-    *reinterpret_cast<uint2*>(payload + slot * 64 + 8 * grp) = make_uint2(packed[0], packed[1]);
-    // the key's 8 scale bytes as one 8-byte store from its first lane: each
-    // quad of lanes ORs its bytes into a word, lane 4 hands its word to lane 0
-    uint32_t word = sb << (8 * (grp & 3));
-    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-    const uint32_t hi = __shfl_down(word, 4, 8);
-    if (grp == 0) *reinterpret_cast<uint2*>(scales + slot * 8) = make_uint2(word, hi);
   }
 }
 
@@ -89,7 +133,8 @@ hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t s
                             const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,
                             int64_t n_slots, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
-  const int64_t want = (n_tokens * 8 + kStoreThreads - 1) / kStoreThreads;
+  const int64_t want = (n_tokens * 8 + (int64_t)kStoreThreads * IDX_STORE_UNROLL - 1) /
+                       ((int64_t)kStoreThreads * IDX_STORE_UNROLL);
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(fp4_store_kernel, dim3(grid), dim3(kStoreThreads), 0, stream, staging,
                      n_tokens, stride, slot_mapping, payload, scales, n_slots);

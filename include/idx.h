@@ -227,6 +227,8 @@ const char* idx_last_error(void);
  *   workspace  at least idx_sparse_attn_workspace(p) bytes, 16-byte aligned,
  *            caller-owned; its contents are scratch (partial results of the
  *            splits of each (request, KV head)), needing no initialisation.
+ *            When the batch fills the device without splitting, the size is 0
+ *            and the workspace may be NULL.
  * Limits: P * G <= IDX_ATTN_MAX_ROWS (the rows of one request and KV head
  * share one 16-row MFMA tile and read each selected K/V page once), P * topk
  * <= IDX_ATTN_MAX_IDS.  q, k, v, out 16-byte aligned.
@@ -264,8 +266,8 @@ typedef struct idx_attn_params {
  * device, or a negative IDX_E_* code when the sizes are refused. */
 int64_t idx_sparse_attn_workspace(const idx_attn_params* p);
 
-/* Sparse attention over the selected blocks (two launches on `stream`: the
- * splits' partials, then their merge).  Refusals as the other calls, plus
+/* Sparse attention over the selected blocks (on `stream`: the splits'
+ * partials, then their merge; one launch when nothing is split).  Refusals as the other calls, plus
  * IDX_E_PACK for P * G > IDX_ATTN_MAX_ROWS, IDX_E_TOPK for P * topk >
  * IDX_ATTN_MAX_IDS, IDX_E_MODE for a bad sm_scale and IDX_E_SHAPE for a
  * workspace below idx_sparse_attn_workspace(p). */

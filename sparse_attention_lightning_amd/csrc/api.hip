@@ -148,7 +148,7 @@ int64_t attn_workspace_bytes(const idx_attn_params* p, int* splits) {
   const int64_t items = (int64_t)p->n_req * p->kv_heads;
   const int s = idx::attn_splits(items);
   if (splits) *splits = s;
-  return items * s * 16 * 132 * (int64_t)sizeof(float);
+  return s > 1 ? items * s * 16 * 132 * (int64_t)sizeof(float) : 0;  // one split: no partials
 }
 
 }  // namespace
@@ -175,7 +175,7 @@ int idx_sparse_attn(const idx_attn_params* p, void* stream) {
     return fail(IDX_E_ALIGN, "q, k, v, out and workspace must be 16-byte aligned");
   int splits = 1;
   const int64_t need = attn_workspace_bytes(p, &splits);
-  if (rows > 0 && (!p->workspace || p->workspace_bytes < need))
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
     return fail(IDX_E_SHAPE, "workspace of %lld bytes is below the %lld needed", (long long)p->workspace_bytes,
                 (long long)need);
   clear_stale_error();

@@ -15,7 +15,8 @@
 // waves take the share's blocks one at a time from an LDS counter and each
 // keeps its own online-softmax state, the four are merged in LDS, and the workgroup writes
 // its partial (max, sum, unnormalized output) per row.  A second kernel merges
-// the splits of an item.
+// the splits of an item; an item that is not split (splits = 1) writes its
+// output directly and no merge runs.
 //
 // Per 32-token unit of a block, per wave:
 //   S^T = K Q^T   MFMA 16x16x32 bf16 with K as the A operand: lane (m, gq)
@@ -62,6 +63,33 @@ struct AttnUnit {
   u32x4 k[2][4];  // [half c][k-step s]
   u32x4 v[8];     // [dim tile dt]
 };
+
+// Row `row` (of the item's P x G) of item (request r, KV head h): output
+// dimensions 8 c8 .. + 8 from the unnormalized sum acc8 over all its tokens,
+// with running max M (log2 units) and sum L; NaN when a bad page was seen.
+__device__ __forceinline__ void attn_finalize(const AttnArgs& a, int r, int h, int row, int c8, float M, float L,
+                                              const float* acc8, bool nan) {
+  const int j = row / a.G, g = row - j * a.G;
+  const int64_t orow = (((int64_t)(r * a.P + j)) * a.H + h) * a.G + g;
+  bf16x8_t ob;
+  float lse;
+  if (nan) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)__builtin_nanf("");
+    lse = __builtin_nanf("");
+  } else if (M == -INFINITY) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)0.f;
+    lse = -INFINITY;
+  } else {
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)(acc8[d] * inv);
+    lse = (M + __builtin_amdgcn_logf(L)) * 0.693147180559945309f;
+  }
+  *reinterpret_cast<bf16x8_t*>(a.out + orow * 128 + 8 * c8) = ob;
+  if (c8 == 0) a.lse[orow] = lse;
+}
 
 __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_kernel(const AttnArgs a) {
   __shared__ int32_t list_id[IDX_ATTN_MAX_IDS];
@@ -282,6 +310,10 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
 #pragma unroll
       for (int d = 0; d < 8; ++d) acc8[d] += f * U.comb.o[w2][row][8 * c8 + d];
     }
+    if (S == 1) {  // the whole union: the output itself
+      if (row < P * G) attn_finalize(a, r, h, row, c8, M, L, acc8, nan);
+      return;
+    }
     if (nan) L = __builtin_nanf("");
     float* part = a.ws + ((int64_t)item * S + split) * 16 * kPartFloats + row * kPartFloats;
     if (c8 == 0) {
@@ -301,7 +333,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnAr
   const int H = a.H, P = a.P, G = a.G, S = a.splits;
   if (row >= P * G) return;
   const int r = item / H, h = item - r * H;
-  const int j = row / G, g = row - j * G;
   const float* part = a.ws + (int64_t)item * S * 16 * kPartFloats + row * kPartFloats;
   float M = -INFINITY;
   bool nan = false;
@@ -325,25 +356,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnAr
       }
     }
   }
-  const int64_t orow = (((int64_t)(r * P + j)) * H + h) * G + g;
-  bf16x8_t ob;
-  float lse;
-  if (nan) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)__builtin_nanf("");
-    lse = __builtin_nanf("");
-  } else if (M == -INFINITY) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)0.f;
-    lse = -INFINITY;
-  } else {
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) ob[d] = (__bf16)(acc8[d] * inv);
-    lse = (M + __builtin_amdgcn_logf(L)) * 0.693147180559945309f;
-  }
-  *reinterpret_cast<bf16x8_t*>(a.out + orow * 128 + 8 * c8) = ob;
-  if (c8 == 0) a.lse[orow] = lse;
+  attn_finalize(a, r, h, row, c8, M, L, acc8, nan);
 }
 
 namespace {
@@ -373,7 +386,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.n_req * a.H;
   if (items == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0, stream, a);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)items), dim3(kAttnThreads), 0, stream, a);
+  if (a.splits > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)items), dim3(kAttnThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -316,9 +316,10 @@ def make_attn_params(*, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, req_s
     p.lse = _dev(lse, "lse", (torch.float32,))
     if workspace is None:
         need = idx_sparse_attn_workspace(p)
-        workspace = torch.empty(max(1, (need + 15) // 16) * 4, dtype=torch.float32, device=q.device)
-    p.workspace = _dev(workspace, "workspace", (torch.float32, torch.uint8))
-    p.workspace_bytes = workspace.numel() * workspace.element_size()
+        if need > 0:
+            workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    p.workspace = _dev(workspace, "workspace", (torch.float32, torch.uint8), optional=True)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     p._keep = (q, k, v, req_slot, block_table, row_len, topk_ids, out, lse, workspace)
     return p
 

@@ -171,6 +171,30 @@ def test_attn_repeated_calls_are_identical(oracle):
         assert np.array_equal(first["lse"], again["lse"], equal_nan=True)
 
 
+def test_attn_unsplit_batch(oracle):
+    """A batch of (request, KV head) items that fills the device on its own
+    is not split: the partial kernel writes the output, no merge runs and no
+    workspace is needed."""
+    say("attn unsplit batch")
+    R = 80
+    lens = [int(x) for x in np.random.default_rng(790).integers(0, 3000, size=R)]
+    w = W.make(name="unsplit", R=R, P=2, H=4, k_format=W.K_BF16, req_len=lens, topk=5, init_blocks=1,
+               local_blocks=1, seed=791, pads=2, pad_len=800, device="cuda")
+    wc = W.make(name="unsplit", R=R, P=2, H=4, k_format=W.K_BF16, req_len=lens, topk=5, init_blocks=1,
+                local_blocks=1, seed=791, pads=2, pad_len=800)
+    at = W.make_attn(w, 8)
+    ids = pins.random_selection(wc, np.random.default_rng(792), topk=5)
+    out = torch.empty_like(at.q)
+    lse = torch.empty(at.q.shape[:3], dtype=torch.float32, device="cuda")
+    p = I.make_attn_params(q=at.q, k=at.k, v=at.v, req_slot=w.req_slot, block_table=w.block_table,
+                           row_len=w.row_len, topk_ids=torch.as_tensor(ids, device="cuda"), out=out, lse=lse,
+                           sm_scale=SCALE)
+    assert I.idx_sparse_attn_workspace(p) == 0 and p.workspace is None
+    from test_gpu_parity import _graph_kernel_nodes
+    assert _graph_kernel_nodes(lambda: I.idx_sparse_attn(p)) == 1
+    assert_attn(gpu_attn(w, at, ids), oracle.sparse_attn(**W.attn_oracle_args(w, at, ids, SCALE)), "unsplit")
+
+
 def test_attn_launch_count():
     from test_gpu_parity import _graph_kernel_nodes
     say("attn launch count")

@@ -218,9 +218,11 @@ const char* idx_last_error(void);
  *   q        bf16 [R*P][H][G][128]
  *   k        bf16 [n_pages][H][128 tokens][128]: token t of page p, head h is
  *            k[p][h][t]
- *   v        bf16 [n_pages][H][128 dims][128 tokens]: each page-head's V
- *            transposed, v[p][h][d][t] (16 consecutive tokens of a dimension
- *            are one load for the PV product)
+ *   v        bf16 [n_pages][H][4][128 dims][32 tokens]: each 32-token quarter
+ *            of a page-head's V transposed, token t, dimension d at
+ *            v[p][h][t / 32][d][t % 32] (8 consecutive tokens of a dimension
+ *            are one 16-byte load for the PV product, and the 16 dimensions a
+ *            load instruction covers are 1 KB in a row)
  *   req_slot, block_table, row_len: as idx_params
  *   topk_ids int32 [R*P][H][topk]
  *   out      bf16 [R*P][H][G][128];  lse fp32 [R*P][H][G]

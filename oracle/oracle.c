@@ -539,8 +539,8 @@ int oracle_sparse_attn(const oracle_attn_params* p) {
         int tt = (int)(tok[e] % 128);
         l += w;
         for (d = 0; d < 128; d++) {
-          /* V is [page][h][dim][token]; mutant 21 reads it as [token][dim] */
-          double v = bf16_value(vp[MUTANT(21) ? tok[e] * 128 + d : (page_h * 128 + d) * 128 + tt]);
+          /* V is [page][h][token / 32][dim][token % 32]; mutant 21 reads it as [token][dim] */
+          double v = bf16_value(vp[MUTANT(21) ? tok[e] * 128 + d : ((page_h * 4 + tt / 32) * 128 + d) * 32 + tt % 32]);
           o[d] += w * v;
           oa[d] += w * fabs(v);
         }

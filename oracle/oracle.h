@@ -109,7 +109,8 @@ int oracle_fp4_store(const void* staging_bf16, int64_t n_tokens,
  *    row's length, the same causal length as the indexer;
  *  - K and V are paged like the index K (page = block = 128 tokens, the same
  *    request slots and block table), bf16, K as [n_pages][kv_heads][128
- *    tokens][128] and V as [n_pages][kv_heads][128 dims][128 tokens];
+ *    tokens][128] and V as [n_pages][kv_heads][4][128 dims][32 tokens] (each
+ *    32-token quarter of a page-head transposed);
  *  - out = sum_t softmax_t(sm_scale * q.k_t) v_t and lse = ln sum_t
  *    exp(sm_scale * q.k_t); a row that sees no selected token gets out = 0 and
  *    lse = -inf, as do graph pads; a row that sees a token of a block whose
@@ -130,7 +131,7 @@ typedef struct oracle_attn_params {
   int64_t n_pages;
   const void*    q;        /* bf16 [n_req*P][H][G][128]                          */
   const void*    k;        /* bf16 [n_pages][H][128 tokens][128]                 */
-  const void*    v;        /* bf16 [n_pages][H][128 dims][128 tokens]            */
+  const void*    v;        /* bf16 [n_pages][H][4][128 dims][32 tokens]          */
   const int32_t* req_slot;    /* [n_req]                                         */
   const int32_t* block_table; /* [n_slot_rows][max_blocks]                       */
   const int32_t* row_len;     /* [n_req*P]                                       */

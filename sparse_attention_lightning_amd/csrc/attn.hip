@@ -26,7 +26,10 @@
 //   O^T += V^T P^T  with P^T as the B operand, which is exactly what each lane
 //                 holds (its row's probabilities of those 8 tokens, in bf16),
 //                 and V^T as the A operand, read as 16 contiguous bytes (8
-//                 tokens of one dimension) from the page's transposed V.
+//                 tokens of one dimension) from the unit's transposed V: each
+//                 32-token quarter of a page-head is stored [128 dims][32
+//                 tokens], so one load instruction (16 dimensions) covers 1 KB
+//                 of whole lines.
 // So K and V go from HBM straight into operand registers, and the rescale of
 // the running output is local to each lane (lane n holds row n's output
 // dimensions 16 dt + 4 gq + i).  Loads go through per-page buffer descriptors;
@@ -210,9 +213,9 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
         w.k[c][s] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (32 * sub + tk0 + 4 * c) * 256 + 64 * s + 16 * gq, 0, 0));
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8; ++dt)  // V quarter `sub`: [128 dims][32 tokens], 64 B a dimension
       w.v[dt] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (16 * dt + n) * 256 + (32 * sub + 8 * gq) * 2, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 8192 * sub + (16 * dt + n) * 64 + 16 * gq, 0, 0));
   };
 
   auto compute = [&](const AttnUnit& w, int U_) {

@@ -42,7 +42,7 @@ struct StepArgs {
 struct AttnArgs {
   const uint16_t* q;          // bf16 [R*P][H][G][128]
   const uint8_t* k;           // bf16 [n_pages][H][128 tokens][128]
-  const uint8_t* v;           // bf16 [n_pages][H][128 dims][128 tokens]
+  const uint8_t* v;           // bf16 [n_pages][H][4][128 dims][32 tokens]
   const int32_t* req_slot;
   const int32_t* block_table;
   const int32_t* row_len;

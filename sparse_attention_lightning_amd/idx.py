@@ -280,14 +280,14 @@ def make_attn_params(*, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, req_s
                      out: torch.Tensor, lse: torch.Tensor, sm_scale: float,
                      workspace: torch.Tensor | None = None) -> IdxAttnParams:
     """Parameter block of the sparse attention from tensors: q [R*P, H, G,
-    128] bf16, k [n_pages, H, 128, 128] bf16, v [n_pages, H, 128 dims, 128
+    128] bf16, k [n_pages, H, 128, 128] bf16, v [n_pages, H, 4, 128 dims, 32
     tokens] bf16, topk_ids [R*P*H, topk] (or [R*P, H, topk]) int32, out like
     q, lse [R*P, H, G] fp32.  Without ``workspace`` one of the size the
     library asks for is allocated here (kept alive by the returned object)."""
     if q.dim() != 4 or q.shape[-1] != 128:
         raise ValueError("q must be [R*P, H, G, 128]")
-    if k.dim() != 4 or k.shape[2:] != (128, 128) or v.shape != k.shape:
-        raise ValueError("k and v must be [n_pages, H, 128, 128]")
+    if k.dim() != 4 or k.shape[2:] != (128, 128) or v.shape != (k.shape[0], k.shape[1], 4, 128, 32):
+        raise ValueError("k must be [n_pages, H, 128, 128] and v [n_pages, H, 4, 128, 32]")
     p = IdxAttnParams()
     n_req = req_slot.numel()
     rows, H, G = q.shape[0], q.shape[1], q.shape[2]

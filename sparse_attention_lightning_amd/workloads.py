@@ -323,7 +323,7 @@ class AttnInputs:
     q_per_kv: int
     q: torch.Tensor     # bf16 [n_req*P, H, G, 128]: query head g of KV head h of each draft row
     k: torch.Tensor     # bf16 [n_pages, H, 128 tokens, 128]
-    v: torch.Tensor     # bf16 [n_pages, H, 128 dims, 128 tokens] (each page-head's V transposed)
+    v: torch.Tensor     # bf16 [n_pages, H, 4, 128 dims, 32 tokens] (each 32-token quarter of a page-head transposed)
     seed: int
 
 
@@ -342,8 +342,8 @@ def make_attn(w: Workload, q_per_kv: int, seed: int | None = None, poison: bool 
     _randn_into(q.view(-1, D), gen)
     k = torch.empty((n_pages, H, BLOCK, D), dtype=torch.bfloat16, device=dev)
     _randn_into(k.view(-1, D), gen)
-    v = torch.empty((n_pages, H, D, BLOCK), dtype=torch.bfloat16, device=dev)
-    _randn_into(v.view(-1, BLOCK), gen)
+    v = torch.empty((n_pages, H, 4, D, BLOCK // 4), dtype=torch.bfloat16, device=dev)
+    _randn_into(v.view(-1, D), gen)
     if poison:
         gap = w.extra["gap_pages"]
         if len(gap):
@@ -352,7 +352,10 @@ def make_attn(w: Workload, q_per_kv: int, seed: int | None = None, poison: bool 
             v[gi] = POISON_ATTN_V
         for pg, off in w.extra["tails"]:
             k[pg, :, off:, :] = 0
-            v[pg, :, :, off:] = POISON_ATTN_V
+            for u in range(4):  # tokens >= off of each 32-token quarter
+                start = max(0, off - 32 * u)
+                if start < 32:
+                    v[pg, :, u, :, start:] = POISON_ATTN_V
     return AttnInputs(q_per_kv=q_per_kv, q=q, k=k, v=v, seed=seed)
 
 

@@ -133,7 +133,7 @@ def sparse_attn(a: dict) -> dict:
     R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
     q = bf16_values(a["q"]).reshape(R * P, H, G, 128)
     k = bf16_values(a["k"]).reshape(a["n_pages"], H, 128, 128)
-    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 128, 128)   # [page][h][dim][token]
+    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 4, 128, 32)   # [page][h][token / 32][dim][token % 32]
     scale = float(np.float32(a["sm_scale"]))  # the softmax scale crosses the interface as fp32
     out = np.zeros((R * P, H, G, 128))
     lse = np.full((R * P, H, G), -np.inf)
@@ -146,7 +146,7 @@ def sparse_attn(a: dict) -> dict:
         pg = np.array([p for p, _ in toks])
         tt = np.array([t for _, t in toks])
         s = scale * (k[pg, h, tt, :] @ q[row, h, g])
-        out[row, h, g] = softmax(s) @ v[pg, h, :, tt]
+        out[row, h, g] = softmax(s) @ v[pg, h, tt // 32, :, tt % 32]
         lse[row, h, g] = logsumexp(s)
     return {"out": out, "lse": lse}
 
@@ -156,7 +156,7 @@ def sparse_attn_loops(a: dict) -> dict:
     R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
     q = bf16_values(a["q"]).reshape(R * P, H, G, 128).tolist()
     k = bf16_values(a["k"]).reshape(a["n_pages"], H, 128, 128)
-    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 128, 128)
+    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 4, 128, 32)
     out = [[[[0.0] * 128 for _ in range(G)] for _ in range(H)] for _ in range(R * P)]
     lse = [[[-math.inf] * G for _ in range(H)] for _ in range(R * P)]
     for row, h, g, toks, bad in _attn_rows(a):
@@ -175,7 +175,7 @@ def sparse_attn_loops(a: dict) -> dict:
         tot = sum(w)
         o = [0.0] * 128
         for wi, (p_, t) in zip(w, toks):
-            col = v[p_, h, :, t].tolist()
+            col = v[p_, h, t // 32, :, t % 32].tolist()
             for d in range(128):
                 o[d] += wi * col[d]
         out[row][h][g] = [x / tot for x in o]

@@ -739,7 +739,7 @@ def pin_attn_dense(o) -> None:
         pages = torch.as_tensor(bt[slot, : (L + 127) // 128].astype(np.int64))
         for h in range(H):
             kc = k64[pages, h].reshape(-1, 128)[:L]                       # [L, 128] in position order
-            vc = v64[pages, h].permute(0, 2, 1).reshape(-1, 128)[:L]      # [L, 128]
+            vc = v64[pages, h].permute(0, 1, 3, 2).reshape(-1, 128)[:L]   # [L, 128] in position order
             for j in range(P):
                 row = r * P + j
                 mask = torch.arange(L) < int(lens[row])
@@ -765,7 +765,7 @@ def pin_attn_closed_forms(o) -> None:
     R, P, H, G = w.n_req, w.packed_queries, w.gqa, at.q_per_kv
     col = torch.randn(128, generator=torch.Generator().manual_seed(642)).to(torch.bfloat16)
     v_const = at.v.clone()
-    v_const[:] = col[None, None, :, None]
+    v_const[:] = col[None, None, None, :, None]
     res = o.sparse_attn(**W.attn_oracle_args(w, W.AttnInputs(G, at.q, at.k, v_const, at.seed), ids, ATTN_SCALE))
     lens = w.row_len.numpy()
     for row in range(R * P):
@@ -793,7 +793,7 @@ def pin_attn_closed_forms(o) -> None:
             cols = []
             for b in sorted(set(ids[row, h][ids[row, h] >= 0].tolist())):
                 page = bt[int(w.req_slot[r]), b]
-                cols += [v64[page, h, :, t] for t in range(min(128, int(lens[row]) - 128 * b))]
+                cols += [v64[page, h, t // 32, :, t % 32] for t in range(min(128, int(lens[row]) - 128 * b))]
             n = len(cols)
             s0 = ATTN_SCALE * (q64[row, h] @ k0.double().numpy())
             assert_attn_close({"out": res["out"][row, h], "lse": res["lse"][row, h]},
@@ -807,7 +807,7 @@ def pin_attn_closed_forms(o) -> None:
     for r in range(2):
         page = bt1[int(w1.req_slot[r]), 0]
         for h in range(2):
-            want = at1.v[page, h, :, 0].float().numpy()
+            want = at1.v[page, h, 0, :, 0].float().numpy()
             assert np.array_equal(res["out"][r, h], np.broadcast_to(want, (3, 128))), "one token: V column"
             s = ATTN_SCALE * (at1.q[r, h].double().numpy() @ at1.k[page, h, 0].double().numpy())
             assert np.allclose(res["lse"][r, h], s, rtol=1e-6, atol=1e-6), "one token: lse"

@@ -251,7 +251,7 @@ def _subset(w: W.Workload, at: W.AttnInputs, ids: np.ndarray, reqs) -> tuple[dic
         return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
     kk = u16(at.k.index_select(0, pg)) if len(pages) else np.zeros((1, H, 128, 128), np.uint16)
-    vv = u16(at.v.index_select(0, pg)) if len(pages) else np.zeros((1, H, 128, 128), np.uint16)
+    vv = u16(at.v.index_select(0, pg)) if len(pages) else np.zeros((1, H, 4, 128, 32), np.uint16)
     q = u16(at.q)[rows]
     a = dict(n_req=len(reqs), n_slot_rows=n_slot, packed_queries=P, kv_heads=H, q_per_kv=at.q_per_kv,
              max_blocks=w.max_blocks, topk=K, sm_scale=SCALE, n_pages=max(1, len(pages)), q=np.ascontiguousarray(q),

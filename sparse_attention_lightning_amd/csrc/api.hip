@@ -2,6 +2,7 @@
 //
 // Every entry point checks its arguments on the host before touching the HIP
 // runtime, so a refused call enqueues nothing and needs no device.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -146,7 +147,8 @@ int check_attn(const idx_attn_params* p) {
 
 int64_t attn_workspace_bytes(const idx_attn_params* p, int* splits) {
   const int64_t items = (int64_t)p->n_req * p->kv_heads;
-  const int s = idx::attn_splits(items);
+  const int64_t max_union = std::min<int64_t>((int64_t)p->packed_queries * p->topk, p->max_blocks);
+  const int s = idx::attn_splits(items, max_union);
   if (splits) *splits = s;
   return s > 1 ? items * s * 16 * 132 * (int64_t)sizeof(float) : 0;  // one split: no partials
 }

@@ -11,9 +11,9 @@
 // selections, each block carrying the mask of the rows that chose it: a block
 // chosen by several draft rows is read from HBM once for all of them, as the
 // indexer reads each K page once for all rows of a request.  An item's union
-// is cut into `splits` contiguous shares, one workgroup of four waves each; the
-// waves take the share's blocks one at a time from an LDS counter and each
-// keeps its own online-softmax state, the four are merged in LDS, and the workgroup writes
+// is cut into `splits` contiguous shares, one workgroup of four waves each
+// (one workgroup a CU, so one wave a SIMD); wave w takes the share's blocks w,
+// w + 4, ... and keeps its own online-softmax state, the four are merged in LDS, and the workgroup writes
 // its partial (max, sum, unnormalized output) per row.  A second kernel merges
 // the splits of an item; an item that is not split (splits = 1) writes its
 // output directly and no merge runs.
@@ -35,6 +35,7 @@
 // dimensions 16 dt + 4 gq + i).  Loads go through per-page buffer descriptors;
 // a page outside the pool gets an empty one (reads nothing) and makes every
 // row that sees it NaN.
+#include <algorithm>
 #include <atomic>
 
 #include "device.h"
@@ -107,7 +108,6 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
     } comb;
   } U;
   __shared__ uint32_t wave_tot[kAttnWaves];
-  __shared__ uint32_t next_block;  // blocks of the share handed out to the waves
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)__builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,12 +149,12 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
   // 3. this workgroup's share of the union and its page ids
   const int lo = (int)((int64_t)split * nu / S), hi = (int)((int64_t)(split + 1) * nu / S);
   for (int x = lo + tid; x < hi; x += kAttnThreads) list_page[x] = a.block_table[(int64_t)slot * MB + list_id[x]];
-  if (tid == 0) next_block = 0;
   __syncthreads();
 
-  // 4. the share's blocks, one at a time to whichever wave asks next (the
-  // waves of a SIMD are not served equally by the memory system, so fixed
-  // per-wave shares would end on the slower one)
+  // 4. the wave's blocks: lo + wave, lo + wave + 4, ... A fixed assignment
+  // keeps the order of every floating-point sum, so repeated calls give
+  // bit-identical outputs; with one wave a SIMD it measured as fast as
+  // handing blocks out from an LDS counter.
   const int n = lane & 15, gq = lane >> 4;
   const bool row_ok = n < P * G;
   const int j = row_ok ? n / G : 0, g = row_ok ? n - j * G : 0;
@@ -168,10 +168,8 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
     if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + 32 * s + 8 * gq);
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
   }
-  const uint32_t n_share = (uint32_t)(hi - lo);
-  int vm_x = -1;      // lane bi % 64 holds the share position of the wave's block bi (-1: none)
-  bool done = false;  // the share is exhausted
-  int last = -1;      // the wave's last block that holds a block
+  const int my_blocks = (hi - lo - wave + kAttnWaves - 1) / kAttnWaves;  // may be <= 0
+  const int n_units = my_blocks > 0 ? 4 * my_blocks : 0;
 
   float m = -INFINITY, l = 0.f;
   bool bad = false;
@@ -182,24 +180,8 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
   const int tk0 = 8 * (n >> 2) + (n & 3);
 
   auto issue = [&](AttnUnit& w, int U_) {
-    const int bi = U_ >> 2;
-    if ((U_ & 3) == 0) {  // a new block: the next one of the share
-      int xn = -1;
-      if (!done) {
-        uint32_t k = 0;
-        if (lane == 0) k = atomicAdd(&next_block, 1u);
-        k = __builtin_amdgcn_readfirstlane(k);
-        if (k < n_share) {
-          xn = lo + (int)k;
-          last = bi;
-        } else {
-          done = true;
-        }
-      }
-      if (lane == (bi & 63)) vm_x = xn;
-    }
-    const int x = __builtin_amdgcn_readlane(vm_x, bi & 63);
-    const bool exists = x >= 0;
+    const int x = lo + wave + kAttnWaves * (U_ >> 2);
+    const bool exists = U_ < n_units;
     const int page = exists ? (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]) : -1;
     const bool ok = exists && page >= 0 && page < a.n_pages;
     const int64_t ph = (int64_t)(ok ? page : 0) * H + h;
@@ -219,8 +201,8 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
   };
 
   auto compute = [&](const AttnUnit& w, int U_) {
-    const int x = __builtin_amdgcn_readlane(vm_x, (U_ >> 2) & 63);
-    if (x < 0) return;
+    if (U_ >= n_units) return;
+    const int x = lo + wave + kAttnWaves * (U_ >> 2);
     const int b = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_id[x]);
     const uint32_t mask = __builtin_amdgcn_readfirstlane((uint32_t)list_mask[x]);
     const int page = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]);
@@ -273,13 +255,12 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
     AttnUnit ring[kAttnRing];
 #pragma unroll
     for (int k = 0; k < kAttnRing - 1; ++k) issue(ring[k], k);
-    for (int U0 = 0;; U0 += kAttnRing) {
+    for (int U0 = 0; U0 < n_units; U0 += kAttnRing) {
 #pragma unroll
       for (int k = 0; k < kAttnRing; ++k) {
         issue(ring[(k + kAttnRing - 1) % kAttnRing], U0 + k + kAttnRing - 1);
         compute(ring[k], U0 + k);
       }
-      if (done && 4 * (last + 1) <= U0 + kAttnRing) break;  // every unit of a held block is computed
     }
   }
 
@@ -339,6 +320,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnAr
   const float* part = a.ws + (int64_t)item * S * 16 * kPartFloats + row * kPartFloats;
   float M = -INFINITY;
   bool nan = false;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float* ps = part + (int64_t)s * 16 * kPartFloats;
     M = fmaxf(M, ps[128]);
@@ -346,6 +328,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnAr
   }
   float L = 0.f, acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
       const float* ps = part + (int64_t)s * 16 * kPartFloats;
       const float f = (ps[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[128] - M);
@@ -379,9 +362,13 @@ int attn_resident_workgroups() {
 }
 }  // namespace
 
-int attn_splits(int64_t items) {
+int attn_splits(int64_t items, int64_t max_union) {
   if (items <= 0) return 1;
-  const int64_t s = (attn_resident_workgroups() + items - 1) / items;
+  // enough workgroups to fill the device, but at least 8 blocks a split of
+  // the largest union an item can have (a split of nothing still costs its
+  // set-up, and the merge one partial more)
+  int64_t s = (attn_resident_workgroups() + items - 1) / items;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, (max_union + 7) / 8));
   return (int)(s < 1 ? 1 : (s > IDX_ATTN_MAX_SPLITS ? IDX_ATTN_MAX_SPLITS : s));
 }
 

@@ -54,8 +54,9 @@ struct AttnArgs {
   int32_t n_req, n_slot_rows, P, H, G, max_blocks, topk, splits;
   float c2;                   // sm_scale * log2(e)
 };
-// Workgroups of the partial kernel per (request, KV head) item.
-int attn_splits(int64_t items);
+// Workgroups of the partial kernel per (request, KV head) item, for `items`
+// items whose unions hold at most `max_union` blocks.
+int attn_splits(int64_t items, int64_t max_union);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
 hipError_t launch_score(const StepArgs& a, hipStream_t stream);       // any rows per request

@@ -198,14 +198,16 @@ def test_attn_unsplit_batch(oracle):
 def test_attn_launch_count():
     from test_gpu_parity import _graph_kernel_nodes
     say("attn launch count")
-    w = W.make(name="lc", R=3, P=4, H=2, k_format=W.K_BF16, req_len=[400, 900, 0], topk=4, init_blocks=1,
+    # few items with long selections: split, so partials and a merge (two launches)
+    w = W.make(name="lc", R=3, P=4, H=2, k_format=W.K_BF16, req_len=[4000, 9000, 0], topk=32, init_blocks=1,
                local_blocks=1, seed=770, device="cuda")
     at = W.make_attn(w, 4)
-    ids = torch.zeros((w.rows, 4), dtype=torch.int32, device="cuda")
+    ids = torch.zeros((w.rows, 32), dtype=torch.int32, device="cuda")
     out = torch.empty_like(at.q)
     lse = torch.empty(at.q.shape[:3], dtype=torch.float32, device="cuda")
     p = I.make_attn_params(q=at.q, k=at.k, v=at.v, req_slot=w.req_slot, block_table=w.block_table,
                            row_len=w.row_len, topk_ids=ids, out=out, lse=lse, sm_scale=SCALE)
+    assert I.idx_sparse_attn_workspace(p) > 0
     assert _graph_kernel_nodes(lambda: I.idx_sparse_attn(p)) == 2
 
 

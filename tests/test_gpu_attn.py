@@ -195,6 +195,76 @@ def test_attn_unsplit_batch(oracle):
     assert_attn(gpu_attn(w, at, ids), oracle.sparse_attn(**W.attn_oracle_args(w, at, ids, SCALE)), "unsplit")
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_attn_random_shapes(oracle, case):
+    """Seeded random shapes: draft rows, KV heads, query heads a KV head
+    (P G <= 16), request lengths (some 0, some straddling block ends),
+    selection sizes, graph pads, repeated and ignored ids."""
+    rng = np.random.default_rng(900 + case)
+    P = int(rng.integers(1, 9))
+    G = int(rng.integers(1, 16 // P + 1))
+    H = int(rng.integers(1, 5))
+    R = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.choice([0, 1, 127, 128, 129, 700, 2048, 5000, 20000], size=R)]
+    topk = int(rng.integers(4, 40))
+    pads = int(rng.integers(0, 3))
+    say("attn random", case, dict(P=P, G=G, H=H, R=R, lens=lens, topk=topk, pads=pads))
+    kw = dict(name="rand", R=R, P=P, H=H, k_format=W.K_BF16, req_len=lens, topk=topk, init_blocks=1,
+              local_blocks=1, seed=910 + case, pads=pads, pad_len=int(rng.integers(1, 3000)))
+    w = W.make(**kw, device="cuda")
+    wc = W.make(**kw)
+    at = W.make_attn(w, G)
+    ids = pins.random_selection(wc, np.random.default_rng(920 + case), topk=topk)
+    scale = float(np.float32(rng.choice([0.05, SCALE, 0.5])))
+    assert_attn(gpu_attn(w, at, ids, scale), oracle.sparse_attn(**W.attn_oracle_args(w, at, ids, scale)),
+                f"random case {case}")
+
+
+def test_attn_graph_replays(oracle):
+    """idx_sparse_attn captured once in a HIP graph and replayed after new
+    queries, values, lengths and selections are written into the captured
+    buffers equals the eager call on every replay (the workspace needs no
+    clearing between replays)."""
+    say("attn graph replays")
+    kw = dict(name="gr", R=3, P=4, H=2, k_format=W.K_BF16, req_len=[3000, 9000, 400], topk=24, init_blocks=1,
+              local_blocks=1, seed=930)
+    w, wc = W.make(**kw, device="cuda"), W.make(**kw)
+    at = W.make_attn(w, 4)
+    ids = torch.as_tensor(pins.random_selection(wc, np.random.default_rng(931), topk=24), device="cuda")
+    out = torch.empty_like(at.q)
+    lse = torch.empty(at.q.shape[:3], dtype=torch.float32, device="cuda")
+    p = I.make_attn_params(q=at.q, k=at.k, v=at.v, req_slot=w.req_slot, block_table=w.block_table,
+                           row_len=w.row_len, topk_ids=ids, out=out, lse=lse, sm_scale=SCALE)
+    assert p.workspace is not None  # split: partials and a merge in the graph
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        I.idx_sparse_attn(p)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        I.idx_sparse_attn(p)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(932)
+    base_len = w.row_len.clone()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        at.q.copy_(torch.randn(at.q.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        at.v.copy_(torch.randn(at.v.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        w.row_len.copy_(torch.clamp(base_len - 301 * rep, min=0))
+        ids.copy_(torch.as_tensor(pins.random_selection(wc, np.random.default_rng(940 + rep), topk=24), device="cuda"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {"out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+        eager = gpu_attn(w, at, ids)
+        assert np.array_equal(got["out"], eager["out"], equal_nan=True), f"replay {rep}: out"
+        assert np.array_equal(got["lse"], eager["lse"], equal_nan=True), f"replay {rep}: lse"
+    assert_attn(got, oracle.sparse_attn(**W.attn_oracle_args(w, at, ids, SCALE)), "graph replay")
+
+
 def test_attn_launch_count():
     from test_gpu_parity import _graph_kernel_nodes
     say("attn launch count")

@@ -333,11 +333,11 @@ def _subset(w: W.Workload, at: W.AttnInputs, ids: np.ndarray, reqs) -> tuple[dic
     return a, rows
 
 
-@pytest.mark.parametrize("cfg,reqs", [(3, "all"), (4, list(range(0, 64, 4)))], ids=["524k_fp8", "150k_nvfp4"])
+@pytest.mark.parametrize("cfg,reqs", [(3, "all"), (4, "all")], ids=["524k_fp8", "150k_nvfp4"])
 def test_attn_full_size(oracle, cfg, reqs):
     """Every row of the 524K workload (its 32 requests and 3 graph pads:
-    about 8 GB of selected K/V pages go to the oracle) and 16 of the 64
-    requests of the 150K one, against the oracle."""
+    about 8 GB of selected K/V pages go to the oracle) and of the 150K one
+    (64 requests, about 16 GB), against the oracle."""
     w = W.config(cfg, device="cuda")
     if reqs == "all":
         reqs = list(range(w.n_req))

@@ -345,10 +345,14 @@ def bench_attn(w, topk_ids, G: int, flush, stream, n_ev: int) -> dict:
     gbps = nbytes / (us / 1e6) / 1e9
     del at, out, lse, p
     torch.cuda.empty_cache()
+    traffic = traffic_from_profiles("attn_partial_kernel_bf16", w.name, source_digest())
     return {"us": round(us, 2), "us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(ms, [10, 50, 90])],
             "q_per_kv": G, "kv_heads": H, "query_heads": rows, "selected_blocks": int(selected),
             "union_blocks": int(union), "kv_bytes": int(tokens * 512), "algorithmic_bytes": int(nbytes),
             "achieved_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "roofline": {"kernel": "attn_partial_kernel + attn_combine_kernel (one call)", "bound": "hbm",
+                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
             "calls": n_ev}
 
 

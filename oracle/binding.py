@@ -37,7 +37,7 @@ class OracleAttnParams(C.Structure):
         ("n_req", C.c_int32), ("n_slot_rows", C.c_int32), ("packed_queries", C.c_int32),
         ("kv_heads", C.c_int32), ("q_per_kv", C.c_int32), ("head_dim", C.c_int32),
         ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
-        ("sm_scale", C.c_float), ("n_pages", C.c_int64),
+        ("sm_scale", C.c_float), ("kv_format", C.c_int32), ("n_pages", C.c_int64),
         ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
         ("topk_ids", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p), ("out_abs", C.c_void_p),
@@ -219,9 +219,11 @@ class Oracle:
         |V| that scales out's rounding error) as float32 arrays."""
         R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
         MB, K, n_pages = a["max_blocks"], a["topk"], a["n_pages"]
+        kv_format = int(a.get("kv_format", K_BF16))
         q = _arr(a["q"], np.uint16)
-        k = _arr(a["k"], np.uint16)
-        v = _arr(a["v"], np.uint16)
+        kv_dtype = np.uint16 if kv_format == K_BF16 else np.uint8
+        k = _arr(a["k"], kv_dtype)
+        v = _arr(a["v"], kv_dtype)
         req_slot = _arr(a["req_slot"], np.int32)
         bt = _arr(a["block_table"], np.int32)
         row_len = _arr(a["row_len"], np.int32)
@@ -238,6 +240,7 @@ class Oracle:
             setattr(pr, f, int(a[f]))
         pr.head_dim, pr.block_size = 128, 128
         pr.sm_scale = float(a["sm_scale"])
+        pr.kv_format = kv_format
         pr.q, pr.k, pr.v = _ptr(q), _ptr(k), _ptr(v)
         pr.req_slot, pr.block_table, pr.row_len, pr.topk_ids = _ptr(req_slot), _ptr(bt), _ptr(row_len), _ptr(ids)
         pr.out, pr.lse, pr.out_abs = _ptr(out), _ptr(lse), _ptr(oabs)

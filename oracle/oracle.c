@@ -431,10 +431,21 @@ int oracle_step(const oracle_params* p) {
 /* Sparse attention over the selected blocks (readings in oracle.h)         */
 /* ------------------------------------------------------------------------ */
 
+/* Element i of a main K or V pool in its format (fp8: the exact widening of
+ * the e4m3 code; mutant 23 uses the raw byte, the cast dropped). */
+static double kv_value(const oracle_attn_params* p, const void* pool, int64_t i) {
+  if (p->kv_format == ORACLE_K_FP8_E4M3) {
+    uint8_t c = ((const uint8_t*)pool)[i];
+    return MUTANT(23) ? (double)c : oracle_fp8_value(c);
+  }
+  return bf16_value(((const uint16_t*)pool)[i]);
+}
+
 int oracle_sparse_attn(const oracle_attn_params* p) {
   int P, H, G, MB, K, failed = 0;
   int64_t item, n_items;
-  if (!p || p->head_dim != 128 || p->block_size != 128 || p->n_req < 0 || p->packed_queries < 1 ||
+  if (!p || (p->kv_format != ORACLE_K_BF16 && p->kv_format != ORACLE_K_FP8_E4M3)) return -1;
+  if (p->head_dim != 128 || p->block_size != 128 || p->n_req < 0 || p->packed_queries < 1 ||
       p->kv_heads < 1 || p->q_per_kv < 1 || p->max_blocks < 0 || p->topk < 0 || p->n_slot_rows < 0 ||
       p->n_pages < 0 || !(p->sm_scale > 0.0f && isfinite(p->sm_scale)))
     return -1;
@@ -459,8 +470,6 @@ int oracle_sparse_attn(const oracle_attn_params* p) {
     int r = (int)(row / P);
     int hs = MUTANT(19) ? (h + 1) % H : h; /* mutant 19: another head's selection */
     const uint16_t* q = (const uint16_t*)p->q;
-    const uint16_t* kp = (const uint16_t*)p->k;
-    const uint16_t* vp = (const uint16_t*)p->v;
     int64_t qrow = MUTANT(22) ? (row * G + g) * H + h : item; /* mutant 22: heads in the wrong order */
     float* out = p->out + item * 128;
     float* oabs = p->out_abs ? p->out_abs + item * 128 : NULL;
@@ -517,7 +526,7 @@ int oracle_sparse_attn(const oracle_attn_params* p) {
         double s = 0.0;
         int64_t kt = (page * H + h) * 128 + t;
         if (128 * b + t >= len && !MUTANT(17)) break; /* mutant 17: length mask dropped */
-        for (d = 0; d < 128; d++) s += bf16_value(q[qrow * 128 + d]) * bf16_value(kp[kt * 128 + d]);
+        for (d = 0; d < 128; d++) s += bf16_value(q[qrow * 128 + d]) * kv_value(p, p->k, kt * 128 + d);
         sc[n] = MUTANT(16) ? s : (double)p->sm_scale * s; /* mutant 16: scale dropped */
         tok[n] = kt;
         n++;
@@ -540,7 +549,7 @@ int oracle_sparse_attn(const oracle_attn_params* p) {
         l += w;
         for (d = 0; d < 128; d++) {
           /* V is [page][h][token / 32][dim][token % 32]; mutant 21 reads it as [token][dim] */
-          double v = bf16_value(vp[MUTANT(21) ? tok[e] * 128 + d : ((page_h * 4 + tt / 32) * 128 + d) * 32 + tt % 32]);
+          double v = kv_value(p, p->v, MUTANT(21) ? tok[e] * 128 + d : ((page_h * 4 + tt / 32) * 128 + d) * 32 + tt % 32);
           o[d] += w * v;
           oa[d] += w * fabs(v);
         }

@@ -108,7 +108,8 @@ int oracle_fp4_store(const void* staging_bf16, int64_t n_tokens,
  *    listed twice counts once) that the row sees: position 128 b + t < the
  *    row's length, the same causal length as the indexer;
  *  - K and V are paged like the index K (page = block = 128 tokens, the same
- *    request slots and block table), bf16, K as [n_pages][kv_heads][128
+ *    request slots and block table), bf16 or OCP fp8 e4m3 with unit scale
+ *    (the index cache's fp8 format), K as [n_pages][kv_heads][128
  *    tokens][128] and V as [n_pages][kv_heads][4][128 dims][32 tokens] (each
  *    32-token quarter of a page-head transposed);
  *  - out = sum_t softmax_t(sm_scale * q.k_t) v_t and lse = ln sum_t
@@ -128,10 +129,11 @@ typedef struct oracle_attn_params {
   int32_t max_blocks;
   int32_t topk;           /* ids per (draft row, KV head)                       */
   float   sm_scale;
+  int32_t kv_format;      /* ORACLE_K_BF16 or ORACLE_K_FP8_E4M3                  */
   int64_t n_pages;
   const void*    q;        /* bf16 [n_req*P][H][G][128]                          */
-  const void*    k;        /* bf16 [n_pages][H][128 tokens][128]                 */
-  const void*    v;        /* bf16 [n_pages][H][4][128 dims][32 tokens]          */
+  const void*    k;        /* [n_pages][H][128 tokens][128] bf16 or fp8          */
+  const void*    v;        /* [n_pages][H][4][128 dims][32 tokens] bf16 or fp8   */
   const int32_t* req_slot;    /* [n_req]                                         */
   const int32_t* block_table; /* [n_slot_rows][max_blocks]                       */
   const int32_t* row_len;     /* [n_req*P]                                       */

@@ -316,23 +316,28 @@ def config(idx: int, device: str | torch.device = "cpu", local_blocks: int | Non
 # Inputs of the sparse attention that follows selection
 # ---------------------------------------------------------------------------
 POISON_ATTN_V = 1.0e4   # V where no row may look: a leaked token moves its row's output by ~1e4 / n
+POISON_ATTN_V_FP8 = 448.0  # the same for fp8 K/V (the largest e4m3 value)
 
 
 @dataclass
 class AttnInputs:
     q_per_kv: int
     q: torch.Tensor     # bf16 [n_req*P, H, G, 128]: query head g of KV head h of each draft row
-    k: torch.Tensor     # bf16 [n_pages, H, 128 tokens, 128]
-    v: torch.Tensor     # bf16 [n_pages, H, 4, 128 dims, 32 tokens] (each 32-token quarter of a page-head transposed)
+    k: torch.Tensor     # bf16 or float8_e4m3fn [n_pages, H, 128 tokens, 128]
+    v: torch.Tensor     # like k: [n_pages, H, 4, 128 dims, 32 tokens] (each 32-token quarter of a page-head transposed)
     seed: int
+    kv_format: int = K_BF16
 
 
-def make_attn(w: Workload, q_per_kv: int, seed: int | None = None, poison: bool = True) -> AttnInputs:
+def make_attn(w: Workload, q_per_kv: int, seed: int | None = None, poison: bool = True,
+              kv_format: int = K_BF16) -> AttnInputs:
     """Seeded N(0,1) attention queries, keys and values over the workload's
     page pool (the same pages, slots and row lengths as its index K; the KV
-    heads are the workload's gqa index heads).  Gap pages and the tail of
-    each request's last page get K = 0 and V = POISON_ATTN_V, so a token no
-    row may see would move that row's output by far more than any tolerance."""
+    heads are the workload's gqa index heads), K and V stored in bf16 or cast
+    (round to nearest even) to fp8 e4m3.  Gap pages and the tail of each
+    request's last page get K = 0 and a large V (1e4 in bf16, 448 in fp8), so
+    a token no row may see would move that row's output by far more than any
+    tolerance."""
     seed = w.seed + 500 if seed is None else seed
     dev = w.q.device
     H, n_pages = w.gqa, w.n_pages
@@ -340,23 +345,25 @@ def make_attn(w: Workload, q_per_kv: int, seed: int | None = None, poison: bool 
     gen.manual_seed(seed)
     q = torch.empty((w.n_req * w.packed_queries, H, q_per_kv, D), dtype=torch.bfloat16, device=dev)
     _randn_into(q.view(-1, D), gen)
-    k = torch.empty((n_pages, H, BLOCK, D), dtype=torch.bfloat16, device=dev)
+    kv_dtype = torch.bfloat16 if kv_format == K_BF16 else torch.float8_e4m3fn
+    k = torch.empty((n_pages, H, BLOCK, D), dtype=kv_dtype, device=dev)
     _randn_into(k.view(-1, D), gen)
-    v = torch.empty((n_pages, H, 4, D, BLOCK // 4), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((n_pages, H, 4, D, BLOCK // 4), dtype=kv_dtype, device=dev)
     _randn_into(v.view(-1, D), gen)
+    pv = POISON_ATTN_V if kv_format == K_BF16 else POISON_ATTN_V_FP8
     if poison:
         gap = w.extra["gap_pages"]
         if len(gap):
             gi = torch.as_tensor(gap, device=dev)
             k[gi] = 0
-            v[gi] = POISON_ATTN_V
+            v[gi] = pv
         for pg, off in w.extra["tails"]:
             k[pg, :, off:, :] = 0
             for u in range(4):  # tokens >= off of each 32-token quarter
                 start = max(0, off - 32 * u)
                 if start < 32:
-                    v[pg, :, u, :, start:] = POISON_ATTN_V
-    return AttnInputs(q_per_kv=q_per_kv, q=q, k=k, v=v, seed=seed)
+                    v[pg, :, u, :, start:] = pv
+    return AttnInputs(q_per_kv=q_per_kv, q=q, k=k, v=v, seed=seed, kv_format=kv_format)
 
 
 def attn_oracle_args(w: Workload, at: AttnInputs, topk_ids, sm_scale: float) -> dict:
@@ -365,11 +372,14 @@ def attn_oracle_args(w: Workload, at: AttnInputs, topk_ids, sm_scale: float) -> 
     def u16(t):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
+    def kv(t):
+        return u16(t) if at.kv_format == K_BF16 else t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
     ids = topk_ids.detach().cpu().numpy() if isinstance(topk_ids, torch.Tensor) else np.asarray(topk_ids)
     ids = np.ascontiguousarray(ids.astype(np.int32).reshape(w.n_req * w.packed_queries * w.gqa, -1))
     return dict(n_req=w.n_req, n_slot_rows=w.n_slot_rows, packed_queries=w.packed_queries,
                 kv_heads=w.gqa, q_per_kv=at.q_per_kv, max_blocks=w.max_blocks, topk=ids.shape[1],
-                sm_scale=sm_scale, n_pages=w.n_pages, q=u16(at.q), k=u16(at.k), v=u16(at.v),
+                sm_scale=sm_scale, n_pages=w.n_pages, kv_format=at.kv_format, q=u16(at.q), k=kv(at.k), v=kv(at.v),
                 req_slot=w.req_slot.cpu().numpy().astype(np.int32),
                 block_table=w.block_table.cpu().numpy().astype(np.int32),
                 row_len=w.row_len.cpu().numpy().astype(np.int32), topk_ids=ids)

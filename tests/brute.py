@@ -125,6 +125,14 @@ def _attn_rows(a: dict):
                 yield row, h, g, toks, bad
 
 
+def kv_values(a: dict, arr: np.ndarray) -> np.ndarray:
+    """A main K or V pool as float64, decoded by torch (bf16 or float8_e4m3fn)."""
+    if a.get("kv_format", K_BF16) == K_FP8_E4M3:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.uint8)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
+    return bf16_values(arr)
+
+
 def sparse_attn(a: dict) -> dict:
     """fp64 reference: for each query head, scipy's softmax and logsumexp over
     the scaled dots with the visible tokens of its selected blocks (numpy
@@ -132,8 +140,8 @@ def sparse_attn(a: dict) -> dict:
     from scipy.special import logsumexp, softmax
     R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
     q = bf16_values(a["q"]).reshape(R * P, H, G, 128)
-    k = bf16_values(a["k"]).reshape(a["n_pages"], H, 128, 128)
-    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 4, 128, 32)   # [page][h][token / 32][dim][token % 32]
+    k = kv_values(a, a["k"]).reshape(a["n_pages"], H, 128, 128)
+    v = kv_values(a, a["v"]).reshape(a["n_pages"], H, 4, 128, 32)   # [page][h][token / 32][dim][token % 32]
     scale = float(np.float32(a["sm_scale"]))  # the softmax scale crosses the interface as fp32
     out = np.zeros((R * P, H, G, 128))
     lse = np.full((R * P, H, G), -np.inf)
@@ -155,8 +163,8 @@ def sparse_attn_loops(a: dict) -> dict:
     """The same in plain Python loops and math.exp (tiny inputs only)."""
     R, P, H, G = a["n_req"], a["packed_queries"], a["kv_heads"], a["q_per_kv"]
     q = bf16_values(a["q"]).reshape(R * P, H, G, 128).tolist()
-    k = bf16_values(a["k"]).reshape(a["n_pages"], H, 128, 128)
-    v = bf16_values(a["v"]).reshape(a["n_pages"], H, 4, 128, 32)
+    k = kv_values(a, a["k"]).reshape(a["n_pages"], H, 128, 128)
+    v = kv_values(a, a["v"]).reshape(a["n_pages"], H, 4, 128, 32)
     out = [[[[0.0] * 128 for _ in range(G)] for _ in range(H)] for _ in range(R * P)]
     lse = [[[-math.inf] * G for _ in range(H)] for _ in range(R * P)]
     for row, h, g, toks, bad in _attn_rows(a):

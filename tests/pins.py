@@ -660,10 +660,11 @@ def pin_bad_page_ids(o) -> None:
 ATTN_SCALE = float(np.float32(128 ** -0.5))  # an fp32 number, as the interface carries it
 
 
-def attn_workload(seed: int, lens=(0, 130, 700, 1500), P: int = 3, H: int = 2, G: int = 3, pads: int = 1):
+def attn_workload(seed: int, lens=(0, 130, 700, 1500), P: int = 3, H: int = 2, G: int = 3, pads: int = 1,
+                  kv_format: int = W.K_BF16):
     w = W.make(name="attn", R=len(lens), P=P, H=H, k_format=W.K_BF16, req_len=list(lens), topk=4,
                 init_blocks=1, local_blocks=1, seed=seed, pads=pads, pad_len=900)
-    return w, W.make_attn(w, G, seed=seed + 1)
+    return w, W.make_attn(w, G, seed=seed + 1, kv_format=kv_format)
 
 
 def random_selection(w, rng, topk: int, messy: bool = True) -> np.ndarray:
@@ -705,6 +706,22 @@ def pin_attn_bruteforce(o) -> None:
     ids = random_selection(w, np.random.default_rng(612), topk=6)
     a = W.attn_oracle_args(w, at, ids, ATTN_SCALE)
     assert_attn_close(o.sparse_attn(**a), brute.sparse_attn(a), "attn brute force")
+
+
+def pin_attn_fp8(o) -> None:
+    """fp8 e4m3 K/V: the oracle against brute force over torch's float8_e4m3fn
+    decode, and equal (bit for bit) to the bf16 path given the same values
+    widened to bf16, which holds every e4m3 value exactly (3 mantissa bits,
+    exponents 2^-9 to 2^8)."""
+    w, at = attn_workload(615, kv_format=W.K_FP8_E4M3)
+    ids = random_selection(w, np.random.default_rng(616), topk=6)
+    a = W.attn_oracle_args(w, at, ids, ATTN_SCALE)
+    got = o.sparse_attn(**a)
+    assert_attn_close(got, brute.sparse_attn(a), "attn fp8 brute force")
+    wide = W.AttnInputs(at.q_per_kv, at.q, at.k.to(torch.bfloat16), at.v.to(torch.bfloat16), at.seed)
+    ref = o.sparse_attn(**W.attn_oracle_args(w, wide, ids, ATTN_SCALE))
+    for key in ("out", "lse"):
+        assert np.array_equal(got[key], ref[key], equal_nan=True), f"attn fp8 vs widened bf16: {key}"
 
 
 def pin_attn_loops(o) -> None:
@@ -875,6 +892,6 @@ PINS = [
     pin_topk_textbook, pin_topk_bruteforce, pin_topk_invariants, pin_exact_tie, pin_straddle,
     pin_packed_equals_per_row, pin_many_rows_equal_per_row, pin_masking, pin_slot_permutation,
     pin_graph_pads, pin_bad_page_ids,
-    pin_attn_bruteforce, pin_attn_loops, pin_attn_dense, pin_attn_closed_forms, pin_attn_invariants,
+    pin_attn_bruteforce, pin_attn_fp8, pin_attn_loops, pin_attn_dense, pin_attn_closed_forms, pin_attn_invariants,
     pin_scale_rounding, pin_code_rounding,
 ]

@@ -9,8 +9,8 @@ partial-block mask dropped, the sign of zero codes dropped, e2m1 ties away
 from zero, the scale rounded toward zero, nibble order swapped, the init block
 not forced, the lse computed without the softmax scale, a bad page scored -inf) and, for the
 sparse attention over the selected blocks, the scale dropped, the length mask dropped, the
-selection ignored, another head's selection, no normalization, V read untransposed and query heads
-out of order.  Each is compiled into its own copy of the oracle (ORACLE_MUTANT).
+selection ignored, another head's selection, no normalization, V read untransposed, query heads
+out of order and the fp8 K/V cast dropped.  Each is compiled into its own copy of the oracle (ORACLE_MUTANT).
 """
 import pytest
 
@@ -41,6 +41,7 @@ MUTANTS = {
     20: "attention: output not normalized",
     21: "attention: V read untransposed",
     22: "attention: query heads in the wrong order",
+    23: "attention: fp8 K/V cast dropped",
 }
 
 

@@ -55,6 +55,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--attn-q-per-kv", type=int, default=4,
                     help="query heads per KV head of the sparse attention measured after the step "
                          "(0: skip it; packed_queries * this must be <= 16)")
+    ap.add_argument("--attn-kv-format", choices=("bf16", "fp8", "both"), default="both",
+                    help="K/V format(s) of the sparse attention measured after the step")
     ap.add_argument("--score-mode", choices=("max", "lse"), default="max",
                     help="block reduction: max (default) or lse")
     ap.add_argument("--sm-scale", type=float, default=1 / 128 ** 0.5,
@@ -71,17 +73,29 @@ def parse() -> argparse.Namespace:
     return ap.parse_args()
 
 
-def source_digest() -> str:
+# The sources each measured kernel is built from (under csrc/).
+KERNEL_SOURCES = {
+    "score_kernel": ("device.h", "tile.h", "score.hip"),
+    "rows_kernel": ("device.h", "tile.h", "score_rows.hip"),
+    "attn_partial_kernel": ("device.h", "attn.hip"),
+}
+
+
+def source_digest(kernel: str) -> str:
+    """First 16 hex digits of the sha256 of a kernel's sources and the C
+    header: a counter summary taken on other sources is stale."""
     h = hashlib.sha256()
-    for f in sorted((ROOT / "sparse_attention_lightning_amd" / "csrc").glob("*")):
+    csrc = ROOT / "sparse_attention_lightning_amd" / "csrc"
+    for f in [csrc / n for n in KERNEL_SOURCES[kernel]] + [ROOT / "include" / "idx.h"]:
         h.update(f.read_bytes())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload: str, digest: str):
+def traffic_from_profiles(kernel: str, fmt: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel sources (else None)."""
-    f = ROOT / "profiles" / f"{kernel}_{workload}_traffic.md"
+    on the kernel's current sources (else None)."""
+    digest = source_digest(kernel)
+    f = ROOT / "profiles" / f"{kernel}_{fmt}_{workload}_traffic.md"
     if not f.exists():
         return None
     text = f.read_text()
@@ -217,12 +231,10 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps if flush is None else float(np.mean(step_ms))
     score_mean_s = float(np.mean(score_ms)) / 1e3
     achieved = score_bytes / score_mean_s / 1e9
-    digest = source_digest()
     fmt_name = {W.K_BF16: "bf16", W.K_FP8_E4M3: "fp8", W.K_NVFP4: "nvfp4"}[w.k_format]
     # the committed counter profiles are of the max reduction
     kname = "score_kernel" if P * H <= 16 else "rows_kernel"
-    traffic = (traffic_from_profiles(f"{kname}_{fmt_name}", w.name, digest)
-               if args.score_mode == "max" else None)
+    traffic = traffic_from_profiles(kname, fmt_name, w.name) if args.score_mode == "max" else None
 
     if P * H <= 16:
         roofline = {"kernel": "score_kernel", "bound": "hbm", "achieved": round(achieved, 1),
@@ -276,8 +288,11 @@ def main() -> int:
         line["fp4_store_step_tokens"] = int(step_staging.shape[0])
         line["fp4_store_pool"] = pool_store
     if args.attn_q_per_kv and P * args.attn_q_per_kv <= 16:
-        line["sparse_attn"] = bench_attn(w, outs["topk_ids"], args.attn_q_per_kv, flush, stream,
-                                         n_ev=max(10, min(args.steps, 50)))
+        for kvf in ("bf16", "fp8"):
+            if args.attn_kv_format in (kvf, "both"):
+                key = "sparse_attn" if kvf == "bf16" else "sparse_attn_fp8kv"
+                line[key] = bench_attn(w, outs["topk_ids"], args.attn_q_per_kv, kvf, flush, stream,
+                                       n_ev=max(10, min(args.steps, 50)))
     if not args.no_read_ceiling and P * H <= 16:
         line["hbm_read_ceiling"] = read_ceiling(w, flush, stream)
         line["score_frac_of_page_gather"] = round(achieved / line["hbm_read_ceiling"]["page_gather_GBps"], 4)
@@ -288,21 +303,22 @@ def main() -> int:
     return 0
 
 
-def bench_attn(w, topk_ids, G: int, flush, stream, n_ev: int) -> dict:
-    """The sparse attention over the blocks the step just selected: bf16 K
-    and V pools of the workload's page count, G query heads per KV head,
-    softmax scale 1/sqrt(128).  Timed with HIP events around each call (its
-    two launches), mean of ``n_ev`` calls after 3 warm-ups.  Algorithmic bytes:
-    for every (request, KV head), the K and V of each block in the union of
-    its draft rows' selections, up to the longest of those rows' visible
-    tokens in it (256 + 256 B a token), plus queries, ids and outputs."""
+def bench_attn(w, topk_ids, G: int, kvf: str, flush, stream, n_ev: int) -> dict:
+    """The sparse attention over the blocks the step just selected: K and V
+    pools (bf16 or fp8 e4m3, ``kvf``) of the workload's page count, G query
+    heads per KV head, softmax scale 1/sqrt(128).  Timed with HIP events
+    around each call (one or two launches), mean of ``n_ev`` calls after 3
+    warm-ups.  Algorithmic bytes: for every (request, KV head), the K and V
+    of each block in the union of its draft rows' selections, up to the
+    longest of those rows' visible tokens in it (2 x 256 B a token in bf16,
+    2 x 128 B in fp8), plus queries, ids and outputs."""
     import numpy as np
     import torch
 
     from sparse_attention_lightning_amd import idx as I
     from sparse_attention_lightning_amd import workloads as W
 
-    at = W.make_attn(w, G)
+    at = W.make_attn(w, G, kv_format=W.K_BF16 if kvf == "bf16" else W.K_FP8_E4M3)
     P, H, R = w.packed_queries, w.gqa, w.n_req
     out = torch.empty_like(at.q)
     lse = torch.empty(at.q.shape[:3], dtype=torch.float32, device=at.q.device)
@@ -340,15 +356,16 @@ def bench_attn(w, topk_ids, G: int, flush, stream, n_ev: int) -> dict:
             union += len(best)
             tokens += sum(best.values())
     rows = R * P * H * G
-    nbytes = tokens * 512 + rows * 256 * 2 + rows * 4 + ids.size * 4
+    kv_token = 512 if kvf == "bf16" else 256
+    nbytes = tokens * kv_token + rows * 256 * 2 + rows * 4 + ids.size * 4
     us = float(np.mean(ms)) * 1e3
     gbps = nbytes / (us / 1e6) / 1e9
     del at, out, lse, p
     torch.cuda.empty_cache()
-    traffic = traffic_from_profiles("attn_partial_kernel_bf16", w.name, source_digest())
+    traffic = traffic_from_profiles("attn_partial_kernel", kvf, w.name)
     return {"us": round(us, 2), "us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(ms, [10, 50, 90])],
-            "q_per_kv": G, "kv_heads": H, "query_heads": rows, "selected_blocks": int(selected),
-            "union_blocks": int(union), "kv_bytes": int(tokens * 512), "algorithmic_bytes": int(nbytes),
+            "kv_format": kvf, "q_per_kv": G, "kv_heads": H, "query_heads": rows, "selected_blocks": int(selected),
+            "union_blocks": int(union), "kv_bytes": int(tokens * kv_token), "algorithmic_bytes": int(nbytes),
             "achieved_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "roofline": {"kernel": "attn_partial_kernel + attn_combine_kernel (one call)", "bound": "hbm",
                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

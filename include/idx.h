@@ -207,7 +207,9 @@ const char* idx_last_error(void);
  *    any int32 list: ids < 0, ids past the row's blocks and repeats are
  *    ignored) that the row sees: position 128 b + t < row_len[row j];
  *  - K and V are paged like the index K (page = block = 128 tokens, the same
- *    req_slot and block_table), bf16;
+ *    req_slot and block_table), both bf16 or both OCP fp8 e4m3fn with unit
+ *    scale (kv_format; the index cache's fp8 format), fp8 widened exactly to
+ *    bf16 for the products;
  *  - out = sum_t softmax_t(sm_scale q.k_t) v_t (fp32 accumulation, stored as
  *    bf16), lse = ln sum_t exp(sm_scale q.k_t) (fp32).  A row that sees no
  *    selected token (length 0, nothing selected, graph pad) gets out = 0 and
@@ -216,13 +218,13 @@ const char* idx_last_error(void);
  *
  * Shapes, with P = packed_queries, H = kv_heads, G = q_per_kv, R = n_req:
  *   q        bf16 [R*P][H][G][128]
- *   k        bf16 [n_pages][H][128 tokens][128]: token t of page p, head h is
- *            k[p][h][t]
- *   v        bf16 [n_pages][H][4][128 dims][32 tokens]: each 32-token quarter
- *            of a page-head's V transposed, token t, dimension d at
+ *   k        [n_pages][H][128 tokens][128] of kv_format: token t of page p,
+ *            head h is k[p][h][t]
+ *   v        [n_pages][H][4][128 dims][32 tokens] of kv_format: each 32-token
+ *            quarter of a page-head's V transposed, token t, dimension d at
  *            v[p][h][t / 32][d][t % 32] (8 consecutive tokens of a dimension
- *            are one 16-byte load for the PV product, and the 16 dimensions a
- *            load instruction covers are 1 KB in a row)
+ *            are one load for the PV product, and the 16 dimensions a load
+ *            instruction covers are whole lines in a row)
  *   req_slot, block_table, row_len: as idx_params
  *   topk_ids int32 [R*P][H][topk]
  *   out      bf16 [R*P][H][G][128];  lse fp32 [R*P][H][G]
@@ -250,6 +252,7 @@ typedef struct idx_attn_params {
   int32_t max_blocks;     /* columns of block_table, 0..IDX_MAX_BLOCKS       */
   int32_t topk;           /* ids per (draft row, KV head), >= 1              */
   float sm_scale;         /* softmax scale, finite and > 0                   */
+  int32_t kv_format;      /* IDX_K_BF16 or IDX_K_FP8_E4M3, K and V alike     */
   int64_t n_pages;        /* pages in the K and V pools, >= 0                */
   int64_t workspace_bytes;
   const void* q;
@@ -271,8 +274,8 @@ int64_t idx_sparse_attn_workspace(const idx_attn_params* p);
 /* Sparse attention over the selected blocks (on `stream`: the splits'
  * partials, then their merge; one launch when nothing is split).  Refusals as the other calls, plus
  * IDX_E_PACK for P * G > IDX_ATTN_MAX_ROWS, IDX_E_TOPK for P * topk >
- * IDX_ATTN_MAX_IDS, IDX_E_MODE for a bad sm_scale and IDX_E_SHAPE for a
- * workspace below idx_sparse_attn_workspace(p). */
+ * IDX_ATTN_MAX_IDS, IDX_E_MODE for a bad sm_scale, IDX_E_FORMAT for another
+ * kv_format and IDX_E_SHAPE for a workspace below idx_sparse_attn_workspace(p). */
 int idx_sparse_attn(const idx_attn_params* p, void* stream);
 
 /* Largest n_req * packed_queries * gqa * max_blocks of idx_step_noalloc: the

@@ -142,6 +142,8 @@ int check_attn(const idx_attn_params* p) {
                 p->topk, p->packed_queries);
   if (!(p->sm_scale > 0.0f && p->sm_scale <= 3.402823466e38f))
     return fail(IDX_E_MODE, "sm_scale must be finite and > 0 (got %g)", (double)p->sm_scale);
+  if (p->kv_format != IDX_K_BF16 && p->kv_format != IDX_K_FP8_E4M3)
+    return fail(IDX_E_FORMAT, "kv_format must be IDX_K_BF16 or IDX_K_FP8_E4M3 (got %d)", p->kv_format);
   return IDX_OK;
 }
 
@@ -205,6 +207,7 @@ int idx_sparse_attn(const idx_attn_params* p, void* stream) {
   a.max_blocks = p->max_blocks;
   a.topk = p->topk;
   a.splits = splits;
+  a.kv_format = p->kv_format;
   a.c2 = p->sm_scale * 1.44269504088896341f;
   return launched(idx::launch_attn(a, (hipStream_t)stream), "sparse attention");
 }

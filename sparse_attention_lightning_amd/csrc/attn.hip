@@ -20,21 +20,30 @@
 //
 // Per 32-token unit of a block, per wave:
 //   S^T = K Q^T   MFMA 16x16x32 bf16 with K as the A operand: lane (m, gq)
-//                 loads 16 bytes of token pi_c(m)'s row, so lane (n, gq) ends
-//                 with row n's scores of tokens 8 gq .. 8 gq + 7 (two 16-token
-//                 halves c = 0, 1, pi_c(m) = 8 (m / 4) + 4 c + m % 4);
+//                 loads its k positions of token pi_c(m)'s row, so lane (n, gq)
+//                 ends with row n's scores of tokens 8 gq .. 8 gq + 7 (two
+//                 16-token halves c = 0, 1, pi_c(m) = 8 (m / 4) + 4 c + m % 4);
 //   O^T += V^T P^T  with P^T as the B operand, which is exactly what each lane
 //                 holds (its row's probabilities of those 8 tokens, in bf16),
-//                 and V^T as the A operand, read as 16 contiguous bytes (8
-//                 tokens of one dimension) from the unit's transposed V: each
-//                 32-token quarter of a page-head is stored [128 dims][32
-//                 tokens], so one load instruction (16 dimensions) covers 1 KB
-//                 of whole lines.
+//                 and V^T as the A operand, read as 8 contiguous tokens of one
+//                 dimension from the unit's transposed V: each 32-token
+//                 quarter of a page-head is stored [128 dims][32 tokens], so
+//                 one load instruction (16 dimensions) covers whole lines.
 // So K and V go from HBM straight into operand registers, and the rescale of
 // the running output is local to each lane (lane n holds row n's output
 // dimensions 16 dt + 4 gq + i).  Loads go through per-page buffer descriptors;
 // a page outside the pool gets an empty one (reads nothing) and makes every
 // row that sees it NaN.
+//
+// K and V in bf16 or in fp8 e4m3 (unit scale, the index cache's fp8 format).
+// fp8 bytes are widened exactly to bf16 in registers (every e4m3 value is a
+// bf16 value) and go through the same bf16 products, so only the bytes read
+// change.  Which head dimensions a lane feeds at k-step s (Q read to match;
+// the dot product does not depend on the order of its terms):
+//   bf16  K row 256 B, four 16-byte loads:  d = 32 s + 8 gq .. + 8
+//   fp8   K row 128 B, two 16-byte loads at bytes 16 gq and 64 + 16 gq:
+//         d = 64 (s / 2) + 16 gq + 8 (s % 2) .. + 8
+// and V's 8 tokens of a dimension are 16 bytes (bf16) or 8 bytes (fp8).
 #include <algorithm>
 #include <atomic>
 
@@ -44,7 +53,10 @@ namespace idx {
 
 // Tuning knobs (compile-time; neither changes what is computed).
 #ifndef IDX_ATTN_RING
-#define IDX_ATTN_RING 3      // 32-token units in registers per wave (64 registers each)
+#define IDX_ATTN_RING 3      // 32-token units in registers per wave, bf16 K/V (64 registers each)
+#endif
+#ifndef IDX_ATTN_RING_FP8
+#define IDX_ATTN_RING_FP8 4  // the same for fp8 K/V (32 registers each)
 #endif
 #ifndef IDX_ATTN_MIN_WGS
 #define IDX_ATTN_MIN_WGS 1   // workgroups a CU must hold at once (sets each wave's register budget)
@@ -53,20 +65,66 @@ namespace idx {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnBitWords = IDX_MAX_BLOCKS / 32;
-constexpr int kAttnRing = IDX_ATTN_RING;
 constexpr int kPartFloats = 132;  // per row of a partial: output [0, 128), max (log2 units), sum, pad
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
+// One page-head of K (and of V): 128 tokens x 128 dimensions.
+template <int KVF>
+constexpr int kPageHeadBytes = KVF == IDX_K_BF16 ? 32768 : 16384;
+
+template <int KVF>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const uint8_t* pool, int64_t page_head, bool ok) {
-  const uint8_t* base = ok ? pool + page_head * 32768 : pool;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, ok ? 32768 : 0, 0x00020000);
+  const uint8_t* base = ok ? pool + page_head * kPageHeadBytes<KVF> : pool;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, ok ? kPageHeadBytes<KVF> : 0,
+                                           0x00020000);
 }
 
-struct AttnUnit {
+// One 32-token unit of a block in a lane's registers.
+template <int KVF>
+struct AttnUnit;
+template <>
+struct AttnUnit<IDX_K_BF16> {
+  static constexpr int kRing = IDX_ATTN_RING;
   u32x4 k[2][4];  // [half c][k-step s]
   u32x4 v[8];     // [dim tile dt]
 };
+template <>
+struct AttnUnit<IDX_K_FP8_E4M3> {
+  static constexpr int kRing = IDX_ATTN_RING_FP8;
+  u32x4 k[2][2];  // [half c][16-byte load i]: k-steps 2 i, 2 i + 1
+  u32x2 v[8];     // [dim tile dt]
+};
+
+// Eight e4m3 bytes (lo: the first four) widened to bf16 (exact, scale 1).
+__device__ __forceinline__ bf16x8_t widen_fp8x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The K operand of half c, k-step s, and the V operand of dimension tile dt.
+__device__ __forceinline__ bf16x8_t k_operand(const AttnUnit<IDX_K_BF16>& w, int c, int s) {
+  return __builtin_bit_cast(bf16x8_t, w.k[c][s]);
+}
+__device__ __forceinline__ bf16x8_t k_operand(const AttnUnit<IDX_K_FP8_E4M3>& w, int c, int s) {
+  const u32x4 x = w.k[c][s >> 1];
+  return (s & 1) ? widen_fp8x8(x.z, x.w) : widen_fp8x8(x.x, x.y);
+}
+__device__ __forceinline__ bf16x8_t v_operand(const AttnUnit<IDX_K_BF16>& w, int dt) {
+  return __builtin_bit_cast(bf16x8_t, w.v[dt]);
+}
+__device__ __forceinline__ bf16x8_t v_operand(const AttnUnit<IDX_K_FP8_E4M3>& w, int dt) {
+  return widen_fp8x8(w.v[dt].x, w.v[dt].y);
+}
+
+// First head dimension of the 8 that a lane of k-group gq feeds at k-step s.
+template <int KVF>
+__device__ __forceinline__ int attn_d0(int s, int gq) {
+  return KVF == IDX_K_BF16 ? 32 * s + 8 * gq : 64 * (s >> 1) + 16 * gq + 8 * (s & 1);
+}
 
 // Row `row` (of the item's P x G) of item (request r, KV head h): output
 // dimensions 8 c8 .. + 8 from the unnormalized sum acc8 over all its tokens,
@@ -95,7 +153,10 @@ __device__ __forceinline__ void attn_finalize(const AttnArgs& a, int r, int h, i
   if (c8 == 0) a.lse[orow] = lse;
 }
 
+template <int KVF>
 __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_kernel(const AttnArgs a) {
+  typedef AttnUnit<KVF> Unit;
+  constexpr int kRing = Unit::kRing;
   __shared__ int32_t list_id[IDX_ATTN_MAX_IDS];
   __shared__ int32_t list_page[IDX_ATTN_MAX_IDS];
   __shared__ uint16_t list_mask[IDX_ATTN_MAX_IDS];
@@ -165,7 +226,7 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + 32 * s + 8 * gq);
+    if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + attn_d0<KVF>(s, gq));
     qf[s] = __builtin_bit_cast(bf16x8_t, w);
   }
   const int my_blocks = (hi - lo - wave + kAttnWaves - 1) / kAttnWaves;  // may be <= 0
@@ -179,28 +240,41 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
   // token of K row this lane loads for half c: pi_c(n)
   const int tk0 = 8 * (n >> 2) + (n & 3);
 
-  auto issue = [&](AttnUnit& w, int U_) {
+  auto issue = [&](Unit& w, int U_) {
     const int x = lo + wave + kAttnWaves * (U_ >> 2);
     const bool exists = U_ < n_units;
     const int page = exists ? (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]) : -1;
     const bool ok = exists && page >= 0 && page < a.n_pages;
     const int64_t ph = (int64_t)(ok ? page : 0) * H + h;
-    const __amdgpu_buffer_rsrc_t rk = attn_rsrc(a.k, ph, ok);
-    const __amdgpu_buffer_rsrc_t rv = attn_rsrc(a.v, ph, ok);
+    const __amdgpu_buffer_rsrc_t rk = attn_rsrc<KVF>(a.k, ph, ok);
+    const __amdgpu_buffer_rsrc_t rv = attn_rsrc<KVF>(a.v, ph, ok);
     const int sub = U_ & 3;
+    if constexpr (KVF == IDX_K_BF16) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        w.k[c][s] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (32 * sub + tk0 + 4 * c) * 256 + 64 * s + 16 * gq, 0, 0));
+        for (int s = 0; s < 4; ++s)
+          w.k[c][s] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (32 * sub + tk0 + 4 * c) * 256 + 64 * s + 16 * gq, 0, 0));
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)  // V quarter `sub`: [128 dims][32 tokens], 64 B a dimension
-      w.v[dt] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 8192 * sub + (16 * dt + n) * 64 + 16 * gq, 0, 0));
+      for (int dt = 0; dt < 8; ++dt)  // V quarter `sub`: [128 dims][32 tokens], 64 B a dimension
+        w.v[dt] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 8192 * sub + (16 * dt + n) * 64 + 16 * gq, 0, 0));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          w.k[c][i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (32 * sub + tk0 + 4 * c) * 128 + 64 * i + 16 * gq, 0, 0));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)  // V quarter `sub`: [128 dims][32 tokens], 32 B a dimension
+        w.v[dt] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 4096 * sub + (16 * dt + n) * 32 + 8 * gq, 0, 0));
+    }
   };
 
-  auto compute = [&](const AttnUnit& w, int U_) {
+  auto compute = [&](const Unit& w, int U_) {
     if (U_ >= n_units) return;
     const int x = lo + wave + kAttnWaves * (U_ >> 2);
     const int b = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_id[x]);
@@ -215,7 +289,7 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
       acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w.k[c][s]), qf[s], acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(w, c, s), qf[s], acc[c], 0, 0, 0);
     }
     // this lane: row n, tokens 8 gq + 4 c + i of the unit
     const int pos0 = 128 * b + 32 * (U_ & 3) + 8 * gq;
@@ -247,18 +321,18 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       o[dt] *= alpha;
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w.v[dt]), pb, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(w, dt), pb, o[dt], 0, 0, 0);
     }
   };
 
   {
-    AttnUnit ring[kAttnRing];
+    Unit ring[kRing];
 #pragma unroll
-    for (int k = 0; k < kAttnRing - 1; ++k) issue(ring[k], k);
-    for (int U0 = 0; U0 < n_units; U0 += kAttnRing) {
+    for (int k = 0; k < kRing - 1; ++k) issue(ring[k], k);
+    for (int U0 = 0; U0 < n_units; U0 += kRing) {
 #pragma unroll
-      for (int k = 0; k < kAttnRing; ++k) {
-        issue(ring[(k + kAttnRing - 1) % kAttnRing], U0 + k + kAttnRing - 1);
+      for (int k = 0; k < kRing; ++k) {
+        issue(ring[(k + kRing - 1) % kRing], U0 + k + kRing - 1);
         compute(ring[k], U0 + k);
       }
     }
@@ -346,6 +420,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnAr
 }
 
 namespace {
+// Both instantiations have the same register and LDS budget (one workgroup
+// a CU); the bf16 one is asked.
 int attn_resident_workgroups() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -354,7 +430,7 @@ int attn_resident_workgroups() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(attn_partial_kernel),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(attn_partial_kernel<IDX_K_BF16>),
                                                    kAttnThreads, 0) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   cache[dev].store(cus * per_cu, std::memory_order_relaxed);
@@ -375,7 +451,12 @@ int attn_splits(int64_t items, int64_t max_union) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.n_req * a.H;
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0, stream, a);
+  if (a.kv_format == IDX_K_FP8_E4M3)
+    hipLaunchKernelGGL(attn_partial_kernel<IDX_K_FP8_E4M3>, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(attn_partial_kernel<IDX_K_BF16>, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0,
+                       stream, a);
   if (a.splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)items), dim3(kAttnThreads), 0, stream, a);
   return hipGetLastError();

@@ -14,6 +14,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 128;   // tokens per block = tokens per page
@@ -41,8 +42,8 @@ struct StepArgs {
 // the merge).
 struct AttnArgs {
   const uint16_t* q;          // bf16 [R*P][H][G][128]
-  const uint8_t* k;           // bf16 [n_pages][H][128 tokens][128]
-  const uint8_t* v;           // bf16 [n_pages][H][4][128 dims][32 tokens]
+  const uint8_t* k;           // bf16 or fp8 [n_pages][H][128 tokens][128]
+  const uint8_t* v;           // bf16 or fp8 [n_pages][H][4][128 dims][32 tokens]
   const int32_t* req_slot;
   const int32_t* block_table;
   const int32_t* row_len;
@@ -52,6 +53,7 @@ struct AttnArgs {
   float* ws;                  // partials: [R*H][splits][16 rows][132]
   int64_t n_pages;
   int32_t n_req, n_slot_rows, P, H, G, max_blocks, topk, splits;
+  int32_t kv_format;          // IDX_K_BF16 or IDX_K_FP8_E4M3 (K and V alike)
   float c2;                   // sm_scale * log2(e)
 };
 // Workgroups of the partial kernel per (request, KV head) item, for `items`

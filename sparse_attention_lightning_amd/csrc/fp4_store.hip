@@ -23,7 +23,6 @@ namespace idx {
 #endif
 
 constexpr int kStoreThreads = 256;
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t e4m3_rne_satfinite(float t) {
   if (!(t < 448.0f)) return 0x7Eu;  // clamp (NaN too: unspecified)

@@ -60,7 +60,8 @@ class IdxAttnParams(C.Structure):
         ("n_req", C.c_int32), ("n_slot_rows", C.c_int32), ("packed_queries", C.c_int32),
         ("kv_heads", C.c_int32), ("q_per_kv", C.c_int32), ("head_dim", C.c_int32),
         ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("topk", C.c_int32),
-        ("sm_scale", C.c_float), ("n_pages", C.c_int64), ("workspace_bytes", C.c_int64),
+        ("sm_scale", C.c_float), ("kv_format", C.c_int32), ("n_pages", C.c_int64),
+        ("workspace_bytes", C.c_int64),
         ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
         ("topk_ids", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p), ("workspace", C.c_void_p),
@@ -278,12 +279,14 @@ def idx_fp4_store(staging: torch.Tensor, slot_mapping: torch.Tensor, payload: to
 def make_attn_params(*, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, req_slot: torch.Tensor,
                      block_table: torch.Tensor, row_len: torch.Tensor, topk_ids: torch.Tensor,
                      out: torch.Tensor, lse: torch.Tensor, sm_scale: float,
-                     workspace: torch.Tensor | None = None) -> IdxAttnParams:
+                     workspace: torch.Tensor | None = None, kv_format: int | None = None) -> IdxAttnParams:
     """Parameter block of the sparse attention from tensors: q [R*P, H, G,
-    128] bf16, k [n_pages, H, 128, 128] bf16, v [n_pages, H, 4, 128 dims, 32
-    tokens] bf16, topk_ids [R*P*H, topk] (or [R*P, H, topk]) int32, out like
-    q, lse [R*P, H, G] fp32.  Without ``workspace`` one of the size the
-    library asks for is allocated here (kept alive by the returned object)."""
+    128] bf16, k [n_pages, H, 128, 128] and v [n_pages, H, 4, 128 dims, 32
+    tokens] both bf16 or both fp8 e4m3 (float8_e4m3fn, or uint8 with
+    ``kv_format`` given), topk_ids [R*P*H, topk] (or [R*P, H, topk]) int32,
+    out like q, lse [R*P, H, G] fp32.  Without ``workspace`` one of the size
+    the library asks for is allocated here (kept alive by the returned
+    object)."""
     if q.dim() != 4 or q.shape[-1] != 128:
         raise ValueError("q must be [R*P, H, G, 128]")
     if k.dim() != 4 or k.shape[2:] != (128, 128) or v.shape != (k.shape[0], k.shape[1], 4, 128, 32):
@@ -305,9 +308,14 @@ def make_attn_params(*, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, req_s
     p.head_dim = p.block_size = 128
     p.n_slot_rows, p.max_blocks = block_table.shape[0], block_table.shape[1]
     p.topk, p.sm_scale, p.n_pages = topk, sm_scale, k.shape[0]
+    if kv_format is None:
+        kv_format = IDX_K_FP8_E4M3 if k.dtype == torch.float8_e4m3fn else IDX_K_BF16
+    if kv_format not in (IDX_K_BF16, IDX_K_FP8_E4M3) or v.dtype != k.dtype:
+        raise ValueError("k and v must share one format: bf16 or fp8 e4m3")
+    p.kv_format = kv_format
     p.q = _dev(q, "q", (torch.bfloat16,))
-    p.k = _dev(k, "k", (torch.bfloat16,))
-    p.v = _dev(v, "v", (torch.bfloat16,))
+    p.k = _dev(k, "k", _K_DTYPES[kv_format])
+    p.v = _dev(v, "v", _K_DTYPES[kv_format])
     p.req_slot = _dev(req_slot, "req_slot", (torch.int32,))
     p.block_table = _dev(block_table, "block_table", (torch.int32,))
     p.row_len = _dev(row_len, "row_len", (torch.int32,))

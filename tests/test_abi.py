@@ -158,6 +158,8 @@ ATTN_REFUSALS = [
     ("sm_scale", 0.0, I.IDX_E_MODE),
     ("sm_scale", float("inf"), I.IDX_E_MODE),
     ("sm_scale", float("nan"), I.IDX_E_MODE),
+    ("kv_format", I.IDX_K_NVFP4, I.IDX_E_FORMAT),
+    ("kv_format", -1, I.IDX_E_FORMAT),
     ("q", None, I.IDX_E_NULL),
     ("v", None, I.IDX_E_NULL),
     ("topk_ids", None, I.IDX_E_NULL),

@@ -1,5 +1,5 @@
 """Sparse attention over the selected blocks: the HIP path (through the C-ABI)
-against the CPU oracle on an MI355X.
+against the CPU oracle on an MI355X, with K/V in bf16 and in fp8 e4m3.
 
 Acceptance (derived from the arithmetic: P in bf16 for the PV product, out
 rounded to bf16, scores in fp32):
@@ -25,6 +25,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not Hn.gpu_ok(), reason="needs an MI355X (gfx950)")]
 
 SCALE = pins.ATTN_SCALE
+KVF = pytest.mark.parametrize("kvf", [W.K_BF16, W.K_FP8_E4M3], ids=["bf16kv", "fp8kv"])
 
 
 def say(*a):
@@ -74,13 +75,14 @@ SHAPES = [  # (P, H, G, lens, topk, pads)
 ]
 
 
+@KVF
 @pytest.mark.parametrize("shape", range(len(SHAPES)))
-def test_attn_small_shapes(oracle, shape):
+def test_attn_small_shapes(oracle, shape, kvf):
     P, H, G, lens, topk, pads = SHAPES[shape]
-    say("attn small", SHAPES[shape])
+    say("attn small", SHAPES[shape], "kv format", kvf)
     w = W.make(name="attn", R=len(lens), P=P, H=H, k_format=W.K_BF16, req_len=lens, topk=topk, init_blocks=1,
                local_blocks=1, seed=700 + shape, pads=pads, pad_len=4000, device="cuda")
-    at = W.make_attn(w, G)
+    at = W.make_attn(w, G, kv_format=kvf)
     wc = W.make(name="attn", R=len(lens), P=P, H=H, k_format=W.K_BF16, req_len=lens, topk=topk, init_blocks=1,
                 local_blocks=1, seed=700 + shape, pads=pads, pad_len=4000)  # CPU copy of the tables
     ids = pins.random_selection(wc, np.random.default_rng(710 + shape), topk=topk)
@@ -88,13 +90,14 @@ def test_attn_small_shapes(oracle, shape):
     assert_attn(gpu_attn(w, at, ids), oracle.sparse_attn(**a), f"shape {shape}")
 
 
-def test_attn_after_the_step(oracle):
+@KVF
+def test_attn_after_the_step(oracle, kvf):
     """The indexer step's own selection feeds the attention (the verify
     pipeline: score -> top-k -> attention)."""
-    say("attn after idx_step")
+    say("attn after idx_step, kv format", kvf)
     w = W.make(name="pipe", R=4, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[3000, 9000, 200, 17000], topk=16,
                init_blocks=1, local_blocks=2, seed=720, pads=1, pad_len=5000, device="cuda")
-    at = W.make_attn(w, 4)
+    at = W.make_attn(w, 4, kv_format=kvf)
     outs = Hn.gpu_outputs(w)
     I.idx_step(Hn.gpu_params(w, outs))
     g = gpu_attn(w, at, outs["topk_ids"])
@@ -115,17 +118,18 @@ def test_attn_scales(oracle, scale):
                 f"scale {scale}")
 
 
-def test_attn_bad_pages_and_empty_rows(oracle):
+@KVF
+def test_attn_bad_pages_and_empty_rows(oracle, kvf):
     """A selected block on a page outside the pool makes exactly the rows
     that see it NaN; rows of length 0, rows selecting nothing and graph pads
     get 0 and -inf."""
-    say("attn bad pages")
+    say("attn bad pages, kv format", kvf)
     lens = [700, 1500, 0, 300]
     w = W.make(name="bad", R=4, P=4, H=2, k_format=W.K_BF16, req_len=lens, topk=6, init_blocks=1,
                local_blocks=1, seed=740, pads=1, pad_len=900, device="cuda")
     wc = W.make(name="bad", R=4, P=4, H=2, k_format=W.K_BF16, req_len=lens, topk=6, init_blocks=1,
                 local_blocks=1, seed=740, pads=1, pad_len=900)
-    at = W.make_attn(w, 3)
+    at = W.make_attn(w, 3, kv_format=kvf)
     ids = pins.random_selection(wc, np.random.default_rng(741), topk=6)
     ids[3 * 4 + 1, 0] = -1  # request 3, draft row 1, head 0 selects nothing
     s1 = int(wc.req_slot[1])
@@ -154,15 +158,16 @@ def test_attn_degenerate(oracle):
     assert (g["out"] == 0).all() and np.isneginf(g["lse"]).all()
 
 
-def test_attn_repeated_calls_are_identical(oracle):
+@KVF
+def test_attn_repeated_calls_are_identical(oracle, kvf):
     """The same inputs give bit-identical outputs over repeated launches (no
     state is carried in the workspace between calls)."""
-    say("attn repeat")
+    say("attn repeat, kv format", kvf)
     w = W.make(name="rep", R=3, P=4, H=4, k_format=W.K_BF16, req_len=[4000, 800, 12000], topk=12, init_blocks=1,
                local_blocks=2, seed=760, device="cuda")
     wc = W.make(name="rep", R=3, P=4, H=4, k_format=W.K_BF16, req_len=[4000, 800, 12000], topk=12, init_blocks=1,
                 local_blocks=2, seed=760)
-    at = W.make_attn(w, 4)
+    at = W.make_attn(w, 4, kv_format=kvf)
     ids = pins.random_selection(wc, np.random.default_rng(761), topk=12)
     first = gpu_attn(w, at, ids)
     for _ in range(20):
@@ -195,8 +200,9 @@ def test_attn_unsplit_batch(oracle):
     assert_attn(gpu_attn(w, at, ids), oracle.sparse_attn(**W.attn_oracle_args(w, at, ids, SCALE)), "unsplit")
 
 
+@KVF
 @pytest.mark.parametrize("case", range(12))
-def test_attn_random_shapes(oracle, case):
+def test_attn_random_shapes(oracle, case, kvf):
     """Seeded random shapes: draft rows, KV heads, query heads a KV head
     (P G <= 16), request lengths (some 0, some straddling block ends),
     selection sizes, graph pads, repeated and ignored ids."""
@@ -208,28 +214,29 @@ def test_attn_random_shapes(oracle, case):
     lens = [int(x) for x in rng.choice([0, 1, 127, 128, 129, 700, 2048, 5000, 20000], size=R)]
     topk = int(rng.integers(4, 40))
     pads = int(rng.integers(0, 3))
-    say("attn random", case, dict(P=P, G=G, H=H, R=R, lens=lens, topk=topk, pads=pads))
+    say("attn random", case, dict(P=P, G=G, H=H, R=R, lens=lens, topk=topk, pads=pads, kv_format=kvf))
     kw = dict(name="rand", R=R, P=P, H=H, k_format=W.K_BF16, req_len=lens, topk=topk, init_blocks=1,
               local_blocks=1, seed=910 + case, pads=pads, pad_len=int(rng.integers(1, 3000)))
     w = W.make(**kw, device="cuda")
     wc = W.make(**kw)
-    at = W.make_attn(w, G)
+    at = W.make_attn(w, G, kv_format=kvf)
     ids = pins.random_selection(wc, np.random.default_rng(920 + case), topk=topk)
     scale = float(np.float32(rng.choice([0.05, SCALE, 0.5])))
     assert_attn(gpu_attn(w, at, ids, scale), oracle.sparse_attn(**W.attn_oracle_args(w, at, ids, scale)),
                 f"random case {case}")
 
 
-def test_attn_graph_replays(oracle):
+@KVF
+def test_attn_graph_replays(oracle, kvf):
     """idx_sparse_attn captured once in a HIP graph and replayed after new
     queries, values, lengths and selections are written into the captured
     buffers equals the eager call on every replay (the workspace needs no
     clearing between replays)."""
-    say("attn graph replays")
+    say("attn graph replays, kv format", kvf)
     kw = dict(name="gr", R=3, P=4, H=2, k_format=W.K_BF16, req_len=[3000, 9000, 400], topk=24, init_blocks=1,
               local_blocks=1, seed=930)
     w, wc = W.make(**kw, device="cuda"), W.make(**kw)
-    at = W.make_attn(w, 4)
+    at = W.make_attn(w, 4, kv_format=kvf)
     ids = torch.as_tensor(pins.random_selection(wc, np.random.default_rng(931), topk=24), device="cuda")
     out = torch.empty_like(at.q)
     lse = torch.empty(at.q.shape[:3], dtype=torch.float32, device="cuda")
@@ -252,7 +259,7 @@ def test_attn_graph_replays(oracle):
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
         at.q.copy_(torch.randn(at.q.shape, generator=gen, device="cuda").to(torch.bfloat16))
-        at.v.copy_(torch.randn(at.v.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        at.v.copy_(torch.randn(at.v.shape, generator=gen, device="cuda").to(at.v.dtype))
         w.row_len.copy_(torch.clamp(base_len - 301 * rep, min=0))
         ids.copy_(torch.as_tensor(pins.random_selection(wc, np.random.default_rng(940 + rep), topk=24), device="cuda"))
         torch.cuda.synchronize()
@@ -322,31 +329,37 @@ def _subset(w: W.Workload, at: W.AttnInputs, ids: np.ndarray, reqs) -> tuple[dic
     def u16(t):
         return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
-    kk = u16(at.k.index_select(0, pg)) if len(pages) else np.zeros((1, H, 128, 128), np.uint16)
-    vv = u16(at.v.index_select(0, pg)) if len(pages) else np.zeros((1, H, 4, 128, 32), np.uint16)
+    def kv(t):  # raw bytes of a K or V pool in its format
+        return u16(t) if at.kv_format == W.K_BF16 else t.contiguous().cpu().view(torch.uint8).numpy()
+
+    kv_dt = np.uint16 if at.kv_format == W.K_BF16 else np.uint8
+    kk = kv(at.k.index_select(0, pg)) if len(pages) else np.zeros((1, H, 128, 128), kv_dt)
+    vv = kv(at.v.index_select(0, pg)) if len(pages) else np.zeros((1, H, 4, 128, 32), kv_dt)
     q = u16(at.q)[rows]
     a = dict(n_req=len(reqs), n_slot_rows=n_slot, packed_queries=P, kv_heads=H, q_per_kv=at.q_per_kv,
-             max_blocks=w.max_blocks, topk=K, sm_scale=SCALE, n_pages=max(1, len(pages)), q=np.ascontiguousarray(q),
+             max_blocks=w.max_blocks, topk=K, sm_scale=SCALE, n_pages=max(1, len(pages)), kv_format=at.kv_format,
+             q=np.ascontiguousarray(q),
              k=np.ascontiguousarray(kk), v=np.ascontiguousarray(vv), req_slot=req_slot, block_table=bt_sub,
              row_len=np.ascontiguousarray(lens[rows].astype(np.int32)),
              topk_ids=np.ascontiguousarray(ids3[rows].reshape(-1, K)))
     return a, rows
 
 
-@pytest.mark.parametrize("cfg,reqs", [(3, "all"), (4, "all")], ids=["524k_fp8", "150k_nvfp4"])
-def test_attn_full_size(oracle, cfg, reqs):
+@pytest.mark.parametrize("cfg,reqs,kvf", [(3, "all", W.K_BF16), (4, "all", W.K_BF16), (3, "all", W.K_FP8_E4M3)],
+                         ids=["524k_fp8", "150k_nvfp4", "524k_fp8_fp8kv"])
+def test_attn_full_size(oracle, cfg, reqs, kvf):
     """Every row of the 524K workload (its 32 requests and 3 graph pads:
-    about 8 GB of selected K/V pages go to the oracle) and of the 150K one
-    (64 requests, about 16 GB), against the oracle."""
+    about 8 GB of selected bf16 K/V pages go to the oracle, 4 GB in fp8) and
+    of the 150K one (64 requests, about 16 GB), against the oracle."""
     w = W.config(cfg, device="cuda")
     if reqs == "all":
         reqs = list(range(w.n_req))
-    say("attn full size", W.CONFIG_NAMES[cfg], "requests", reqs)
+    say("attn full size", W.CONFIG_NAMES[cfg], "kv format", kvf, "requests", reqs)
     if w.k_format == W.K_NVFP4:
         Hn.gpu_fp4_store(w)
     outs = Hn.gpu_outputs(w)
     I.idx_step(Hn.gpu_params(w, outs))
-    at = W.make_attn(w, 4)
+    at = W.make_attn(w, 4, kv_format=kvf)
     g = gpu_attn(w, at, outs["topk_ids"])
     ids = outs["topk_ids"].cpu().numpy()
     a, rows = _subset(w, at, ids, reqs)
@@ -355,7 +368,7 @@ def test_attn_full_size(oracle, cfg, reqs):
     # every real row saw something; pads none
     real = np.arange(w.n_real * w.packed_queries)
     assert np.isfinite(g["lse"][real]).all() and np.isneginf(g["lse"][w.n_real * w.packed_queries:]).all()
-    conftest.REPORT.append(f"sparse attention {w.name}: {len(reqs)} of {w.n_req} requests compared "
+    conftest.REPORT.append(f"sparse attention {w.name} ({'fp8' if kvf else 'bf16'} K/V): {len(reqs)} of {w.n_req} requests compared "
                            f"({len(rows) * w.gqa * 4} query heads)")
     del at
     torch.cuda.empty_cache()

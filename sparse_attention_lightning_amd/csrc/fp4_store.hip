@@ -53,20 +53,23 @@ __device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot,
   }
   const uint32_t sb = e4m3_rne_satfinite(amax / 6.0f);
   const float s = e4m3_value(sb);
-  // midpoints of the e2m1 grid 0 .5 1 1.5 2 3 4 6, times s (exact)
-  const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
-  const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
+  // midpoints of the e2m1 grid 0 .5 1 1.5 2 3 4 6, times s (exact); a zero
+  // scale makes them infinite, so every code has magnitude 0
+  const float sz = s > 0.0f ? s : __builtin_inff();
+  float m0 = 0.25f * sz, m1 = 0.75f * sz, m2 = 1.25f * sz, m3 = 1.75f * sz;
+  float m4 = 2.5f * sz, m5 = 3.5f * sz, m6 = 5.0f * sz;
+  // keep the seven products in registers: otherwise the compiler selects the
+  // constant per value and multiplies it again
+  asm volatile("" : "+v"(m0), "+v"(m1), "+v"(m2), "+v"(m3), "+v"(m4), "+v"(m5), "+v"(m6));
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const float a = fabsf(x[j]);
     // ties: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
-    const uint32_t b2 = a >= m3;
-    const uint32_t b1 = a >= (b2 ? m5 : m1);
+    const bool b2 = a >= m3;
+    const bool b1 = a >= (b2 ? m5 : m1);
     const float t3 = b2 ? (b1 ? m6 : m4) : (b1 ? m2 : m0);
-    const uint32_t b0 = a > t3;
-    uint32_t mag = (b2 << 2) | (b1 << 1) | b0;
-    mag = (s > 0.0f) ? mag : 0u;
+    const uint32_t mag = (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (a > t3 ? 1u : 0u);
     const uint32_t code = mag | ((__float_as_uint(x[j]) >> 28) & 8u);
     packed[j >> 3] |= code << (4 * (j & 7));
   }

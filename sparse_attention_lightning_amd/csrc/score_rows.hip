@@ -31,9 +31,27 @@
 // p + 1 tokens, items above the diagonal exit at once) and the C chunks of a
 // row group split that extent evenly, so the chunks of a row group are equal
 // however long its rows are.  Each XCD takes a contiguous run of items, so
-// the workgroups that read the same K pages share an L2.  Each lane keeps its
-// row's scores of four consecutive pages and writes them as one 16-byte store
-// (max mode; lse writes each page's score at once).
+// the workgroups that read the same K pages share an L2.
+//
+// Max mode: block scores leave in granules of 16 blocks of a row (64 bytes,
+// aligned in the array when max_blocks is a multiple of 16).  Each lane puts
+// its row's score of a page in LDS (two granule buffers, by granule parity,
+// rows consecutive so that a page's scores are one conflict-free write),
+// and when an item has scored all its blocks of a granule the workgroup
+// writes that granule for all its rows, four lanes a row, 16 rows an
+// instruction.  The chunk that ends a row group's extent pads its last
+// granule with -inf and writes the -inf past it.  A granule cut by a chunk
+// boundary is written in two parts by two workgroups; boundaries fall on
+// 16-byte pieces, and odd chunks walk their blocks backwards, so both parts
+// are written at about the same time (both at the start or both at the end
+// of their items).  Values stored one by one as each page was scored left
+// each line to be assembled over many pages while the streaming K evicted it:
+// about ten times the block-score bytes reached HBM on the prefill workload
+// (3.3 times with four values a 16-byte store, 1.3 times staged, the rest
+// all at chunk boundaries: 1.00 with one chunk a row group).  lse mode
+// stores each score as it is made: it is bound by its vector work, the
+// writes do not bound it, and staging cost it 5 % (more wait states in its
+// tighter register budget).
 #include <algorithm>
 #include <atomic>
 #include <climits>
@@ -57,18 +75,6 @@ namespace idx {
                               // lse: after the page (its half-page accumulators leave no registers)
 #endif
 
-// Block scores a lane keeps before one store (4: an aligned 16-byte store; 1:
-// each alone).  Per-value stores leave each 128-byte output line to be
-// assembled over 32 pages, and the streaming K evicts the partly written
-// lines: 10.4x the block-score bytes reach HBM on the prefill workload, 3.3x
-// with 4 values a store, 2.0x with 8.  4 costs nothing in max mode; lse mode
-// has no registers to spare (4 measured 3 % slower), 8 cost max mode 4.5 %.
-#ifndef IDX_ROWS_OUT_VEC_MAX
-#define IDX_ROWS_OUT_VEC_MAX 4
-#endif
-#ifndef IDX_ROWS_OUT_VEC_LSE
-#define IDX_ROWS_OUT_VEC_LSE 1
-#endif
 #ifndef IDX_ROWS_ITEMS
 #define IDX_ROWS_ITEMS 1      // items per resident workgroup the block chunks aim at
 #endif
@@ -83,6 +89,7 @@ constexpr int kItemRows = kWaveRows * kRowWaves;
 static_assert(kWaveTiles % 4 == 0, "tiles a wave: a multiple of the four lane groups");
 constexpr int kMaxItemBlocks = 1024;                   // blocks of an item at most (page ids in LDS)
 constexpr int kPageUnits = kHeadDim * 2 / 16;          // 16-byte units of a bf16 token row (16)
+constexpr int kGran = 16;                              // blocks of a row in one 64-byte output granule
 
 // LDS slot of 16-byte unit `unit` of token `tok` in a page: rows of 256 bytes,
 // the unit index XORed with the token's low four bits.  Sixteen lanes that
@@ -98,11 +105,13 @@ constexpr int rows_ring() {
 }
 
 // LDS of a workgroup: two bf16 K pages in 16-byte units (typed so that each
-// access is one 16-byte LDS instruction) and the item's page ids.
+// access is one 16-byte LDS instruction), the item's page ids, and each row's
+// scores of its current output granule.
 struct RowsLds {
   u32x4 page[2][kBlock * kPageUnits];
   int32_t pid[kMaxItemBlocks];
   int32_t nbw[kRowWaves];
+  float gran[2][kGran][kItemRows];  // [granule parity][slot][row]: a page's scores are one conflict-free write
 };
 
 // A page's bytes in flight in registers: 16-byte pieces, consecutive threads
@@ -324,22 +333,40 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   for (int w = 0; w < kRowWaves; ++w) nb_item = max(nb_item, L.nbw[w]);
   nb_item = (int)uniform((uint32_t)nb_item);
 
-  // blocks no item covers (past the row group's longest row, every block of a
-  // graph pad) get -inf from the chunk-0 workgroup of the row group
-  if (c == 0) {
+  // The end (exclusive) of the output granule holding a row's last scored
+  // block, capped at the row's end: the chunk that scores that block fills
+  // the granule's rest with -inf.  Blocks from there on (past the row
+  // group's longest row, every block of a graph pad) get -inf from the
+  // chunk-0 workgroup of the row group.
+  constexpr bool kStaged = MODE == IDX_SCORE_MAX;  // lse stores each score as it is made (see the header)
+  // chunk c of C: an even share of the row group's own extent, so the items
+  // of a row group do the same work whatever its rows' lengths; in max mode
+  // the inner boundaries are rounded to multiples of four blocks, so the
+  // parts of a granule two chunks write are whole 16-byte pieces (at most
+  // kMaxItemBlocks blocks: the launch makes ceil(max_blocks / C) + 4 no more)
+  auto chunk_start = [&](int cc) -> int {
+    const int x = (int)((int64_t)cc * nb_item / C);
+    return (cc >= C) ? nb_item : (kStaged ? min(nb_item, (x + 2) & ~3) : x);
+  };
+  const int b0 = chunk_start(c);
+  const int nblk = chunk_start(c + 1) - b0;
+  // blocks past the row group's longest row (every block of a graph pad) get
+  // -inf from the chunk that ends the extent (chunk 0 when there is none);
+  // with aligned granules its last one is padded, and the rest starts whole
+  const bool whole = kStaged && (MB % kGran) == 0 && (reinterpret_cast<uintptr_t>(a.block_scores) & 15) == 0;
+  const bool ends = (nb_item == 0) ? (c == 0) : (nblk > 0 && b0 + nblk == nb_item);
+  if (ends) {
+    const int fill_from = whole ? min(MB, (nb_item + kGran - 1) & ~(kGran - 1)) : nb_item;
     for (int i = 0; i < kWaveRows; ++i) {
       const int row = wrow0 + i;
       if (row >= PH) break;
       float* out = a.block_scores + ((int64_t)r * PH + row) * MB;
-      for (int b = nb_item + lane; b < MB; b += 64) out[b] = -INFINITY;
+      for (int b = fill_from + lane; b < MB; b += 64) out[b] = -INFINITY;
     }
   }
-  // chunk c of C: an even share of the row group's own extent, so the items
-  // of a row group do the same work whatever its rows' lengths (at most
-  // kMaxItemBlocks blocks: the launch makes ceil(max_blocks / C) no more)
-  const int b0 = (int)((int64_t)c * nb_item / C);
-  const int nblk = (int)((int64_t)(c + 1) * nb_item / C) - b0;
   if (nblk <= 0) return;
+  const bool rev = kStaged && (c & 1) != 0;  // odd chunks take their blocks last to first
+  auto blk = [&](int k) -> int { return b0 + (rev ? nblk - 1 - k : k); };  // the block of the k-th page
   const bool active = wrow0 < PH;  // the wave has rows
   for (int j = tid; j < nblk; j += kRowThreads) L.pid[j] = a.block_table[(int64_t)slot * MB + b0 + j];
 
@@ -361,18 +388,46 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
     }
   }
   const float c2 = (MODE == IDX_SCORE_LSE) ? a.sm_scale * 1.44269504088896341f : 0.f;
-  // the lane's row's scores of the current group of IDX_ROWS_OUT_VEC blocks
-  // (block b in slot b % IDX_ROWS_OUT_VEC), written as one store when the
-  // group is complete; a group cut by the item's ends goes out value by value
-  constexpr int kOutVec = (MODE == IDX_SCORE_MAX) ? IDX_ROWS_OUT_VEC_MAX : IDX_ROWS_OUT_VEC_LSE;
-  static_assert(kOutVec == 1 || kOutVec % 4 == 0, "whole 16-byte stores");
-  float obuf[kWaveTiles / 4][kOutVec];
-  const bool vec_rows = kOutVec > 1 && (MB % kOutVec) == 0 &&
-                        (reinterpret_cast<uintptr_t>(a.block_scores) & (4 * kOutVec - 1)) == 0;
+  // the item's blocks gl .. gh of granule G (blocks 16 G .. 16 G + 15; at
+  // the extent's end padded with -inf to the granule's end), written by the
+  // whole workgroup: four lanes a row, 16 rows an instruction
+  auto write_granule = [&](int G, int gl, int gh) {
+    const int ge = (ends && whole && gh == nb_item - 1) ? kGran * G + kGran - 1 : gh;
+    float* base = a.block_scores + ((int64_t)r * PH + gi * kItemRows) * MB + kGran * G;
+#pragma unroll 1
+    for (int x = tid; x < kItemRows * (kGran / 4); x += kRowThreads) {
+      const int lr = x >> 2, e = x & 3;
+      if (gi * kItemRows + lr >= PH) break;  // x grows with the row
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = L.gran[G & 1][4 * e + i][lr];
+      float* dst = base + (int64_t)lr * MB + 4 * e;
+      const int b1 = kGran * G + 4 * e;  // the block of v[0]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (b1 + i <= gh) ? v[i] : -INFINITY;
+      if (whole) {  // the item's blocks of a granule are whole 16-byte pieces
+        if (b1 >= gl && b1 <= ge) *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (b1 + i >= gl && b1 + i <= ge) dst[i] = v[i];
+      }
+    }
+  };
+  // after the pages k0 .. k1 - 1: the granules whose blocks of this item are
+  // now all scored (at most two)
+  auto write_done = [&](int k0, int k1) {
+    const int lo = rev ? b0 + nblk - k1 : b0, hi = rev ? b0 + nblk - 1 : b0 + k1 - 1;  // scored so far
+    const int pl = rev ? lo : b0 + k0, ph = rev ? b0 + nblk - 1 - k0 : hi;             // by these pages
+    for (int G = pl / kGran; G <= ph / kGran; ++G) {
+      const int gl = max(kGran * G, b0), gh = min(kGran * G + kGran - 1, b0 + nblk - 1);
+      if (gl >= lo && gh <= hi) write_granule(G, gl, gh);
+    }
+  };
 
   // page j of the item: its id (-1 past the item) and descriptors
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k);
-  auto page_of = [&](int j) -> int { return (j < nblk) ? L.pid[j] : -1; };
+  auto page_of = [&](int k) -> int { return (k < nblk) ? L.pid[rev ? nblk - 1 - k : k] : -1; };
   auto issue = [&](PageRegs<FMT>& pr, int pid) {
     const bool ok = pid >= 0 && pid < a.n_pages;
     const __amdgpu_buffer_rsrc_t rk = page_rsrc(kp, pid, ok, kPageBytes);
@@ -427,7 +482,7 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   // mid(): the next page's copy into the other LDS buffer, placed among this
   // page's MFMAs so that its conversions and LDS writes overlap them
   auto score_page = [&](int k, int pid, auto&& mid) {
-    const int b = b0 + k;
+    const int b = blk(k);
     const u32x4* P = L.page[k & 1];
     BlockState st;
 #pragma unroll
@@ -452,33 +507,11 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
       else
         o = (m == -INFINITY) ? -INFINITY : (m + __builtin_amdgcn_logf(s)) * 0.693147180559945309f;
       if (!ok) o = (b * kBlock < my_len[q]) ? __builtin_nanf("") : -INFINITY;
-      const int row = wrow0 + kTileRows * (4 * q + g) + n;
-      float* dst = a.block_scores + ((int64_t)r * PH + row) * MB;
-      if constexpr (kOutVec == 1) {
-        if (row < PH) dst[b] = o;
+      if constexpr (kStaged) {
+        L.gran[(b / kGran) & 1][b & (kGran - 1)][kWaveRows * wave + kTileRows * (4 * q + g) + n] = o;
       } else {
-        constexpr int V = kOutVec;
-        const int sl = b % V;
-#pragma unroll
-        for (int e = 0; e < V; ++e) obuf[q][e] = (sl == e) ? o : obuf[q][e];
-        if (sl == V - 1 || k == nblk - 1) {  // the group is complete, or the item ends
-          const int g0 = b - sl;
-          if (row < PH) {
-            if (vec_rows && sl == V - 1 && g0 >= b0) {
-              if constexpr (V == 4) {
-                *reinterpret_cast<f32x4*>(dst + g0) = f32x4{obuf[q][0], obuf[q][1], obuf[q][2], obuf[q][3]};
-              } else {
-#pragma unroll
-                for (int e = 0; e < V; e += 4)
-                  *reinterpret_cast<f32x4*>(dst + g0 + e) = f32x4{obuf[q][e], obuf[q][e + 1], obuf[q][e + 2], obuf[q][e + 3]};
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < V; ++e)
-                if (e <= sl && g0 + e >= b0) dst[g0 + e] = obuf[q][e];
-            }
-          }
-        }
+        const int row = wrow0 + kTileRows * (4 * q + g) + n;
+        if (row < PH) a.block_scores[((int64_t)r * PH + row) * MB + b] = o;
       }
     };
     out(std::integral_constant<int, 0>{});
@@ -495,6 +528,7 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   for (int u = 0; u < D; ++u) issue(ring[u], page_of(u));
   page_store<FMT>(ring[0], L.page[0], tid);
   __syncthreads();
+  static_assert(D <= kGran, "a ring pass finishes at most two granules");
   for (int k0 = 0; k0 < nblk; k0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
@@ -510,6 +544,9 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
       }
       __syncthreads();
     }
+    // granules finished by this pass go out (the next pass writes the other
+    // granule buffer; this one is reused only 16 blocks later)
+    if constexpr (kStaged) write_done(k0, min(k0 + D, nblk));
   }
 }
 
@@ -554,7 +591,7 @@ void launch_rows(const StepArgs& a, hipStream_t stream) {
   const int slots = rows_resident<FMT, MODE>();
   const int64_t groups = (int64_t)a.n_req * G;
   const int64_t want = std::max<int64_t>(1, (IDX_ROWS_ITEMS * (int64_t)slots + groups - 1) / groups);
-  const int CB = (int)std::min<int64_t>(kMaxItemBlocks, std::max<int64_t>(1, (a.max_blocks + want - 1) / want));
+  const int CB = (int)std::min<int64_t>(kMaxItemBlocks - 4, std::max<int64_t>(1, (a.max_blocks + want - 1) / want));
   const int C = (a.max_blocks + CB - 1) / CB;
   const int64_t M = groups * C;
   const int64_t grid = std::min<int64_t>(8 * ((M + 7) / 8), 8 * ((slots + 7) / 8));

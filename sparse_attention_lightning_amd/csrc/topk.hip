@@ -34,6 +34,9 @@
 #ifndef IDX_TOPK_VALU_COUNT
 #define IDX_TOPK_VALU_COUNT 1  // 1: the one-wave kernel counts keys per lane and sums them with DPP
 #endif                         // (vector work); 0: a ballot and a scalar popcount per slot
+#ifndef IDX_TOPK_RADIX
+#define IDX_TOPK_RADIX 1           // one-wave kernel: 1 finds its threshold by 8-bit digits over LDS
+#endif                             // histograms; 0: bit by bit, one wave-wide count a bit
 #ifndef IDX_TOPK_BALLOT_ROWS
 #define IDX_TOPK_BALLOT_ROWS 1024  // rows from which rows of <= 1,024 blocks take one wave each
 #endif
@@ -306,23 +309,23 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// The same selection with one wave a row and no LDS, for rows of at most
-// 64 S blocks: lane l holds blocks l, l + 64, ... (slot j: block 64 j + l).
-// The want-th largest competing key is found bit by bit from the top: a
-// candidate threshold c (>= 1) is kept when at least `want` competing keys
-// reach it, each count one ballot per slot (blocks that do not compete hold
-// key 0 there, below every c).  Keys equal to the threshold are taken lowest
-// id first, and the output positions (ascending ids) come from the same
-// ballot masks.
+// The same selection with one wave a row, for rows of at most 64 S blocks:
+// lane l holds blocks l, l + 64, ... (slot j: block 64 j + l).  The
+// want-th largest competing key T is found by a radix select over 8-bit
+// digits with a 256-bin histogram in LDS per wave (or, with
+// IDX_TOPK_RADIX 0, bit by bit from the top: a candidate threshold c >= 1 is
+// kept when at least `want` competing keys reach it; blocks that do not
+// compete hold key 0, below every c).  Keys equal to T are taken lowest id
+// first, and the output positions (ascending ids) come from ballot masks.
+// (A resident grid of these waves walking the rows, each loading its next
+// row's scores during the current selection, measured 20 % slower: the loop
+// state spilled scalar registers and cost occupancy.)
+
+// The selection of row o; hw: the wave's histogram.
 template <int S>
-__global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rows = a.P * a.H;
-  const int64_t o = (int64_t)blockIdx.x * kBallotWaves + wave;
-  if (o >= (int64_t)a.n_req * rows) return;
+__device__ __forceinline__ void ballot_row(const StepArgs& a, int64_t o, int rows, int K, int MB, int lane,
+                                           uint32_t* hw) {
   const int r = (int)(o / rows), i = (int)(o - (int64_t)r * rows);
-  const int K = a.topk, MB = a.max_blocks;
   const float* bs = a.block_scores + o * MB;
   const int slot = a.req_slot[r];
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
@@ -378,6 +381,48 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
       T = kmin;
       hi = -1;
     }
+#if IDX_TOPK_RADIX
+    // Radix select, 8 bits a pass from bit hi down: count the competing
+    // keys that share T's bits above the digit into a 256-bin histogram in
+    // LDS, take the highest digit at which the count from the top reaches
+    // `need`, and keep the keys above it.  Stop when that digit's bin holds
+    // exactly the keys still needed (T = its lower bound selects them) or
+    // the last bit is fixed (T is the key itself).  Lane l holds bins
+    // 255 - 4 l - 3 .. 255 - 4 l, so an inclusive scan over the lanes
+    // counts from the top.
+    uint32_t need = want;
+    while (hi >= 0) {
+      const int lo = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
+      reinterpret_cast<u32x4*>(hw)[lane] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        const bool same = (hi == 31) || (((ckey[j] ^ T) >> (hi + 1)) == 0u);
+        if (((cand >> j) & 1u) && same) atomicAdd(&hw[(ckey[j] >> lo) & dmask], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const u32x4 c = reinterpret_cast<const u32x4*>(hw)[63 - lane];  // bins 252 - 4 l .. 255 - 4 l
+      const uint32_t sum = c.x + c.y + c.z + c.w;
+      const uint32_t incl = wave_inclusive_sum(sum);
+      const uint32_t a3 = incl - sum + c.w, a2 = a3 + c.z, a1 = a2 + c.y;  // counts from the top
+      const bool here = incl >= need && incl - sum < need;                  // the digit is in this lane
+      const uint64_t hm = __builtin_amdgcn_ballot_w64(here);
+      const int src = (int)__builtin_ctzll(hm);
+      // in the found lane: the digit, the keys above it and in its bin
+      const uint32_t sel = a3 >= need ? 3u : a2 >= need ? 2u : a1 >= need ? 1u : 0u;
+      const uint32_t above = sel == 3u ? incl - sum : sel == 2u ? a3 : sel == 1u ? a2 : a1;
+      const uint32_t inbin = sel == 3u ? c.w : sel == 2u ? c.z : sel == 1u ? c.y : c.x;
+      const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)(252u - 4u * (uint32_t)lane + sel), src);
+      const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+      const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)inbin, src);
+      T |= d << lo;
+      need -= ab;
+      if (ib == need || lo == 0) break;
+      hi = lo - 1;
+    }
+#else
     // unrolled: no loop control among the counting (bits above hi skip).
     // Once exactly `want` keys reach c they are the ones to take, and T = c
     // (a key or not) selects them: keys above T, then all keys equal to it;
@@ -402,6 +447,7 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
       if (n >= want) T = c;
       if (n == want) break;
     }
+#endif
   }
 
   // taken: forced, competing keys above T, and of those equal to T the first
@@ -415,6 +461,8 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
   }
   const uint32_t rem = want - above;  // keys equal to T to take
   uint32_t eq_before = 0, sel_before = 0;
+  const __amdgpu_buffer_rsrc_t rid = __builtin_amdgcn_make_buffer_rsrc(ids, (short)0, 4 * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(sc, (short)0, 4 * K, 0x00020000);
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const bool c = (cand >> j) & 1u;
@@ -424,13 +472,27 @@ __global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepA
         ((forced >> j) & 1u) || (want > 0 && c && key[j] > T) || (eq && eq_before + lanes_below(em) < rem);
     const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
     const uint32_t pos = sel_before + lanes_below(tm);
-    if (take && pos < (uint32_t)K) {  // exactly K are taken: F forced + want
-      ids[pos] = 64 * j + lane;
-      sc[pos] = sv[j];
-    }
+    // exactly K are taken (F forced + want); a lane with nothing to write
+    // stores past the row's descriptor, which drops it (no branch)
+    const uint32_t off = (take && pos < (uint32_t)K) ? 4u * pos : 4u * (uint32_t)K;
+    __builtin_amdgcn_raw_buffer_store_b32(64 * j + lane, rid, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[j]), rsc, off, 0, 0);
     eq_before += (uint32_t)__builtin_popcountll(em);
     sel_before += (uint32_t)__builtin_popcountll(tm);
   }
+}
+
+template <int S>
+__global__ __launch_bounds__(kBallotThreads) void topk_ballot_kernel(const StepArgs a) {
+  __shared__ alignas(16) uint32_t ballot_hist[kBallotWaves][256];  // one histogram a wave
+  auto hw_of = [&](int w) { return ballot_hist[w]; };
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows = a.P * a.H;
+  const int K = a.topk, MB = a.max_blocks;
+  const int64_t o = (int64_t)blockIdx.x * kBallotWaves + wave;
+  if (o >= (int64_t)a.n_req * rows) return;
+  ballot_row<S>(a, o, rows, K, MB, lane, hw_of(wave));
 }
 
 // topk_ballot_kernel for the row's slot count S = ceil(max_blocks / 64), 1..16.

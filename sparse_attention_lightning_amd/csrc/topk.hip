@@ -360,10 +360,8 @@ __device__ __forceinline__ void ballot_row(const StepArgs& a, int64_t o, int row
       kmax = max(kmax, key[j]);
     }
   }
-  uint32_t F = 0;
-#pragma unroll
-  for (int j = 0; j < S; ++j) F += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((forced >> j) & 1u));
-  const uint32_t want = (uint32_t)K - F;  // nb > K >= init + local: every forced block exists
+  // nb > K >= init + local: the two forced ranges exist whole and do not overlap
+  const uint32_t want = (uint32_t)(K - init - a.local_blocks);
 
   // T: the want-th largest competing key.  Every threshold tried is >= 1;
   // T stays 0 only when fewer than `want` competing keys are above 0 (NaN

@@ -596,6 +596,36 @@ def test_many_rows_equal_per_row():
         assert np.array_equal(g[key], gp[key], equal_nan=True), f"many rows != per-row ({key})"
 
 
+@pytest.mark.parametrize("mb", [48, 272])
+def test_many_rows_output_layouts(oracle, mb):
+    """The many-rows kernel's block-score writes: with max_blocks a multiple
+    of 16 the scores leave in whole 64-byte granules staged in LDS, chunk
+    boundaries rounded to four blocks and odd chunks walking backwards; the
+    same step into a block-score array one float off 16-byte alignment takes
+    the value-by-value path.  Both equal the oracle and each other bit for
+    bit, with -inf past each row group's extent (prefill-like causal rows,
+    a short request, a graph pad)."""
+    say("many rows output layouts, max_blocks", mb)
+    kw = dict(name="layout", R=3, P=64, H=4, k_format=W.K_FP8_E4M3, req_len=[1000, 5000, 60], topk=8,
+              init_blocks=1, local_blocks=2, seed=560 + mb, pads=1, pad_len=2000, max_blocks=mb)
+    w = W.make(**kw, device="cuda")
+    aligned = Hn.gpu_step(w)
+    # the same into views one float past 16-byte alignment
+    rows = w.rows
+    big = torch.full((rows * mb + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    outs = {"block_scores": big[1:1 + rows * mb].view(rows, mb),
+            "topk_ids": torch.full((rows, w.topk), -7, dtype=torch.int32, device="cuda"),
+            "topk_scores": torch.full((rows, w.topk), float("nan"), dtype=torch.float32, device="cuda")}
+    assert outs["block_scores"].data_ptr() % 16 == 4
+    I.idx_step(Hn.gpu_params(w, outs))
+    torch.cuda.synchronize()
+    shifted = {k: v.cpu().numpy() for k, v in outs.items()}
+    for key in aligned:
+        assert np.array_equal(aligned[key], shifted[key], equal_nan=True), key
+    a = w.oracle_args()
+    Hn.assert_parity(aligned, oracle.step(**a), a)
+
+
 def test_many_rows_invalid_pages(oracle):
     say("many rows, invalid page ids")
     w = W.make(name="rows_bad", R=2, P=40, H=2, k_format=W.K_BF16, req_len=[1500, 900], topk=4,

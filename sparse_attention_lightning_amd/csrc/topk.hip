@@ -32,8 +32,8 @@
 
 
 #ifndef IDX_TOPK_VALU_COUNT
-#define IDX_TOPK_VALU_COUNT 1  // 1: the one-wave kernel counts keys per lane and sums them with DPP
-#endif                         // (vector work); 0: a ballot and a scalar popcount per slot
+#define IDX_TOPK_VALU_COUNT 1  // bit-by-bit one-wave kernel: 1 counts keys per lane and sums them with
+#endif                         // DPP (vector work); 0: a ballot and a scalar popcount per slot
 #ifndef IDX_TOPK_RADIX
 #define IDX_TOPK_RADIX 1           // one-wave kernel: 1 finds its threshold by 8-bit digits over LDS
 #endif                             // histograms; 0: bit by bit, one wave-wide count a bit
@@ -470,7 +470,7 @@ __device__ __forceinline__ void ballot_row(const StepArgs& a, int64_t o, int row
         ((forced >> j) & 1u) || (want > 0 && c && key[j] > T) || (eq && eq_before + lanes_below(em) < rem);
     const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
     const uint32_t pos = sel_before + lanes_below(tm);
-    // exactly K are taken (F forced + want); a lane with nothing to write
+    // exactly K are taken (init + local forced, want competing); a lane with nothing to write
     // stores past the row's descriptor, which drops it (no branch)
     const uint32_t off = (take && pos < (uint32_t)K) ? 4u * pos : 4u * (uint32_t)K;
     __builtin_amdgcn_raw_buffer_store_b32(64 * j + lane, rid, off, 0, 0);

@@ -54,7 +54,7 @@ def parse() -> argparse.Namespace:
                     help="skip the plain-read measurement of the step's K pages")
     ap.add_argument("--attn-q-per-kv", type=int, default=4,
                     help="query heads per KV head of the sparse attention measured after the step "
-                         "(0: skip it; packed_queries * this must be <= 16)")
+                         "(0: skip it; packed_queries * this must be <= 64)")
     ap.add_argument("--attn-kv-format", choices=("bf16", "fp8", "both"), default="both",
                     help="K/V format(s) of the sparse attention measured after the step")
     ap.add_argument("--score-mode", choices=("max", "lse"), default="max",
@@ -287,7 +287,7 @@ def main() -> int:
     if fp4:
         line["fp4_store_step_tokens"] = int(step_staging.shape[0])
         line["fp4_store_pool"] = pool_store
-    if args.attn_q_per_kv and P * args.attn_q_per_kv <= 16:
+    if args.attn_q_per_kv and P <= 16 and P * args.attn_q_per_kv <= 64:
         for kvf in ("bf16", "fp8"):
             if args.attn_kv_format in (kvf, "both"):
                 key = "sparse_attn" if kvf == "bf16" else "sparse_attn_fp8kv"

@@ -233,11 +233,13 @@ const char* idx_last_error(void);
  *            splits of each (request, KV head)), needing no initialisation.
  *            When the batch fills the device without splitting, the size is 0
  *            and the workspace may be NULL.
- * Limits: P * G <= IDX_ATTN_MAX_ROWS (the rows of one request and KV head
- * share one 16-row MFMA tile and read each selected K/V page once), P * topk
- * <= IDX_ATTN_MAX_IDS.  q, k, v, out 16-byte aligned.
+ * Limits: P <= IDX_ATTN_MAX_DRAFT and P * G <= IDX_ATTN_MAX_ROWS (the rows
+ * of one request and KV head are up to four 16-row MFMA tiles that read each
+ * selected K/V page once for all of them), P * topk <= IDX_ATTN_MAX_IDS.
+ * q, k, v, out 16-byte aligned.
  */
-#define IDX_ATTN_MAX_ROWS 16
+#define IDX_ATTN_MAX_ROWS 64
+#define IDX_ATTN_MAX_DRAFT 16
 #define IDX_ATTN_MAX_IDS 1024
 #define IDX_ATTN_MAX_SPLITS 64
 
@@ -273,7 +275,7 @@ int64_t idx_sparse_attn_workspace(const idx_attn_params* p);
 
 /* Sparse attention over the selected blocks (on `stream`: the splits'
  * partials, then their merge; one launch when nothing is split).  Refusals as the other calls, plus
- * IDX_E_PACK for P * G > IDX_ATTN_MAX_ROWS, IDX_E_TOPK for P * topk >
+ * IDX_E_PACK for P > IDX_ATTN_MAX_DRAFT or P * G > IDX_ATTN_MAX_ROWS, IDX_E_TOPK for P * topk >
  * IDX_ATTN_MAX_IDS, IDX_E_MODE for a bad sm_scale, IDX_E_FORMAT for another
  * kv_format and IDX_E_SHAPE for a workspace below idx_sparse_attn_workspace(p). */
 int idx_sparse_attn(const idx_attn_params* p, void* stream);

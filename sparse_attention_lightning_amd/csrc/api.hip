@@ -125,8 +125,10 @@ int check_attn(const idx_attn_params* p) {
   if (p->packed_queries < 1 || p->kv_heads < 1 || p->q_per_kv < 1)
     return fail(IDX_E_SHAPE, "packed_queries, kv_heads and q_per_kv must be >= 1 (got %d, %d, %d)",
                 p->packed_queries, p->kv_heads, p->q_per_kv);
+  if (p->packed_queries > IDX_ATTN_MAX_DRAFT)
+    return fail(IDX_E_PACK, "packed_queries %d exceeds %d draft rows", p->packed_queries, IDX_ATTN_MAX_DRAFT);
   if ((int64_t)p->packed_queries * p->q_per_kv > IDX_ATTN_MAX_ROWS)
-    return fail(IDX_E_PACK, "packed_queries * q_per_kv = %lld exceeds %d rows a tile",
+    return fail(IDX_E_PACK, "packed_queries * q_per_kv = %lld exceeds %d rows a (request, KV head)",
                 (long long)p->packed_queries * p->q_per_kv, IDX_ATTN_MAX_ROWS);
   if (p->n_req < 0 || p->n_slot_rows < 0 || p->n_pages < 0)
     return fail(IDX_E_SHAPE, "negative count (n_req %d, n_slot_rows %d, n_pages %lld)", p->n_req, p->n_slot_rows,
@@ -152,7 +154,8 @@ int64_t attn_workspace_bytes(const idx_attn_params* p, int* splits) {
   const int64_t max_union = std::min<int64_t>((int64_t)p->packed_queries * p->topk, p->max_blocks);
   const int s = idx::attn_splits(items, max_union);
   if (splits) *splits = s;
-  return s > 1 ? items * s * 16 * 132 * (int64_t)sizeof(float) : 0;  // one split: no partials
+  const int64_t rows = 16 * (int64_t)idx::attn_tiles(p->packed_queries, p->q_per_kv);
+  return s > 1 ? items * s * rows * 132 * (int64_t)sizeof(float) : 0;  // one split: no partials
 }
 
 }  // namespace

@@ -6,8 +6,10 @@
 // kernel's tests beside the packed scorer; ROCm/ATOM PR 2745, Validation,
 // times the fused verify kernel on MI355X).
 //
-// Work item = (request, KV head).  Its P draft rows x G query heads (P G <= 16)
-// form one 16-row MFMA tile, and the item walks the union of its P rows'
+// Work item = (request, KV head).  Its P draft rows x G query heads (P <= 16,
+// P G <= 64) form T = ceil(P G / 16) 16-row MFMA tiles, each wave holding
+// all T: every 32-token unit of K and V it loads serves all of them.  The
+// item walks the union of its P rows'
 // selections, each block carrying the mask of the rows that chose it: a block
 // chosen by several draft rows is read from HBM once for all of them, as the
 // indexer reads each K page once for all rows of a request.  An item's union
@@ -153,17 +155,24 @@ __device__ __forceinline__ void attn_finalize(const AttnArgs& a, int r, int h, i
   if (c8 == 0) a.lse[orow] = lse;
 }
 
-template <int KVF>
+// Ring depth for T query tiles a wave: the tiles' outputs and queries take
+// the registers a deeper ring would.
+template <int KVF, int T>
+constexpr int attn_ring() {
+  return T == 1 ? AttnUnit<KVF>::kRing : (KVF == IDX_K_BF16 ? 2 : 3);
+}
+
+template <int KVF, int T>
 __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_kernel(const AttnArgs a) {
   typedef AttnUnit<KVF> Unit;
-  constexpr int kRing = Unit::kRing;
+  constexpr int kRing = attn_ring<KVF, T>();
   __shared__ int32_t list_id[IDX_ATTN_MAX_IDS];
   __shared__ int32_t list_page[IDX_ATTN_MAX_IDS];
   __shared__ uint16_t list_mask[IDX_ATTN_MAX_IDS];
   __shared__ union {
-    uint32_t bits[IDX_ATTN_MAX_ROWS][kAttnBitWords];  // each draft row's selected blocks
+    uint32_t bits[IDX_ATTN_MAX_DRAFT][kAttnBitWords];  // each draft row's selected blocks
     struct {
-      float o[kAttnWaves][16][128];
+      float o[kAttnWaves][16][128];  // one 16-row tile at a time
       float m[kAttnWaves][16];
       float l[kAttnWaves][16];
     } comb;
@@ -215,28 +224,41 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
   // 4. the wave's blocks: lo + wave, lo + wave + 4, ... A fixed assignment
   // keeps the order of every floating-point sum, so repeated calls give
   // bit-identical outputs; with one wave a SIMD it measured as fast as
-  // handing blocks out from an LDS counter.
+  // handing blocks out from an LDS counter.  Tile t holds rows 16 t .. 16 t
+  // + 15 of the item's P x G; lane n of it is row 16 t + n.
   const int n = lane & 15, gq = lane >> 4;
-  const bool row_ok = n < P * G;
-  const int j = row_ok ? n / G : 0, g = row_ok ? n - j * G : 0;
-  const int64_t qrow = (((int64_t)(r * P + j)) * H + h) * G + g;
-  const int my_len = row_ok && !pad ? clamp_len(a.row_len[r * P + j], MB) : 0;
-  const uint32_t jbit = row_ok ? (1u << j) : 0u;
-  bf16x8_t qf[4];
+  bf16x8_t qf[T][4];
+  int my_len[T];
+  uint32_t jbit[T];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + attn_d0<KVF>(s, gq));
-    qf[s] = __builtin_bit_cast(bf16x8_t, w);
+  for (int t = 0; t < T; ++t) {
+    const int rr = 16 * t + n;
+    const bool row_ok = rr < P * G;
+    const int j = row_ok ? rr / G : 0, g = row_ok ? rr - j * G : 0;
+    const int64_t qrow = (((int64_t)(r * P + j)) * H + h) * G + g;
+    my_len[t] = row_ok && !pad ? clamp_len(a.row_len[r * P + j], MB) : 0;
+    jbit[t] = row_ok ? (1u << j) : 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok) w = *reinterpret_cast<const u32x4*>(a.q + qrow * 128 + attn_d0<KVF>(s, gq));
+      qf[t][s] = __builtin_bit_cast(bf16x8_t, w);
+    }
   }
   const int my_blocks = (hi - lo - wave + kAttnWaves - 1) / kAttnWaves;  // may be <= 0
   const int n_units = my_blocks > 0 ? 4 * my_blocks : 0;
 
-  float m = -INFINITY, l = 0.f;
-  bool bad = false;
-  f32x4 o[8];
+  float m[T], l[T];
+  bool bad[T];
+  f32x4 o[T][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+    bad[t] = false;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   // token of K row this lane loads for half c: pi_c(n)
   const int tk0 = 8 * (n >> 2) + (n & 3);
 
@@ -281,47 +303,57 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
     const uint32_t mask = __builtin_amdgcn_readfirstlane((uint32_t)list_mask[x]);
     const int page = (int)__builtin_amdgcn_readfirstlane((uint32_t)list_page[x]);
     const bool ok = page >= 0 && page < a.n_pages;
-    const bool sel = (mask & jbit) != 0u;
-    bad |= sel && !ok;
-    f32x4 acc[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(w, c, s), qf[s], acc[c], 0, 0, 0);
-    }
-    // this lane: row n, tokens 8 gq + 4 c + i of the unit
-    const int pos0 = 128 * b + 32 * (U_ & 3) + 8 * gq;
-    float xv[8];
-    float mt = -INFINITY;
+    // the unit's operands, widened once for all tiles
+    bf16x8_t ko[2][4], vo[8];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool vis = sel && ok && pos0 + 4 * c + i < my_len;
-        xv[4 * c + i] = vis ? acc[c][i] * a.c2 : -INFINITY;
-        mt = fmaxf(mt, xv[4 * c + i]);
+      for (int s = 0; s < 4; ++s) ko[c][s] = k_operand(w, c, s);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) vo[dt] = v_operand(w, dt);
+    // this lane: row 16 t + n, tokens 8 gq + 4 c + i of the unit
+    const int pos0 = 128 * b + 32 * (U_ & 3) + 8 * gq;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const bool sel = (mask & jbit[t]) != 0u;
+      bad[t] |= sel && !ok;
+      f32x4 acc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ko[c][s], qf[t][s], acc[c], 0, 0, 0);
       }
-    mt = fmaxf(mt, x16(mt, gq));
-    mt = fmaxf(mt, x32(mt, gq));
-    const float mn = fmaxf(m, mt);
-    const bool live = mn != -INFINITY;  // some token of this row seen so far
-    const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
-    float sum = 0.f;
-    bf16x8_t pb;
+      float xv[8];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = live ? __builtin_amdgcn_exp2f(xv[e] - mn) : 0.f;
-      sum += pe;
-      pb[e] = (__bf16)pe;
-    }
-    l = l * alpha + sum;
-    m = mn;
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt] *= alpha;
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(w, dt), pb, o[dt], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = sel && ok && pos0 + 4 * c + i < my_len[t];
+          xv[4 * c + i] = vis ? acc[c][i] * a.c2 : -INFINITY;
+          mt = fmaxf(mt, xv[4 * c + i]);
+        }
+      mt = fmaxf(mt, x16(mt, gq));
+      mt = fmaxf(mt, x32(mt, gq));
+      const float mn = fmaxf(m[t], mt);
+      const bool live = mn != -INFINITY;  // some token of this row seen so far
+      const float alpha = live ? __builtin_amdgcn_exp2f(m[t] - mn) : 1.f;
+      float sum = 0.f;
+      bf16x8_t pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = live ? __builtin_amdgcn_exp2f(xv[e] - mn) : 0.f;
+        sum += pe;
+        pb[e] = (__bf16)pe;
+      }
+      l[t] = l[t] * alpha + sum;
+      m[t] = mn;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        o[t][dt] *= alpha;
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo[dt], pb, o[t][dt], 0, 0, 0);
+      }
     }
   };
 
@@ -338,20 +370,23 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
     }
   }
 
-  // 5. merge the four waves in LDS (the bitmaps are dead), write the partial
-  l += x16(l, gq);
-  l += x32(l, gq);
-  __syncthreads();
-  if (gq == 0) {
-    U.comb.m[wave][n] = m;
-    U.comb.l[wave][n] = bad ? __builtin_nanf("") : l;
-  }
+  // 5. per tile, merge the four waves in LDS (the bitmaps are dead) and
+  // write the partial (or, unsplit, the output)
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    *reinterpret_cast<f32x4*>(&U.comb.o[wave][n][16 * dt + 4 * gq]) = o[dt];
-  __syncthreads();
-  {
-    const int row = tid >> 4, c8 = tid & 15;
+  for (int t = 0; t < T; ++t) {
+    float lt = l[t];
+    lt += x16(lt, gq);
+    lt += x32(lt, gq);
+    __syncthreads();
+    if (gq == 0) {
+      U.comb.m[wave][n] = m[t];
+      U.comb.l[wave][n] = bad[t] ? __builtin_nanf("") : lt;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<f32x4*>(&U.comb.o[wave][n][16 * dt + 4 * gq]) = o[t][dt];
+    __syncthreads();
+    const int row = tid >> 4, c8 = tid & 15;  // row of the tile
     float M = -INFINITY;
     bool nan = false;
 #pragma unroll
@@ -368,12 +403,13 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
 #pragma unroll
       for (int d = 0; d < 8; ++d) acc8[d] += f * U.comb.o[w2][row][8 * c8 + d];
     }
+    const int irow = 16 * t + row;  // row of the item
     if (S == 1) {  // the whole union: the output itself
-      if (row < P * G) attn_finalize(a, r, h, row, c8, M, L, acc8, nan);
-      return;
+      if (irow < P * G) attn_finalize(a, r, h, irow, c8, M, L, acc8, nan);
+      continue;
     }
     if (nan) L = __builtin_nanf("");
-    float* part = a.ws + ((int64_t)item * S + split) * 16 * kPartFloats + row * kPartFloats;
+    float* part = a.ws + (((int64_t)item * S + split) * 16 * T + irow) * kPartFloats;
     if (c8 == 0) {
       part[128] = M;
       part[129] = L;
@@ -383,45 +419,49 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
   }
 }
 
-// Merge the splits of each item: row n = tid / 16 writes output dimensions
-// 8 (tid % 16) .. + 8 (and its lse).
-__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnArgs a) {
+// Merge the splits of each item: row 16 t + tid / 16 writes output
+// dimensions 8 (tid % 16) .. + 8 (and its lse), t over the item's T tiles.
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const AttnArgs a, int T) {
   const int item = blockIdx.x, tid = threadIdx.x;
-  const int row = tid >> 4, c8 = tid & 15;
   const int H = a.H, P = a.P, G = a.G, S = a.splits;
-  if (row >= P * G) return;
   const int r = item / H, h = item - r * H;
-  const float* part = a.ws + (int64_t)item * S * 16 * kPartFloats + row * kPartFloats;
-  float M = -INFINITY;
-  bool nan = false;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float* ps = part + (int64_t)s * 16 * kPartFloats;
-    M = fmaxf(M, ps[128]);
-    nan |= ps[129] != ps[129];
-  }
-  float L = 0.f, acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
+  const int c8 = tid & 15;
+  const int64_t step = (int64_t)16 * T * kPartFloats;  // one split further
+  for (int t = 0; t < T; ++t) {
+    const int row = 16 * t + (tid >> 4);
+    if (row >= P * G) break;  // rows grow with t
+    const float* part = a.ws + ((int64_t)item * S * 16 * T + row) * kPartFloats;
+    float M = -INFINITY;
+    bool nan = false;
 #pragma unroll 8
     for (int s = 0; s < S; ++s) {
-      const float* ps = part + (int64_t)s * 16 * kPartFloats;
-      const float f = (ps[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[128] - M);
-      L += f * ps[129];
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(ps + 8 * c8);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(ps + 8 * c8 + 4);
+      const float* ps = part + s * step;
+      M = fmaxf(M, ps[128]);
+      nan |= ps[129] != ps[129];
+    }
+    float L = 0.f, acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int s = 0; s < S; ++s) {
+        const float* ps = part + s * step;
+        const float f = (ps[128] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[128] - M);
+        L += f * ps[129];
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(ps + 8 * c8);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(ps + 8 * c8 + 4);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc8[d] += f * v0[d];
-        acc8[4 + d] += f * v1[d];
+        for (int d = 0; d < 4; ++d) {
+          acc8[d] += f * v0[d];
+          acc8[4 + d] += f * v1[d];
+        }
       }
     }
+    attn_finalize(a, r, h, row, c8, M, L, acc8, nan);
   }
-  attn_finalize(a, r, h, row, c8, M, L, acc8, nan);
 }
 
 namespace {
-// Both instantiations have the same register and LDS budget (one workgroup
-// a CU); the bf16 one is asked.
+// Every instantiation has the same register and LDS budget (one workgroup a
+// CU); the bf16 one-tile one is asked.
 int attn_resident_workgroups() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -430,7 +470,7 @@ int attn_resident_workgroups() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(attn_partial_kernel<IDX_K_BF16>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(attn_partial_kernel<IDX_K_BF16, 1>),
                                                    kAttnThreads, 0) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   cache[dev].store(cus * per_cu, std::memory_order_relaxed);
@@ -448,17 +488,33 @@ int attn_splits(int64_t items, int64_t max_union) {
   return (int)(s < 1 ? 1 : (s > IDX_ATTN_MAX_SPLITS ? IDX_ATTN_MAX_SPLITS : s));
 }
 
+namespace {
+template <int KVF, int T>
+void launch_partial(const AttnArgs& a, int64_t items, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_partial_kernel<KVF, T>), dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0, stream,
+                     a);
+}
+template <int KVF>
+void launch_partial_tiles(const AttnArgs& a, int64_t items, int T, hipStream_t stream) {
+  switch (T) {
+    case 1: launch_partial<KVF, 1>(a, items, stream); break;
+    case 2: launch_partial<KVF, 2>(a, items, stream); break;
+    case 3: launch_partial<KVF, 3>(a, items, stream); break;
+    default: launch_partial<KVF, 4>(a, items, stream); break;
+  }
+}
+}  // namespace
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.n_req * a.H;
   if (items == 0) return hipSuccess;
+  const int T = attn_tiles(a.P, a.G);
   if (a.kv_format == IDX_K_FP8_E4M3)
-    hipLaunchKernelGGL(attn_partial_kernel<IDX_K_FP8_E4M3>, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0,
-                       stream, a);
+    launch_partial_tiles<IDX_K_FP8_E4M3>(a, items, T, stream);
   else
-    hipLaunchKernelGGL(attn_partial_kernel<IDX_K_BF16>, dim3((unsigned)(items * a.splits)), dim3(kAttnThreads), 0,
-                       stream, a);
+    launch_partial_tiles<IDX_K_BF16>(a, items, T, stream);
   if (a.splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)items), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)items), dim3(kAttnThreads), 0, stream, a, T);
   return hipGetLastError();
 }
 

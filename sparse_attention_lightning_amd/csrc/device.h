@@ -59,6 +59,8 @@ struct AttnArgs {
 // Workgroups of the partial kernel per (request, KV head) item, for `items`
 // items whose unions hold at most `max_union` blocks.
 int attn_splits(int64_t items, int64_t max_union);
+// 16-row query tiles of an item's P x G rows.
+inline int attn_tiles(int P, int G) { return (P * G + 15) / 16; }
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
 hipError_t launch_score(const StepArgs& a, hipStream_t stream);       // any rows per request

@@ -26,7 +26,8 @@ IDX_MAX_REQ = 8192
 IDX_MAX_REQ_ROWS = 65536
 IDX_MAX_ROWS = 1 << 24
 IDX_NOALLOC_MAX_SCORES = 4 << 20
-IDX_ATTN_MAX_ROWS = 16
+IDX_ATTN_MAX_ROWS = 64
+IDX_ATTN_MAX_DRAFT = 16
 IDX_ATTN_MAX_IDS = 1024
 IDX_ATTN_MAX_SPLITS = 64
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error",

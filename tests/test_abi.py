@@ -148,7 +148,8 @@ ATTN_REFUSALS = [
     ("packed_queries", 0, I.IDX_E_SHAPE),
     ("kv_heads", 0, I.IDX_E_SHAPE),
     ("q_per_kv", 0, I.IDX_E_SHAPE),
-    ("q_per_kv", 5, I.IDX_E_PACK),           # 4 * 5 rows > 16
+    ("q_per_kv", 17, I.IDX_E_PACK),          # 4 * 17 rows > 64
+    ("packed_queries", 17, I.IDX_E_PACK),    # more than 16 draft rows
     ("n_req", -1, I.IDX_E_SHAPE),
     ("n_req", I.IDX_MAX_REQ + 1, I.IDX_E_SHAPE),
     ("max_blocks", I.IDX_MAX_BLOCKS + 1, I.IDX_E_SHAPE),
@@ -182,7 +183,7 @@ def test_attn_refusals(lib, field, value, code):
 def test_attn_workspace_query(lib):
     p = good_attn_params()
     assert lib.idx_sparse_attn_workspace(C.byref(p)) > 0
-    p.q_per_kv = 5
+    p.q_per_kv = 17
     assert lib.idx_sparse_attn_workspace(C.byref(p)) == I.IDX_E_PACK
     assert lib.idx_sparse_attn_workspace(None) == I.IDX_E_NULL
 
@@ -273,7 +274,7 @@ def test_binding_constants_match_header():
         assert m and int(m.group(1)) == getattr(I, name), name
     m = re.search(r"#define\s+IDX_MAX_ROWS\s+\(1 << (\d+)\)", text)
     assert m and (1 << int(m.group(1))) == I.IDX_MAX_ROWS
-    for name in ("IDX_ATTN_MAX_ROWS", "IDX_ATTN_MAX_IDS", "IDX_ATTN_MAX_SPLITS"):
+    for name in ("IDX_ATTN_MAX_ROWS", "IDX_ATTN_MAX_DRAFT", "IDX_ATTN_MAX_IDS", "IDX_ATTN_MAX_SPLITS"):
         m = re.search(rf"#define\s+{name}\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(I, name), name
     m = re.search(r"#define\s+IDX_NOALLOC_MAX_SCORES\s+\((\d+) << (\d+)\)", text)

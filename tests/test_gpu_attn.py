@@ -72,6 +72,12 @@ SHAPES = [  # (P, H, G, lens, topk, pads)
     (16, 1, 1, [513, 2049], 4, 0),
     (3, 2, 5, [90, 1030, 40], 7, 2),
     (4, 2, 2, [20000], 64, 0),
+    # more than one 16-row tile a (request, KV head): 20, 32, 48 and 64 rows
+    (5, 2, 4, [300, 2600], 6, 1),
+    (4, 2, 8, [0, 130, 5000], 8, 1),
+    (3, 2, 16, [700, 1500], 5, 0),
+    (4, 1, 16, [129, 9000], 12, 1),
+    (16, 1, 4, [2049, 600], 4, 0),
 ]
 
 
@@ -204,11 +210,11 @@ def test_attn_unsplit_batch(oracle):
 @pytest.mark.parametrize("case", range(12))
 def test_attn_random_shapes(oracle, case, kvf):
     """Seeded random shapes: draft rows, KV heads, query heads a KV head
-    (P G <= 16), request lengths (some 0, some straddling block ends),
+    (P G <= 64: one to four 16-row tiles), request lengths (some 0, some straddling block ends),
     selection sizes, graph pads, repeated and ignored ids."""
     rng = np.random.default_rng(900 + case)
     P = int(rng.integers(1, 9))
-    G = int(rng.integers(1, 16 // P + 1))
+    G = int(rng.integers(1, 64 // P + 1))
     H = int(rng.integers(1, 5))
     R = int(rng.integers(1, 7))
     lens = [int(x) for x in rng.choice([0, 1, 127, 128, 129, 700, 2048, 5000, 20000], size=R)]
@@ -345,21 +351,22 @@ def _subset(w: W.Workload, at: W.AttnInputs, ids: np.ndarray, reqs) -> tuple[dic
     return a, rows
 
 
-@pytest.mark.parametrize("cfg,reqs,kvf", [(3, "all", W.K_BF16), (4, "all", W.K_BF16), (3, "all", W.K_FP8_E4M3)],
-                         ids=["524k_fp8", "150k_nvfp4", "524k_fp8_fp8kv"])
-def test_attn_full_size(oracle, cfg, reqs, kvf):
+@pytest.mark.parametrize("cfg,reqs,kvf,G", [(3, "all", W.K_BF16, 4), (4, "all", W.K_BF16, 4),
+                                            (3, "all", W.K_FP8_E4M3, 4), (3, "all", W.K_FP8_E4M3, 16)],
+                         ids=["524k_fp8", "150k_nvfp4", "524k_fp8_fp8kv", "524k_fp8_fp8kv_g16"])
+def test_attn_full_size(oracle, cfg, reqs, kvf, G):
     """Every row of the 524K workload (its 32 requests and 3 graph pads:
     about 8 GB of selected bf16 K/V pages go to the oracle, 4 GB in fp8) and
     of the 150K one (64 requests, about 16 GB), against the oracle."""
     w = W.config(cfg, device="cuda")
     if reqs == "all":
         reqs = list(range(w.n_req))
-    say("attn full size", W.CONFIG_NAMES[cfg], "kv format", kvf, "requests", reqs)
+    say("attn full size", W.CONFIG_NAMES[cfg], "kv format", kvf, "query heads a KV head", G, "requests", reqs)
     if w.k_format == W.K_NVFP4:
         Hn.gpu_fp4_store(w)
     outs = Hn.gpu_outputs(w)
     I.idx_step(Hn.gpu_params(w, outs))
-    at = W.make_attn(w, 4, kv_format=kvf)
+    at = W.make_attn(w, G, kv_format=kvf)
     g = gpu_attn(w, at, outs["topk_ids"])
     ids = outs["topk_ids"].cpu().numpy()
     a, rows = _subset(w, at, ids, reqs)
@@ -368,7 +375,7 @@ def test_attn_full_size(oracle, cfg, reqs, kvf):
     # every real row saw something; pads none
     real = np.arange(w.n_real * w.packed_queries)
     assert np.isfinite(g["lse"][real]).all() and np.isneginf(g["lse"][w.n_real * w.packed_queries:]).all()
-    conftest.REPORT.append(f"sparse attention {w.name} ({'fp8' if kvf else 'bf16'} K/V): {len(reqs)} of {w.n_req} requests compared "
-                           f"({len(rows) * w.gqa * 4} query heads)")
+    conftest.REPORT.append(f"sparse attention {w.name} ({'fp8' if kvf else 'bf16'} K/V, {G} query heads a KV head): "
+                           f"{len(reqs)} of {w.n_req} requests compared ({len(rows) * w.gqa * G} query heads)")
     del at
     torch.cuda.empty_cache()

@@ -68,6 +68,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnBitWords = IDX_MAX_BLOCKS / 32;
 constexpr int kPartFloats = 132;  // per row of a partial: output [0, 128), max (log2 units), sum, pad
+constexpr float kAttnLazy = 8.f;  // log2 units a row's max may pass its reference before a rescale
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -160,6 +161,15 @@ __device__ __forceinline__ void attn_finalize(const AttnArgs& a, int r, int h, i
 template <int KVF, int T>
 constexpr int attn_ring() {
   return T == 1 ? AttnUnit<KVF>::kRing : (KVF == IDX_K_BF16 ? 2 : 3);
+}
+
+// Whether the running output is rescaled lazily (see compute below), by
+// measurement: it pays where the vector work and the registers are tight
+// (fp8 widening, several tiles, the tiles' outputs held in AGPRs), and costs
+// where they are not or where it pushes the register allocation into spills.
+template <int KVF, int T>
+constexpr bool attn_lazy() {
+  return KVF == IDX_K_FP8_E4M3 ? T >= 2 : T == 3;
 }
 
 template <int KVF, int T>
@@ -336,24 +346,34 @@ __global__ __launch_bounds__(kAttnThreads, IDX_ATTN_MIN_WGS) void attn_partial_k
         }
       mt = fmaxf(mt, x16(mt, gq));
       mt = fmaxf(mt, x32(mt, gq));
-      const float mn = fmaxf(m[t], mt);
-      const bool live = mn != -INFINITY;  // some token of this row seen so far
-      const float alpha = live ? __builtin_amdgcn_exp2f(m[t] - mn) : 1.f;
+      // Lazy (attn_lazy): the exponentials are taken against a reference m
+      // that moves only when some row's max passes it by more than
+      // kAttnLazy (then every row of the tile moves to its true max and its
+      // sums are rescaled), so most units leave the running output alone; a
+      // weight is then at most 2^kAttnLazy, well inside bf16 and fp32, and
+      // the final normalisation uses the same m.  Otherwise m follows the
+      // max at every unit.
+      if (!attn_lazy<KVF, T>() || __builtin_amdgcn_ballot_w64(mt > m[t] + kAttnLazy) != 0) {
+        const float mn = fmaxf(m[t], mt);
+        const float alpha = mn != -INFINITY ? __builtin_amdgcn_exp2f(m[t] - mn) : 1.f;
+        l[t] *= alpha;
+        m[t] = mn;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
+      }
+      const bool live = m[t] != -INFINITY;  // some token of this row seen so far
       float sum = 0.f;
       bf16x8_t pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = live ? __builtin_amdgcn_exp2f(xv[e] - mn) : 0.f;
+        const float pe = live ? __builtin_amdgcn_exp2f(xv[e] - m[t]) : 0.f;
         sum += pe;
         pb[e] = (__bf16)pe;
       }
-      l[t] = l[t] * alpha + sum;
-      m[t] = mn;
+      l[t] += sum;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        o[t][dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt)
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo[dt], pb, o[t][dt], 0, 0, 0);
-      }
     }
   };
 

@@ -129,6 +129,17 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
       L.ridx[k] = (uint8_t)j;
     }
   }
+  // query tiles (loaded before the page order is sorted, so their latency
+  // overlaps it): piece e = (request j, row, group of 8 values); kQPiecesPerThread per thread
+  u32x4 pc[kQPiecesPerThread];
+#pragma unroll
+  for (int i = 0; i < kQPiecesPerThread; ++i) {
+    const int e = tid + kThreads * i, j = e >> 8, row = (e >> 4) & 15, col = (e & 15) * 8;
+    pc[i] = u32x4{0u, 0u, 0u, 0u};
+    if (j < nreq && row < rows)
+      pc[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                              ((int64_t)(r0 + j) * rows + row) * kHeadDim + col);
+  }
   int pos[kPagesPerThread];  // hand-out position of each page
 #pragma unroll
   for (int m = 0; m < kPagesPerThread; ++m) pos[m] = tid + kThreads * m;
@@ -178,16 +189,6 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
       L.pid[pos[m]] = pk[m];
       L.sk[pos[m]] = (uint16_t)(k | (jk[m] << 10));
     }
-  }
-  // query tiles: piece e = (request j, row, group of 8 values); kQPiecesPerThread per thread
-  u32x4 pc[kQPiecesPerThread];
-#pragma unroll
-  for (int i = 0; i < kQPiecesPerThread; ++i) {
-    const int e = tid + kThreads * i, j = e >> 8, row = (e >> 4) & 15, col = (e & 15) * 8;
-    pc[i] = u32x4{0u, 0u, 0u, 0u};
-    if (j < nreq && row < rows)
-      pc[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                              ((int64_t)(r0 + j) * rows + row) * kHeadDim + col);
   }
   if constexpr (FMT == IDX_K_NVFP4) {
     __syncthreads();  // amax cleared

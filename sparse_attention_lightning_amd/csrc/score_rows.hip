@@ -206,51 +206,103 @@ struct BlockState {
   float s[kWaveTiles];
 };
 
-// Fold one half page's dot products (acc[u][t][e]: tile u's row n against
-// token 16 t + 4 g + e of the half, whose block position is pos0 + 16 t + e)
-// into the state.  len[u]: the length of tile u's row n.  FULL: every token
-// of the block is visible to every row of the wave (no masks).
-template <int MODE, bool FULL>
-__device__ __forceinline__ void fold_half(const f32x4 (*acc)[4], int pos0, const int* len, BlockState& st,
-                                          float c2) {
-#pragma unroll
-  for (int u = 0; u < kWaveTiles; ++u) {
-    float v[16];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * t + e] = (FULL || pos0 + 16 * t + e < len[u]) ? acc[u][t][e] : -INFINITY;
-    float am = v[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) am = max2(am, v[i]);
-    if constexpr (MODE == IDX_SCORE_MAX) {
-      st.m[u] = fmaxf(st.m[u], am);
-    } else if constexpr (FULL) {
-      // every token visible: the new max is finite (c2 > 0, finite dots)
-      const float mnew = fmaxf(st.m[u], am * c2);
-      float sum = st.s[u] * __builtin_amdgcn_exp2f(st.m[u] - mnew);  // 0 while m is -inf
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(v[i], c2, -mnew));
-      st.s[u] = sum;
-      st.m[u] = mnew;
-    } else {
-      const float mnew = fmaxf(st.m[u], am * c2);  // -inf * c2 = -inf
-      const float base = (mnew == -INFINITY) ? 0.f : mnew;  // nothing visible yet: every term is 0
-      float sum = st.s[u] * __builtin_amdgcn_exp2f(st.m[u] - base);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(v[i] * c2 - base);
-      st.s[u] = sum;
-      st.m[u] = mnew;
-    }
-  }
-}
-
 // Two partial log-sum-exp states (max m, sum s of 2^(v - m)) merged.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
   const float base = (mn == -INFINITY) ? 0.f : mn;
   s = s * __builtin_amdgcn_exp2f(m - base) + s2 * __builtin_amdgcn_exp2f(m2 - base);
   m = mn;
+}
+
+// lse terms v[0..N) (masked ones -inf) of tile u's row folded into the
+// block state against the lane's base ref[u], taking the terms' own max as
+// the new base when their sum against the old one leaves [2^-64, 2^64) (0
+// included: nothing visible, or no base yet).  The exact path for
+// fold_half's exceptions.
+template <int N>
+__device__ __forceinline__ void fold_terms(const float* v, int u, BlockState& st, float c2, float* ref) {
+  float base = ref[u], sum = 0.f;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {  // a second pass only after a new base
+    sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) sum += __builtin_amdgcn_exp2f(fmaf(v[i], c2, -base));
+    // on its own max the sum lies in [1, N], unless a dot is NaN or
+    // infinite: then the NaN it gives is kept
+    if (((sum >= 0x1p-64f) & (sum < 0x1p64f)) | (pass == 1)) break;
+    float am = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) am = max2(am, v[i]);
+    base = am * c2;  // -inf * c2 = -inf
+    if (base == -INFINITY) {  // nothing visible
+      sum = 0.f;
+      break;
+    }
+  }
+  if (sum != 0.f) {
+    ref[u] = base;
+    if (st.m[u] == base) {
+      st.s[u] += sum;
+    } else if (st.m[u] == -INFINITY) {
+      st.m[u] = base;
+      st.s[u] = sum;
+    } else {
+      lse_merge(st.m[u], st.s[u], base, sum);
+    }
+  }
+}
+
+// Fold one half page's dot products (acc[u][t][e]: tile u's row n against
+// token 16 t + 4 g + e of the half, whose block position is pos0 + 16 t + e)
+// into the state.  len[u]: the length of tile u's row n.  FULL: every token
+// of the block is visible to every row of the wave (no masks).
+// lse: each lane keeps a base ref[u] for tile u's row from block to block;
+// the half's terms 2^(c2 v - ref) are summed against it and, while the
+// sums stay in [2^-64, 2^64) and the block's state is on the same base,
+// simply added (no max, no rescaling).  Otherwise the exact path makes the
+// terms' own max the base.  c2 m + log2 s does not depend on the base, and
+// inside that window no term that matters underflows and none overflows.
+template <int MODE, bool FULL>
+__device__ __forceinline__ void fold_half(const f32x4 (*acc)[4], int pos0, const int* len, BlockState& st,
+                                          float c2, float* ref) {
+  float v[kWaveTiles][16];
+#pragma unroll
+  for (int u = 0; u < kWaveTiles; ++u)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[u][4 * t + e] = (FULL || pos0 + 16 * t + e < len[u]) ? acc[u][t][e] : -INFINITY;
+  if constexpr (MODE == IDX_SCORE_MAX) {
+#pragma unroll
+    for (int u = 0; u < kWaveTiles; ++u) {
+      float am = v[u][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) am = max2(am, v[u][i]);
+      st.m[u] = fmaxf(st.m[u], am);
+    }
+  } else {
+    float sum[kWaveTiles];
+    bool fast = true;
+#pragma unroll
+    for (int u = 0; u < kWaveTiles; ++u) {
+      const float nb = -ref[u];
+      sum[u] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum[u] += __builtin_amdgcn_exp2f(fmaf(v[u][i], c2, nb));
+      fast = fast & (sum[u] >= 0x1p-64f) & (sum[u] < 0x1p64f) & ((st.m[u] == ref[u]) | (st.m[u] == -INFINITY));
+    }
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {  // every lane: its sums on its bases, as they are
+#pragma unroll
+      for (int u = 0; u < kWaveTiles; ++u) {
+        st.s[u] = ((st.m[u] == -INFINITY) ? 0.f : st.s[u]) + sum[u];
+        st.m[u] = ref[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kWaveTiles; ++u) fold_terms<16>(v[u], u, st, c2, ref);
+    }
+  }
 }
 
 // Reduce the values of tiles Q .. Q+3 over the four lane groups (lanes n,
@@ -388,6 +440,9 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
     }
   }
   const float c2 = (MODE == IDX_SCORE_LSE) ? a.sm_scale * 1.44269504088896341f : 0.f;
+  float ref[kWaveTiles];  // lse: each tile row's base for its terms (+inf: none yet)
+#pragma unroll
+  for (int u = 0; u < kWaveTiles; ++u) ref[u] = INFINITY;
   // the item's blocks gl .. gh of granule G (blocks 16 G .. 16 G + 15; at
   // the extent's end padded with -inf to the granule's end), written by the
   // whole workgroup: four lanes a row, 16 rows an instruction
@@ -443,7 +498,8 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   // the page's eight 16-token tiles against the wave's four query tiles
   // (acc[u]: tile u's row n x tokens 16 T + 4 g .. +3), the next tile's K
   // operands read while this one's MFMAs run; max folds each tile as it is
-  // done, lse a half page at a time (one rescaling exp per 16 values)
+  // done, lse a half page at a time (against each row's base: no max, no
+  // rescaling)
   auto page_dots = [&](const u32x4* P, auto full_tag, int b, BlockState& st, auto&& mid) {
     constexpr bool FULL = decltype(full_tag)::value;
     u32x4 ko[2][4];
@@ -473,7 +529,7 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
       } else {
 #pragma unroll
         for (int u = 0; u < kWaveTiles; ++u) acch[u][T & 3] = acc[u];
-        if ((T & 3) == 3) fold_half<MODE, FULL>(acch, pos0 - 48, len, st, c2);
+        if ((T & 3) == 3) fold_half<MODE, FULL>(acch, pos0 - 48, len, st, c2, ref);
       }
       if constexpr (MODE == IDX_SCORE_MAX)
         if (T == IDX_ROWS_STORE_AT) mid();

@@ -5,7 +5,8 @@
 // 6; two codes a byte, the even element in the low nibble; 64 B payload and
 // 8 B scales per key, written at the key's slot.
 //
-// Eight threads per key, one per 16-element group.  amax / 6 is an IEEE fp32
+// Eight threads per key, one per 16-element group (from 65,536 keys on, four
+// threads a key, two groups each).  amax / 6 is an IEEE fp32
 // division; its E4M3 rounding (nearest, ties to even, clamped at 448) is done
 // on the bits.  Codes come from exact comparisons of |x| with the e2m1
 // midpoints times the scale (each product is exact in fp32), which is the
@@ -17,6 +18,12 @@ namespace idx {
 
 #ifndef IDX_STORE_UNROLL
 #define IDX_STORE_UNROLL 1  // 16-element groups a thread loads before it quantizes them
+#endif
+#ifndef IDX_STORE_WIDE_MIN
+#define IDX_STORE_WIDE_MIN 65536  // keys from which four lanes a key store them (fewer, wider accesses)
+#endif
+#ifndef IDX_STORE_WIDE_LANES
+#define IDX_STORE_WIDE_LANES 4  // lanes a key of the large-store kernel (4 or 2)
 #endif
 #ifndef IDX_STORE_NT
 #define IDX_STORE_NT 0      // 1: non-temporal staging loads and payload / scale stores
@@ -38,10 +45,9 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// Quantize one 16-element group (this lane's) of a key and store it; the
-// key's eight lanes call this together.
-__device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot, int grp, uint8_t* payload,
-                                               uint8_t* scales) {
+// One 16-element group: its E4M3 scale byte and its 16 codes, two a byte
+// (the even element in the low nibble) in packed[0..1].
+__device__ __forceinline__ uint32_t quantize16(u32x4 w0, u32x4 w1, uint32_t* packed) {
   const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
   float x[16];
   float amax = 0.0f;
@@ -61,7 +67,7 @@ __device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot,
   // keep the seven products in registers: otherwise the compiler selects the
   // constant per value and multiplies it again
   asm volatile("" : "+v"(m0), "+v"(m1), "+v"(m2), "+v"(m3), "+v"(m4), "+v"(m5), "+v"(m6));
-  uint32_t packed[2] = {0u, 0u};
+  packed[0] = packed[1] = 0u;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const float a = fabsf(x[j]);
@@ -73,6 +79,15 @@ __device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot,
     const uint32_t code = mag | ((__float_as_uint(x[j]) >> 28) & 8u);
     packed[j >> 3] |= code << (4 * (j & 7));
   }
+  return sb;
+}
+
+// Quantize one group (this lane's) of a key and store it; the key's eight
+// lanes call this together.
+__device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot, int grp, uint8_t* payload,
+                                               uint8_t* scales) {
+  uint32_t packed[2];
+  const uint32_t sb = quantize16(w0, w1, packed);
   u32x2* pdst = reinterpret_cast<u32x2*>(payload + slot * 64 + 8 * grp);
   // the key's 8 scale bytes as one 8-byte store from its first lane: each
   // quad of lanes ORs its bytes into a word, lane 4 hands its word to lane 0
@@ -87,6 +102,51 @@ __device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot,
   } else {
     *pdst = u32x2{packed[0], packed[1]};
     if (grp == 0) *sdst = u32x2{word, hi};
+  }
+}
+
+// KL lanes a key, 8 / KL groups a lane: lane q of the key loads its 256 / KL
+// bytes of staging and stores its 64 / KL bytes of payload as 16-byte
+// pieces; lane 0 of the key stores the 8 scale bytes.  For large stores:
+// fewer, wider accesses a key.  The whole 150K NVFP4 pool (9.87 M keys)
+// stored in 692 us with four lanes a key, 727 with eight (the other kernel)
+// and 769 with two (medians of 36 interleaved calls, one box); 256 keys keep
+// eight lanes a key (one group a lane in series is the short chain there).
+template <int KL>
+__global__ __launch_bounds__(kStoreThreads) void fp4_store_wide_kernel(
+    const uint16_t* __restrict__ staging, int64_t n_tokens, int64_t stride,
+    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ payload,
+    uint8_t* __restrict__ scales, int64_t n_slots) {
+  constexpr int NG = 8 / KL;  // groups a lane
+  const int64_t n_items = n_tokens * KL;
+  const int64_t step = (int64_t)gridDim.x * kStoreThreads;
+  for (int64_t item = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x; item < n_items; item += step) {
+    const int64_t t = item / KL;
+    const int q = (int)(item % KL);
+    const u32x4* src = reinterpret_cast<const u32x4*>(staging + t * stride + 16 * NG * q);
+    u32x4 w[2 * NG];
+#pragma unroll
+    for (int i = 0; i < 2 * NG; ++i) w[i] = src[i];
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= n_slots) continue;  // the key's lanes skip it together
+    uint32_t p[2 * NG], sw = 0;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) sw |= quantize16(w[2 * gi], w[2 * gi + 1], &p[2 * gi]) << (8 * (gi & 3));
+#pragma unroll
+    for (int i = 0; i < NG / 2; ++i)
+      *reinterpret_cast<u32x4*>(payload + slot * 64 + 16 * (NG / 2) * q + 16 * i) =
+          u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+    uint32_t lo, hi;
+    if constexpr (KL == 4) {  // lanes 0, 1 of the quad make bytes 0..3, lanes 2, 3 bytes 4..7
+      uint32_t word = sw << (16 * (q & 1));
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+      lo = word;
+      hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else {  // lane 0 bytes 0..3, lane 1 bytes 4..7
+      lo = sw;
+      hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sw, 0xB1, 0xF, 0xF, false);
+    }
+    if (q == 0) *reinterpret_cast<u32x2*>(scales + slot * 8) = u32x2{lo, hi};
   }
 }
 
@@ -135,6 +195,14 @@ hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t s
                             const int64_t* slot_mapping, uint8_t* payload, uint8_t* scales,
                             int64_t n_slots, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
+  if (n_tokens >= IDX_STORE_WIDE_MIN) {
+    constexpr int KL = IDX_STORE_WIDE_LANES;
+    const int64_t want = (n_tokens * KL + kStoreThreads - 1) / kStoreThreads;
+    const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(fp4_store_wide_kernel<KL>, dim3(grid), dim3(kStoreThreads), 0, stream, staging,
+                       n_tokens, stride, slot_mapping, payload, scales, n_slots);
+    return hipGetLastError();
+  }
   const int64_t want = (n_tokens * 8 + (int64_t)kStoreThreads * IDX_STORE_UNROLL - 1) /
                        ((int64_t)kStoreThreads * IDX_STORE_UNROLL);
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);

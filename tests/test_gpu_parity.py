@@ -90,10 +90,13 @@ def test_invalid_page_ids(oracle):
 # ---------------------------------------------------------------------------
 # NVFP4 store
 # ---------------------------------------------------------------------------
-def test_fp4_store_exhaustive_rounding(oracle):
+@pytest.mark.parametrize("copies", [1, 2], ids=["eight_lanes", "four_lanes"])
+def test_fp4_store_exhaustive_rounding(oracle, copies):
     """Every bf16 x with |x| <= 6 s at every positive finite E4M3 scale s
-    (4.2M values) stored by the GPU and by the oracle: identical bytes."""
-    say("fp4 store exhaustive rounding set")
+    (4.2M values) stored by the GPU and by the oracle: identical bytes.  The
+    set is 39,162 keys; twice over (78,324) it goes through the kernel that
+    stores 65,536 keys or more four lanes a key."""
+    say("fp4 store exhaustive rounding set", copies)
     fp8 = pins.fp8_values_torch()
     pos = np.arange(0, 0x7F80, dtype=np.uint32)
     posv = (pos << 16).view(np.float32)
@@ -112,7 +115,7 @@ def test_fp4_store_exhaustive_rounding(oracle):
     groups.append(g2)
     groups = np.concatenate(groups)
     groups = np.concatenate([groups, np.zeros(((-len(groups)) % 8, 16), np.uint16)])
-    st = groups.reshape(-1, 128)
+    st = np.concatenate([groups.reshape(-1, 128)] * copies)
     n = st.shape[0]
     perm = np.random.default_rng(3).permutation(n).astype(np.int64)   # scattered slots
     pay_o = np.full((n, 64), 0x5A, np.uint8)
@@ -127,11 +130,13 @@ def test_fp4_store_exhaustive_rounding(oracle):
     assert np.array_equal(pay_g.cpu().numpy(), pay_o), "payload bytes differ"
 
 
-def test_fp4_store_skips_and_strides(oracle):
+@pytest.mark.parametrize("n", [3000, 80000], ids=["eight_lanes", "four_lanes"])
+def test_fp4_store_skips_and_strides(oracle, n):
     """Negative and out-of-range slots are skipped (their bytes keep the
-    fill); a staging row stride larger than 128 is honoured."""
-    say("fp4 store skip/stride")
-    n, n_slots = 3000, 2500
+    fill); a staging row stride larger than 128 is honoured.  Both store
+    kernels (four lanes a key from 65,536 keys)."""
+    say("fp4 store skip/stride", n)
+    n_slots = n - 500
     rng = np.random.default_rng(5)
     big = torch.randn(n, 200, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
     st = big[:, :128]

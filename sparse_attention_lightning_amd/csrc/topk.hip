@@ -6,8 +6,10 @@
 // nb are always taken and the remaining topk - |forced| slots go to the
 // highest block scores, ties to the lower block id.  Selection is exact.
 //
-// One workgroup of 512 threads per (row, head).  Thread t owns the contiguous
-// blocks [t*C, t*C + C), C = ceil(max_blocks / 512) <= 8 or 16 (rounded up to
+// One workgroup of NT threads per (row, head): 256 for rows of at most 2,048
+// blocks, else 512 (1,024 rows of 1,184 blocks: 7.5 against 9.4 us; 560 rows
+// of 4,096: 9.8 against 9.2 us).  Thread t owns the contiguous blocks
+// [t*C, t*C + C), C = ceil(max_blocks / NT) <= 8 or 16 (rounded up to
 // a multiple of 4 when rows are 16-byte aligned), and loads their scores into
 // registers first thing; the row's slot and length are fetched before them and
 // the score loads do not wait for them.  Keys are 32-bit integers whose
@@ -16,7 +18,7 @@
 // blocks in two bit masks.  A radix select over the competing keys finds the
 // k-th largest key T, k = topk - |forced|: it starts at the highest bit where
 // those keys differ, takes up to 11 bits a pass into a 2,048-bin LDS histogram
-// (thread t scans and clears 4 bins), and stops once the chosen bin holds
+// (thread t scans and clears 2,048 / NT bins), and stops once the chosen bin holds
 // exactly the keys still needed.  One packed scan of (taken-for-sure,
 // equal-to-T) counts then gives every thread its output positions, so ids
 // leave in ascending order without a sort.  Reductions and scans inside a
@@ -43,8 +45,8 @@
 
 namespace idx {
 
-constexpr int kTopkThreads = 512;  // the workgroup kernel: one row a workgroup
-constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkThreads = 512;        // the workgroup kernel: one row a workgroup
+constexpr int kTopkThreadsNarrow = 256;  // its threads for rows of at most 2,048 blocks
 constexpr int kBallotThreads = 256;  // the one-wave kernel: four rows a workgroup
 constexpr int kBallotWaves = kBallotThreads / 64;
 
@@ -74,6 +76,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
 
 // Exclusive prefix sum over the workgroup; *total gets the sum of all.  One
 // barrier: the caller must not reuse `wave_tot` before another barrier.
+template <int NW>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_inclusive_sum(v);
@@ -81,7 +84,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_tot, u
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t t = wave_tot[w];
     before += (w < wave) ? t : 0u;
     all += t;
@@ -114,11 +117,13 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
   return combine<OP>(combine<OP>(a, b), combine<OP>(c, d));
 }
 
-// PER: blocks per thread (8 covers max_blocks <= 4096, 16 the full limit).
-template <int PER>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
+// PER: blocks per thread, NT threads (8 x 256 covers max_blocks <= 2048, 8 x 512
+// <= 4096, 16 x 512 the full limit).
+template <int PER, int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(const StepArgs a) {
+  constexpr int kTopkWaves = NT / 64;
   static_assert(PER <= 32, "per-thread block sets are 32-bit masks");
-  constexpr int kBins = 2048, kBinsPerThread = kBins / kTopkThreads;  // 4
+  constexpr int kBins = 2048, kBinsPerThread = kBins / NT;  // 4 or 8
   __shared__ u32x4 hist4[kBins / 4];
   uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
   __shared__ uint32_t red[3][kTopkWaves];
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   // this thread's scores (they do not wait for the length); 16-byte loads
   // when every thread's range starts 16-byte aligned
   const bool vec = (MB % 4) == 0 && (reinterpret_cast<uintptr_t>(a.block_scores) & 15u) == 0;
-  const int C = vec ? ((MB / 4 + kTopkThreads - 1) / kTopkThreads) * 4 : (MB + kTopkThreads - 1) / kTopkThreads;
+  const int C = vec ? ((MB / 4 + NT - 1) / NT) * 4 : (MB + NT - 1) / NT;
   const int b0 = tid * C;
   float sv[PER];
   if (vec) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
     for (int j = 0; j < PER; ++j) sv[j] = (j < C && b0 + j < MB) ? bs[b0 + j] : 0.0f;
   }
 
-  // this thread's 4 bins, highest digits first: bins [kBins - 4(t+1), kBins - 4 t)
+  // this thread's bins, highest digits first: [kBins - B(t+1), kBins - B t), B = kBinsPerThread
   const int bin0 = kBins - kBinsPerThread * (tid + 1);
 #pragma unroll
   for (int q = 0; q < kBinsPerThread / 4; ++q) hist4[bin0 / 4 + q] = u32x4{0u, 0u, 0u, 0u};
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   float* sc = a.topk_scores + (int64_t)o * K;
 
   if (nb <= K) {
-    for (int t = tid; t < K; t += kTopkThreads) {
+    for (int t = tid; t < K; t += NT) {
       ids[t] = t < nb ? t : -1;
       sc[t] = t < nb ? bs[t] : -INFINITY;
     }
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
         if (((cand >> j) & 1u) && match) atomicAdd(&hist[(key[j] >> lo) & dmask], 1u);
       }
       __syncthreads();
-      // this thread's 4 bins (descending digits) into registers, then clear them
+      // this thread's bins (descending digits) into registers, then clear them
       uint32_t h[kBinsPerThread];
 #pragma unroll
       for (int q = 0; q < kBinsPerThread / 4; ++q) {
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
 #pragma unroll
       for (int q = 0; q < kBinsPerThread; ++q) local += h[q];
       uint32_t tot;
-      const uint32_t above = block_scan(local, wave_tot[0], &tot);
+      const uint32_t above = block_scan<kTopkWaves>(local, wave_tot[0], &tot);
       if (above < want && want <= above + local) {
         // the cut is in this thread's bins: walk them from the highest digit
         uint32_t run = above;
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const StepArgs a) {
   }
   uint32_t total;
   const uint32_t packed = ((uint32_t)__builtin_popcount(sure) << 16) | (uint32_t)__builtin_popcount(eq);
-  const uint32_t ex = block_scan(packed, wave_tot[1], &total);
+  const uint32_t ex = block_scan<kTopkWaves>(packed, wave_tot[1], &total);
   // equal keys taken by lower threads, and how many are left for this one
   // (no conditional subtraction here: hipcc's optimizer turned the form
   // `want > x ? min(n, want - x) : 0` into one that dropped the min below)
@@ -517,10 +522,13 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   // rows of 12)
   if (a.max_blocks <= 16 * 64 && (grid >= IDX_TOPK_BALLOT_ROWS || a.max_blocks <= 64))
     launch_ballot<1>(a, grid, stream);
+  else if (a.max_blocks <= 8 * kTopkThreadsNarrow)
+    hipLaunchKernelGGL((topk_kernel<8, kTopkThreadsNarrow>), dim3((unsigned)grid), dim3(kTopkThreadsNarrow), 0, stream,
+                       a);
   else if (a.max_blocks <= 8 * kTopkThreads)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
+    hipLaunchKernelGGL((topk_kernel<8, kTopkThreads>), dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
+    hipLaunchKernelGGL((topk_kernel<16, kTopkThreads>), dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

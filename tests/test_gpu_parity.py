@@ -243,10 +243,13 @@ def test_exact_tie_lower_id():
 def test_topk_synthetic_scores_exact(oracle, R):
     """Selection alone on the same fp32 scores (many exact ties, NaN, -0):
     ids and scores identical to the oracle's.  1,100 rows of at most 1,024
-    blocks take the one-wave-per-row kernel, 48 rows the workgroup kernel."""
+    blocks take the one-wave-per-row kernel, 48 rows the workgroup kernel
+    (256 threads up to 2,048 blocks, 512 beyond, 16 blocks a thread past
+    4,096)."""
     rng = np.random.default_rng(9)
     for MB, topk, init, local in [(40, 8, 1, 2), (300, 64, 1, 2), (1000, 64, 0, 0), (8192, 64, 3, 5),
-                                  (700, 1, 1, 0), (50, 50, 2, 2), (1024, 64, 1, 2)]:
+                                  (700, 1, 1, 0), (50, 50, 2, 2), (1024, 64, 1, 2), (2048, 64, 1, 2),
+                                  (2052, 100, 2, 3), (4096, 64, 1, 2), (1190, 64, 1, 2)]:
         say("topk synthetic", R, MB, topk, init, local)
         nb = rng.integers(0, MB + 1, size=R)
         nb[:3] = [MB, topk, topk + 1]

@@ -296,15 +296,19 @@ def test_fp4_equals_bf16_of_dequant():
     assert np.max(np.abs(a[f] - b[f]) / np.maximum(np.abs(b[f]), 1)) <= 1e-5
 
 
-def test_repeat_launches_identical():
+@pytest.mark.parametrize("mode", ["max", "lse"])
+@pytest.mark.parametrize("P,H", [(4, 4), (40, 4)], ids=["one_tile", "many_rows"])
+def test_repeat_launches_identical(P, H, mode):
     """Repeated launches give bit-identical outputs (the graph-replay
-    analogue of sglang PR 45451's tests)."""
-    say("determinism")
-    w = W.make(name="det", R=5, P=4, H=4, k_format=W.K_FP8_E4M3, req_len=[100, 900, 4000, 1, 2222],
+    analogue of sglang PR 45451's tests), in both kernels and both score
+    modes (the many-rows lse fold keeps a base per row across blocks)."""
+    say("determinism", P, H, mode)
+    m = LSE if mode == "lse" else {}
+    w = W.make(name="det", R=5, P=P, H=H, k_format=W.K_FP8_E4M3, req_len=[100, 900, 4000, 1, 2222],
                topk=8, init_blocks=1, local_blocks=2, seed=91, device="cuda")
-    first = Hn.gpu_step(w)
+    first = Hn.gpu_step(w, **m)
     outs = Hn.gpu_outputs(w)
-    p = Hn.gpu_params(w, outs)
+    p = Hn.gpu_params(w, outs, **m)
     for _ in range(50):
         I.idx_step(p)
     torch.cuda.synchronize()

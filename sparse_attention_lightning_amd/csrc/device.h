@@ -130,12 +130,16 @@ template <int THREADS>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // inclusive sum over the wave with DPP: row_shr within rows of 16 lanes,
+  // then row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3
+  // (a shifted-out or masked-off lane adds 0)
   uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x143, 0xC, 0xF, false);  // row_bcast:31
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
   uint32_t before = 0, all = 0;

@@ -103,7 +103,11 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
     rq.p0 = (int)pre[r];
     rq.nbg = (int)(pre[r + 1] - pre[r]);
     int lm = INT_MAX;
-    for (int j = 0; j < P; ++j) lm = min(lm, clamp_len(a.row_len[r * P + j], MB));
+    int lv[kTileRows];  // P <= 16: every load issues before any is used
+#pragma unroll
+    for (int j = 0; j < kTileRows; ++j) lv[j] = a.row_len[r * P + min(j, P - 1)];
+#pragma unroll
+    for (int j = 0; j < kTileRows; ++j) lm = min(lm, clamp_len(lv[j], MB));  // repeats of row P - 1 change nothing
     rq.lmin = lm;
     rq.sigma = 0;
     L.amax[tid] = 0;
@@ -406,7 +410,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
     if (r < R) {
       const int slot = a.req_slot[r];
       int lmax = 0;  // loaded without waiting for the slot
-      for (int j = 0; j < P; ++j) lmax = max(lmax, clamp_len(a.row_len[r * P + j], MB));
+      int lv[kTileRows];  // P <= 16: every load issues before any is used
+#pragma unroll
+      for (int j = 0; j < kTileRows; ++j) lv[j] = a.row_len[r * P + min(j, P - 1)];
+#pragma unroll
+      for (int j = 0; j < kTileRows; ++j) lmax = max(lmax, clamp_len(lv[j], MB));  // repeats change nothing
       slot_of[r] = slot;
       if (slot >= 0 && slot < a.n_slot_rows) nbg = (uint32_t)blocks_of(lmax);
     }

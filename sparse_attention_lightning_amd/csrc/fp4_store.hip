@@ -110,8 +110,9 @@ __device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot,
 // pieces; lane 0 of the key stores the 8 scale bytes.  For large stores:
 // fewer, wider accesses a key.  The whole 150K NVFP4 pool (9.87 M keys)
 // stored in 692 us with four lanes a key, 727 with eight (the other kernel)
-// and 769 with two (medians of 36 interleaved calls, one box); 256 keys keep
-// eight lanes a key (one group a lane in series is the short chain there).
+// and 769 with two (medians of 36 interleaved calls, one box).  A small store
+// (a step's 256 new keys) keeps eight lanes a key: with one group a lane its
+// chain is shortest, and a small grid has no bandwidth to win.
 template <int KL>
 __global__ __launch_bounds__(kStoreThreads) void fp4_store_wide_kernel(
     const uint16_t* __restrict__ staging, int64_t n_tokens, int64_t stride,

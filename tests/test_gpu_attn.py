@@ -207,7 +207,7 @@ def test_attn_unsplit_batch(oracle):
 
 
 @KVF
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(32))
 def test_attn_random_shapes(oracle, case, kvf):
     """Seeded random shapes: draft rows, KV heads, query heads a KV head
     (P G <= 64: one to four 16-row tiles), request lengths (some 0, some straddling block ends),

@@ -9,7 +9,10 @@
 //
 // Work split.  One workgroup of eight waves per CU stays resident for the
 // whole launch.  The pages of the step, in (request, block) order, are cut
-// into equal contiguous shares, one per workgroup, and a workgroup takes its
+// into contiguous shares, one per workgroup: equal ones, or, for long shares
+// once every workgroup has reported, sized by the rate each XCD reached on
+// the previous launch (XCDs stream at rates a few per cent apart, so equal
+// shares leave the slower ones finishing last).  A workgroup takes its
 // share in rounds of at most 768 pages touching at most 8 requests.  A round
 // first stages its page ids, the query tiles and row lengths of its requests
 // in LDS; the eight waves then take pages one at a time from an LDS counter,
@@ -42,6 +45,12 @@ namespace idx {
 #endif
 #ifndef IDX_SCORE_SORT_MIN
 #define IDX_SCORE_SORT_MIN 32       // rounds with fewer pages keep round order
+#endif
+#ifndef IDX_SCORE_ADAPT
+#define IDX_SCORE_ADAPT 1        // shares follow the XCDs' measured page rates (see below)
+#endif
+#ifndef IDX_SCORE_ADAPT_MIN
+#define IDX_SCORE_ADAPT_MIN 384  // pages a workgroup from which they do (below, fixed costs blur the rates)
 #endif
 #ifndef IDX_SCORE_NT_OUT
 #define IDX_SCORE_NT_OUT 0       // 1: non-temporal block-score stores
@@ -390,6 +399,13 @@ __device__ __forceinline__ int request_of(const uint32_t* pre, int R, uint32_t x
   return lo;
 }
 
+// Each workgroup's page rate on its last launch (pages a 10 ns tick, 2^16
+// fixed point; 0: none yet), per device.  Workgroup b runs on XCD b % 8; the
+// next launch sizes each XCD's shares in proportion to its workgroups' summed
+// rates.  Calls racing on it change only how the pages are shared, never a
+// result.
+__device__ uint32_t g_wg_rate[1024];
+
 template <int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   extern __shared__ uint32_t pre[];  // n_req + 1 prefix sums of per-request block counts, then n_req slots
@@ -427,9 +443,44 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   __syncthreads();
   const uint32_t N = uniform(carry);
 
-  // 2. this workgroup's equal share of the step's pages, in rounds
-  const uint32_t lo = (uint32_t)((uint64_t)blockIdx.x * N / gridDim.x);
-  const uint32_t hi = (uint32_t)((uint64_t)(blockIdx.x + 1) * N / gridDim.x);
+  // 2. this workgroup's share of the step's pages, in rounds: equal, or in
+  // proportion to its XCD's measured rate
+  const int G = gridDim.x, b = blockIdx.x;
+  uint32_t lo = (uint32_t)((uint64_t)b * N / G);
+  uint32_t hi = (uint32_t)((uint64_t)(b + 1) * N / G);
+  const bool adapt = IDX_SCORE_ADAPT && (G % 8) == 0 && G <= 1024 && N >= (uint32_t)IDX_SCORE_ADAPT_MIN * G;
+  if (adapt) {
+    uint32_t* xs = reinterpret_cast<uint32_t*>(&L.stage[0][0]);  // [0, 8): summed rates, [8, 16): known
+    if (tid < 16) xs[tid] = 0;
+    __syncthreads();
+    for (int w = tid; w < G; w += kThreads) {
+      const uint32_t v = g_wg_rate[w];
+      atomicAdd(&xs[w & 7], v);
+      atomicAdd(&xs[8 + (w & 7)], v != 0u ? 1u : 0u);
+    }
+    __syncthreads();
+    uint64_t wx[8], w8 = 0;
+    bool known = true;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      wx[x] = uniform(xs[x]);
+      known = known && uniform(xs[8 + x]) == (uint32_t)(G / 8);
+      w8 += wx[x];
+    }
+    __syncthreads();  // the stage is the round's again
+    if (known && w8 > 0) {
+      auto cum = [&](int c) -> uint64_t {  // weight of workgroups 0 .. c - 1
+        uint64_t t = (uint64_t)(c / 8) * w8;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) t += (x < (c & 7)) ? wx[x] : 0u;
+        return t;
+      };
+      const uint64_t total = (uint64_t)(G / 8) * w8;
+      lo = (uint32_t)((uint64_t)N * cum(b) / total);
+      hi = (uint32_t)((uint64_t)N * cum(b + 1) / total);
+    }
+  }
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   if (a.n_pages == 0) {
     // nothing can be read: every visible block is NaN
     for (uint32_t u = lo + tid; u < hi; u += kThreads) {
@@ -460,6 +511,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
       write_round(a, L, rl, np, tid);
       __syncthreads();
       rl = rh;
+    }
+  }
+
+  if (adapt) {
+    const uint64_t dt = __builtin_amdgcn_s_memrealtime() - t_start;
+    // below 2^20, so that N (< 2^26 pages) times the summed weights stays in 64 bits
+    const uint32_t rate = (uint32_t)min((uint64_t)(hi - lo) * 65536u / (dt > 0 ? dt : 1), (uint64_t)0xFFFFF);
+    if (tid == 0 && hi > lo) {
+      const uint32_t old = g_wg_rate[b];
+      g_wg_rate[b] = old ? (old + rate) / 2 : rate;
     }
   }
 

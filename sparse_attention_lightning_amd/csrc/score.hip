@@ -9,8 +9,8 @@
 //
 // Work split.  One workgroup of eight waves per CU stays resident for the
 // whole launch.  The pages of the step, in (request, block) order, are cut
-// into contiguous shares, one per workgroup: equal ones, or, for long shares
-// once every workgroup has reported, sized by the rate each XCD reached on
+// into contiguous shares, one per workgroup: equal ones, or, for shares of
+// 4 MiB of K and more once every workgroup has reported, sized by the rate each XCD reached on
 // the previous launch (XCDs stream at rates a few per cent apart, so equal
 // shares leave the slower ones finishing last).  A workgroup takes its
 // share in rounds of at most 768 pages touching at most 8 requests.  A round
@@ -49,9 +49,9 @@ namespace idx {
 #ifndef IDX_SCORE_ADAPT
 #define IDX_SCORE_ADAPT 1        // shares follow the XCDs' measured page rates (see below)
 #endif
-#ifndef IDX_SCORE_ADAPT_MIN
-#define IDX_SCORE_ADAPT_MIN 384  // pages a workgroup from which they do (below, fixed costs blur the rates)
-#endif
+#ifndef IDX_SCORE_ADAPT_MIN_BYTES
+#define IDX_SCORE_ADAPT_MIN_BYTES (4 << 20)  // K bytes a workgroup from which they do (below, fixed
+#endif                                       // costs and vector work blur the XCDs' memory rates)
 #ifndef IDX_SCORE_NT_OUT
 #define IDX_SCORE_NT_OUT 0       // 1: non-temporal block-score stores
 #endif
@@ -448,7 +448,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   const int G = gridDim.x, b = blockIdx.x;
   uint32_t lo = (uint32_t)((uint64_t)b * N / G);
   uint32_t hi = (uint32_t)((uint64_t)(b + 1) * N / G);
-  const bool adapt = IDX_SCORE_ADAPT && (G % 8) == 0 && G <= 1024 && N >= (uint32_t)IDX_SCORE_ADAPT_MIN * G;
+  constexpr uint64_t kPageKBytes = (uint64_t)kBlock * (Fmt<FMT>::kRowBytes + (FMT == IDX_K_NVFP4 ? 8 : 0));
+  const bool adapt = IDX_SCORE_ADAPT && (G % 8) == 0 && G <= 1024 &&
+                     (uint64_t)N * kPageKBytes >= (uint64_t)IDX_SCORE_ADAPT_MIN_BYTES * G;
   if (adapt) {
     uint32_t* xs = reinterpret_cast<uint32_t*>(&L.stage[0][0]);  // [0, 8): summed rates, [8, 16): known
     if (tid < 16) xs[tid] = 0;

@@ -40,18 +40,20 @@
 // and when an item has scored all its blocks of a granule the workgroup
 // writes that granule for all its rows, four lanes a row, 16 rows an
 // instruction.  The chunk that ends a row group's extent pads its last
-// granule with -inf and writes the -inf past it.  A granule cut by a chunk
-// boundary is written in two parts by two workgroups; boundaries fall on
-// 16-byte pieces, and odd chunks walk their blocks backwards, so both parts
-// are written at about the same time (both at the start or both at the end
-// of their items).  Values stored one by one as each page was scored left
-// each line to be assembled over many pages while the streaming K evicted it:
-// about ten times the block-score bytes reached HBM on the prefill workload
-// (3.3 times with four values a 16-byte store, 1.3 times staged, the rest
-// all at chunk boundaries: 1.00 with one chunk a row group).  lse mode
-// stores each score as it is made: it is bound by its vector work, the
-// writes do not bound it, and staging cost it 5 % (more wait states in its
-// tighter register budget).
+// granule with -inf and writes the -inf past it.  Where whole granules can
+// be dealt out to the chunks without lengthening the longest one, chunk
+// boundaries fall between granules; otherwise on 16-byte pieces, and a
+// granule cut by a boundary is written in two parts by two workgroups (odd
+// chunks walk their blocks backwards, so both parts are written at about
+// the same time).  The stores are nontemporal: a 128-byte line holds two
+// granules, written 16 pages apart, and as ordinary stores its first half
+// often left L2 before the second came, so 1.3 times the block-score bytes
+// reached HBM on the prefill workload; nontemporal, 1.09 times, in the same
+// time.  Values stored one by one as each page was scored, before the
+// staging, reached HBM about ten times over (3.3 times with four values a
+// 16-byte store).  lse mode stores each score as it is made: it is bound
+// by its vector work, the writes do not bound it, and staging cost it 5 %
+// (more wait states in its tighter register budget).
 #include <algorithm>
 #include <atomic>
 #include <climits>
@@ -77,6 +79,12 @@ namespace idx {
 
 #ifndef IDX_ROWS_ITEMS
 #define IDX_ROWS_ITEMS 1      // items per resident workgroup the block chunks aim at
+#endif
+#ifndef IDX_ROWS_NT_STORE
+#define IDX_ROWS_NT_STORE 1   // max: block scores leave with nontemporal stores
+#endif
+#ifndef IDX_ROWS_GRAN_SPLIT
+#define IDX_ROWS_GRAN_SPLIT 1  // max: chunk boundaries between output granules where that costs no time
 #endif
 // Eight waves of four tiles: two waves a SIMD share the matrix core (one
 // wave of eight tiles a SIMD measured a third slower: it cannot keep the
@@ -396,9 +404,18 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   // the inner boundaries are rounded to multiples of four blocks, so the
   // parts of a granule two chunks write are whole 16-byte pieces (at most
   // kMaxItemBlocks blocks: the launch makes ceil(max_blocks / C) + 4 no more)
+  // When whole granules can be dealt out to the C chunks without making the
+  // row group's largest chunk longer than ceil(max_blocks / C) (the chunk
+  // the launch sized for), the boundaries fall between granules and no
+  // granule is written in two parts.
+  const int ngran = (nb_item + kGran - 1) / kGran;
+  const bool gran_split = IDX_ROWS_GRAN_SPLIT && kStaged &&
+                          kGran * ((ngran + C - 1) / C) <= (MB + C - 1) / C;
   auto chunk_start = [&](int cc) -> int {
+    if (cc >= C) return nb_item;
+    if (gran_split) return min(nb_item, kGran * (int)((int64_t)cc * ngran / C));
     const int x = (int)((int64_t)cc * nb_item / C);
-    return (cc >= C) ? nb_item : (kStaged ? min(nb_item, (x + 2) & ~3) : x);
+    return kStaged ? min(nb_item, (x + 2) & ~3) : x;
   };
   const int b0 = chunk_start(c);
   const int nblk = chunk_start(c + 1) - b0;
@@ -407,13 +424,20 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
   // with aligned granules its last one is padded, and the rest starts whole
   const bool whole = kStaged && (MB % kGran) == 0 && (reinterpret_cast<uintptr_t>(a.block_scores) & 15) == 0;
   const bool ends = (nb_item == 0) ? (c == 0) : (nblk > 0 && b0 + nblk == nb_item);
+  // max mode: block scores leave with nontemporal stores (see the header)
+  constexpr bool kNt = kStaged && IDX_ROWS_NT_STORE;
   if (ends) {
     const int fill_from = whole ? min(MB, (nb_item + kGran - 1) & ~(kGran - 1)) : nb_item;
     for (int i = 0; i < kWaveRows; ++i) {
       const int row = wrow0 + i;
       if (row >= PH) break;
       float* out = a.block_scores + ((int64_t)r * PH + row) * MB;
-      for (int b = fill_from + lane; b < MB; b += 64) out[b] = -INFINITY;
+      for (int b = fill_from + lane; b < MB; b += 64) {
+        if constexpr (kNt)
+          __builtin_nontemporal_store(-INFINITY, out + b);
+        else
+          out[b] = -INFINITY;
+      }
     }
   }
   if (nblk <= 0) return;
@@ -461,7 +485,12 @@ __device__ __forceinline__ void score_item(const StepArgs& a, RowsLds& L, int it
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (b1 + i <= gh) ? v[i] : -INFINITY;
       if (whole) {  // the item's blocks of a granule are whole 16-byte pieces
-        if (b1 >= gl && b1 <= ge) *reinterpret_cast<f32x4*>(dst) = v;
+        if (b1 >= gl && b1 <= ge) {
+          if constexpr (kNt)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+          else
+            *reinterpret_cast<f32x4*>(dst) = v;
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)

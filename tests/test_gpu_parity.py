@@ -654,6 +654,47 @@ def test_many_rows_output_layouts(oracle, mb):
     Hn.assert_parity(aligned, oracle.step(**a), a)
 
 
+def test_many_rows_granule_chunks(oracle):
+    """Row groups whose block chunks are dealt whole 64-byte granules: 1,024
+    block columns over few row groups make chunks of 16 to 64 blocks, so the
+    chunk boundaries fall between granules.  Extents of 1,021..1,024 blocks
+    (64 granules), of 319..322 (20 and 21 granules, unequal shares, a
+    partial last granule padded with -inf) and of 16..19 (one or two
+    granules: most chunks empty), and a graph pad.  Sampled query rows of
+    every request against the oracle; every block column of every row is
+    written (no NaN fill left); aligned and misaligned block-score arrays
+    agree bit for bit."""
+    say("many rows, granule-aligned chunks")
+    P, H, mb = 512, 4, 1024
+    lens = [1020 * 128 - 126, 318 * 128 - 126, 1900]
+    w = W.make(name="gran", R=3, P=P, H=H, k_format=W.K_FP8_E4M3, req_len=lens, topk=8,
+               init_blocks=1, local_blocks=2, seed=575, pads=1, pad_len=3000, max_blocks=mb, device="cuda")
+    g = Hn.gpu_step(w)
+    assert not np.isnan(g["block_scores"]).any(), "a block column left unwritten"
+    a = w.oracle_args()
+    ends = [(128 * gi + 127) * H for gi in range(4)]  # each row group's longest row
+    assert list(Hn.row_blocks(a)[ends]) == [1021, 1022, 1023, 1024]
+    assert list(Hn.row_blocks(a)[[P * H + e for e in ends]]) == [319, 320, 321, 322]
+    qrows = [0, 1, 127, 128, 255, 256, 300, 383, 384, 510, 511]
+    for req in range(3):
+        sub = Hn.subset_rows_args(a, req, qrows, P, H)
+        rows = (req * P * H + np.asarray(qrows)[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+        Hn.assert_parity({k: v[rows] for k, v in g.items()}, oracle.step(**sub), sub)
+    pad_rows = slice(3 * P * H, 4 * P * H)
+    sub = Hn.subset_rows_args(a, 3, qrows, P, H)
+    rows = (3 * P * H + np.asarray(qrows)[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+    Hn.assert_parity({k: v[rows] for k, v in g.items()}, oracle.step(**sub), sub)
+    assert np.all(g["block_scores"][pad_rows] == -np.inf)
+    big = torch.full((w.rows * mb + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    outs = {"block_scores": big[1:1 + w.rows * mb].view(w.rows, mb),
+            "topk_ids": torch.full((w.rows, w.topk), -7, dtype=torch.int32, device="cuda"),
+            "topk_scores": torch.full((w.rows, w.topk), float("nan"), dtype=torch.float32, device="cuda")}
+    I.idx_step(Hn.gpu_params(w, outs))
+    torch.cuda.synchronize()
+    for key, v in outs.items():
+        assert np.array_equal(g[key], v.cpu().numpy(), equal_nan=True), key
+
+
 def test_many_rows_invalid_pages(oracle):
     say("many rows, invalid page ids")
     w = W.make(name="rows_bad", R=2, P=40, H=2, k_format=W.K_BF16, req_len=[1500, 900], topk=4,

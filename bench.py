@@ -61,6 +61,14 @@ def parse() -> argparse.Namespace:
                     help="block reduction: max (default) or lse")
     ap.add_argument("--sm-scale", type=float, default=1 / 128 ** 0.5,
                     help="softmax scale of the lse mode (default 1/sqrt(128))")
+    ap.add_argument("--other-workloads", dest="other_workloads", action="store_true", default=None,
+                    help="also time the other decode workloads, the ~150K shape with fp8 keys and the "
+                         "prefill workload (default: on for the headline run)")
+    ap.add_argument("--no-other-workloads", dest="other_workloads", action="store_false")
+    ap.add_argument("--other-first", action="store_true",
+                    help="time the other workloads before the headline one instead of after it")
+    ap.add_argument("--other-pause", type=float, default=10.0,
+                    help="seconds of idle GPU between the headline workload and the others")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=None,
                     help="requests in the CPU-oracle sample (default: all real requests)")
@@ -129,78 +137,27 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.other_workloads is None:
+        args.other_workloads = args.config == 3 and args.k_format is None and args.score_mode == "max"
+    others = None
+    if args.other_workloads and args.other_first:
+        others = bench_other_workloads(n_ev=max(20, min(args.steps, 50)), warmup=min(args.warmup, 5))
+        torch.cuda.empty_cache()
+        time.sleep(args.other_pause)
     kf = {None: None, "bf16": W.K_BF16, "fp8": W.K_FP8_E4M3, "nvfp4": W.K_NVFP4}[args.k_format]
     w = W.config(args.config, device=dev, local_blocks=args.local_blocks, k_format=kf)
-    rows, K, MB = w.rows, w.topk, w.max_blocks
-    outs = {"block_scores": torch.empty((rows, MB), dtype=torch.float32, device=dev),
-            "topk_ids": torch.empty((rows, K), dtype=torch.int32, device=dev),
-            "topk_scores": torch.empty((rows, K), dtype=torch.float32, device=dev)}
-    fp4 = w.k_format == W.K_NVFP4
-    pool_store = None
-    if fp4:
-        # the whole pool (timed on its own: median of 5 calls, each after a
-        # 1 GiB read that leaves the caches without its data), then per step
-        # only the step's new keys: each request's last packed_queries tokens
-        I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale)
-        evict = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        pool_ms = []
-        for _ in range(5):
-            evict.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale)
-            e1.record()
-            torch.cuda.synchronize()
-            pool_ms.append(e0.elapsed_time(e1))
-        del evict
-        n_pool = w.staging.shape[0]
-        pool_us = float(np.median(pool_ms)) * 1e3
-        pool_store = {"tokens": n_pool, "us": round(pool_us, 2), "calls": 5,
-                      "GBps": round(n_pool * (256 + 72 + 8) / (pool_us / 1e6) / 1e9, 1)}
-        ends = np.cumsum(w.group_len()[: w.n_real].astype(np.int64))
-        new_rows = np.concatenate([np.arange(e - w.packed_queries, e) for e in ends])
-        sel = torch.as_tensor(new_rows, device=dev)
-        step_staging = w.staging.index_select(0, sel).contiguous()
-        step_slots = w.slot_mapping.index_select(0, sel).contiguous()
     mode = ({"score_mode": I.IDX_SCORE_LSE, "sm_scale": args.sm_scale} if args.score_mode == "lse"
             else {"score_mode": I.IDX_SCORE_MAX})
-    p = I.make_params(k_format=w.k_format, q=w.q, k=w.k, k_scale=w.k_scale, req_slot=w.req_slot,
-                      block_table=w.block_table, row_len=w.row_len, packed_queries=w.packed_queries,
-                      gqa=w.gqa, topk=K, init_blocks=w.init_blocks, local_blocks=w.local_blocks,
-                      max_blocks=MB, n_slot_rows=w.n_slot_rows, n_pages=w.n_pages, **mode, **outs)
-
-    # algorithmic bytes (token-exact K of each real request's longest row)
+    st = Step(w, mode, dev, time_pool=True)
+    rows, K, MB = w.rows, w.topk, w.max_blocks
+    outs, p, fp4, pool_store = st.outs, st.p, st.fp4, st.pool_store
     P, H = w.packed_queries, w.gqa
-    tokens = w.k_tokens()
-    k_bytes = tokens * W.BYTES_PER_TOKEN[w.k_format]
-    real_rows = w.n_real * P * H
-    nbg = w.pool_pages_used()
-    score_bytes = k_bytes + real_rows * 256 + nbg * 4 + (w.n_req * P + w.n_req) * 4
-    out_bytes = rows * K * 8
-    step_bytes = score_bytes + out_bytes
-    store_bytes = step_staging.shape[0] * (256 + 72 + 8) if fp4 else 0   # staging in, payload+scales out, slot
-
-    # cold L2/MALL between steps only for workloads the 256 MB cache could hold:
-    # a 1 GiB read (reads leave clean lines, so the step pays no write-back)
-    flush = None
-    if k_bytes < (1 << 30):
-        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-
+    k_bytes, score_bytes, step_bytes = st.k_bytes, st.score_bytes, st.step_bytes
+    flush = st.flush
     stream = torch.cuda.current_stream()
 
     def one_step(ev=None):
-        if fp4:
-            if ev is not None:
-                ev[0].record(stream)
-            I.idx_fp4_store(step_staging, step_slots, w.k, w.k_scale, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        I.idx_score_packed(p, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        I.idx_block_topk(p, stream)
-        if ev is not None:
-            ev[3].record(stream)
+        st.run(stream, ev)
 
     for _ in range(args.warmup):
         if flush is not None:
@@ -224,16 +181,8 @@ def main() -> int:
     # steps the step time is the mean of the event-timed kernels, since the
     # wall clock then includes the flush.
     n_ev = args.event_steps if args.event_steps else max(20, min(args.steps, 100))
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
-    for e in ev:
-        if flush is not None:
-            flush.sum()
-        one_step(e)
-    torch.cuda.synchronize()
-
-    store_ms = [e[0].elapsed_time(e[1]) for e in ev] if fp4 else [0.0] * len(ev)
-    score_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    topk_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    t_ev = st.event_pass(stream, n_ev)
+    store_ms, score_ms, topk_ms = t_ev["store"], t_ev["score"], t_ev["topk"]
     step_ms = [a + b + c for a, b, c in zip(store_ms, score_ms, topk_ms)]
     ms_per_step = wall * 1e3 / args.steps if flush is None else float(np.mean(step_ms))
     score_mean_s = float(np.mean(score_ms)) / 1e3
@@ -285,14 +234,14 @@ def main() -> int:
         "kernels_us": {"score": round(score_mean_s * 1e6, 2),
                        "topk": round(float(np.mean(topk_ms)) * 1e3, 2),
                        **({"fp4_store": round(float(np.mean(store_ms)) * 1e3, 2)} if fp4 else {})},
-        "kernel_samples": len(ev),
+        "kernel_samples": n_ev,
         # spread of the event-timed score kernel over the event pass
         "score_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(score_ms, [10, 50, 90])],
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if fp4:
-        line["fp4_store_step_tokens"] = int(step_staging.shape[0])
+        line["fp4_store_step_tokens"] = int(st.step_staging.shape[0])
         line["fp4_store_pool"] = pool_store
     if args.attn_q_per_kv and P <= 16 and P * args.attn_q_per_kv <= 64:
         for kvf in ("bf16", "fp8"):
@@ -306,8 +255,188 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_requests, args.cpu_rows, mode)
+    if others is None and args.other_workloads:
+        del st, outs, p, w, flush, one_step
+        torch.cuda.empty_cache()
+        time.sleep(args.other_pause)
+        others = bench_other_workloads(n_ev=max(20, min(args.steps, 50)), warmup=min(args.warmup, 5))
+    if others is not None:
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
     return 0
+
+
+class Step:
+    """One workload's step: its parameters and outputs, the NVFP4 store of the
+    step's new keys (each request's last packed_queries tokens; the whole pool
+    is stored once first, and that store is timed when ``time_pool``), the
+    algorithmic byte counts, and the 1 GiB read that leaves the caches without
+    K between steps when the 256 MB MALL could hold it."""
+
+    def __init__(self, w, mode: dict, dev: str, time_pool: bool = False):
+        import numpy as np
+        import torch
+
+        from sparse_attention_lightning_amd import idx as I
+        from sparse_attention_lightning_amd import workloads as W
+
+        self.w = w
+        rows, K, MB = w.rows, w.topk, w.max_blocks
+        self.outs = {"block_scores": torch.empty((rows, MB), dtype=torch.float32, device=dev),
+                     "topk_ids": torch.empty((rows, K), dtype=torch.int32, device=dev),
+                     "topk_scores": torch.empty((rows, K), dtype=torch.float32, device=dev)}
+        self.fp4 = w.k_format == W.K_NVFP4
+        self.pool_store = None
+        self.step_staging = self.step_slots = None
+        if self.fp4:
+            I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale)
+            if time_pool:
+                # median of 5 calls, each after a 1 GiB read that leaves the
+                # caches without its data
+                evict = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+                pool_ms = []
+                for _ in range(5):
+                    evict.sum()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    I.idx_fp4_store(w.staging, w.slot_mapping, w.k, w.k_scale)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    pool_ms.append(e0.elapsed_time(e1))
+                del evict
+                n_pool = w.staging.shape[0]
+                pool_us = float(np.median(pool_ms)) * 1e3
+                self.pool_store = {"tokens": n_pool, "us": round(pool_us, 2), "calls": 5,
+                                   "GBps": round(n_pool * (256 + 72 + 8) / (pool_us / 1e6) / 1e9, 1)}
+            ends = np.cumsum(w.group_len()[: w.n_real].astype(np.int64))
+            new_rows = np.concatenate([np.arange(e - w.packed_queries, e) for e in ends])
+            sel = torch.as_tensor(new_rows, device=dev)
+            self.step_staging = w.staging.index_select(0, sel).contiguous()
+            self.step_slots = w.slot_mapping.index_select(0, sel).contiguous()
+        self.p = I.make_params(k_format=w.k_format, q=w.q, k=w.k, k_scale=w.k_scale, req_slot=w.req_slot,
+                               block_table=w.block_table, row_len=w.row_len, packed_queries=w.packed_queries,
+                               gqa=w.gqa, topk=K, init_blocks=w.init_blocks, local_blocks=w.local_blocks,
+                               max_blocks=MB, n_slot_rows=w.n_slot_rows, n_pages=w.n_pages, **mode,
+                               **self.outs)
+        # algorithmic bytes (token-exact K of each real request's longest row)
+        P, H = w.packed_queries, w.gqa
+        self.k_bytes = w.k_tokens() * W.BYTES_PER_TOKEN[w.k_format]
+        real_rows = w.n_real * P * H
+        self.score_bytes = (self.k_bytes + real_rows * 256 + w.pool_pages_used() * 4
+                            + (w.n_req * P + w.n_req) * 4)
+        self.step_bytes = self.score_bytes + rows * K * 8
+        # reads leave clean lines, so the step pays no write-back
+        self.flush = torch.ones(1 << 28, dtype=torch.int32, device=dev) if self.k_bytes < (1 << 30) else None
+
+    def run(self, stream, ev=None):
+        """One step on ``stream``; ``ev``: four events around the store,
+        the scoring and the selection."""
+        from sparse_attention_lightning_amd import idx as I
+
+        w = self.w
+        if self.fp4:
+            if ev is not None:
+                ev[0].record(stream)
+            I.idx_fp4_store(self.step_staging, self.step_slots, w.k, w.k_scale, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        I.idx_score_packed(self.p, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        I.idx_block_topk(self.p, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    def step_pass(self, stream, n: int) -> list:
+        """Whole-step durations (ms) over ``n`` steps, one event pair around
+        each step (the gaps between its launches included), each after the
+        cache-clearing read when there is one."""
+        import torch
+
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for e in ev:
+            if self.flush is not None:
+                self.flush.sum()
+            e[0].record(stream)
+            self.run(stream)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) for e in ev]
+
+    def event_pass(self, stream, n: int) -> dict:
+        """Kernel durations (ms lists) from HIP events on ``stream`` over
+        ``n`` steps, each after the cache-clearing read when there is one."""
+        import torch
+
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for e in ev:
+            if self.flush is not None:
+                self.flush.sum()
+            self.run(stream, e)
+        torch.cuda.synchronize()
+        return {"store": [e[0].elapsed_time(e[1]) for e in ev] if self.fp4 else [0.0] * n,
+                "score": [e[1].elapsed_time(e[2]) for e in ev],
+                "topk": [e[2].elapsed_time(e[3]) for e in ev]}
+
+
+# The other workloads measured after the headline one, with the keys' format
+# override of the ~150K shape (fp8 beside NVFP4, the comparison the pages make).
+OTHER_WORKLOADS = ((1, None), (2, None), (4, None), (4, "fp8"), (5, None), (0, None))
+
+
+def bench_other_workloads(n_ev: int, warmup: int) -> dict:
+    """Each other workload's step in max mode, ``n_ev`` steps after
+    ``warmup``, a 1 GiB read before each step when K fits the MALL: the step
+    from one event pair around each step (launch gaps included), the
+    kernels from the four-event pass, the score kernel's roofline fraction,
+    and the step against the 70 %-of-HBM-peak time of its K bytes."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_lightning_amd import idx as I
+    from sparse_attention_lightning_amd import workloads as W
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for cfg, kfname in OTHER_WORKLOADS:
+        kf = {None: None, "fp8": W.K_FP8_E4M3}[kfname]
+        w = W.config(cfg, device="cuda", k_format=kf)
+        st = Step(w, {"score_mode": I.IDX_SCORE_MAX}, "cuda")
+        for _ in range(warmup):
+            if st.flush is not None:
+                st.flush.sum()
+            st.run(stream)
+        torch.cuda.synchronize()
+        step_us = float(np.mean(st.step_pass(stream, n_ev))) * 1e3
+        t = st.event_pass(stream, n_ev)
+        score_s = float(np.mean(t["score"])) / 1e3
+        P, H = w.packed_queries, w.gqa
+        entry = {"k_format": W.FORMAT_NAMES[w.k_format], "step_us": round(step_us, 2),
+                 "kernels_us": {"score": round(score_s * 1e6, 2), "topk": round(float(np.mean(t["topk"])) * 1e3, 2),
+                                **({"fp4_store": round(float(np.mean(t["store"])) * 1e3, 2)} if st.fp4 else {})},
+                 "k_bytes_per_step": st.k_bytes}
+        if P * H <= 16:
+            gbps = st.score_bytes / score_s / 1e9
+            entry["score_roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                       "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            if w.n_real > 2:  # the tiny workload is launch-bound: no bar
+                bar = st.k_bytes / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e6
+                entry["step_bar_us_70pct_hbm"] = round(bar, 1)
+                entry["step_frac_of_hbm_peak"] = round(st.k_bytes / (step_us / 1e6) / 1e9 / HBM_PEAK_GBPS, 4)
+        else:
+            rl = w.row_len.cpu().numpy().astype(np.int64).reshape(w.n_req, P)[: w.n_real]
+            tflops = int(rl.sum()) * H * 2 * 128 / score_s / 1e12
+            entry["score_roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4)}
+        entry["steps"] = n_ev
+        entry["timing"] = "step: one event pair a step; kernels: an event pair each, in a pass of their own"
+        res[w.name] = entry
+        del st, w
+        torch.cuda.empty_cache()
+    a, b = res.get("64req_150k_nvfp4"), res.get("64req_150k_fp8")
+    if a and b:
+        res["nvfp4_over_fp8_step"] = round(a["step_us"] / b["step_us"], 3)
+    return res
 
 
 def bench_attn(w, topk_ids, G: int, kvf: str, flush, stream, n_ev: int) -> dict:

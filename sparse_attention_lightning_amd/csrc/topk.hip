@@ -39,6 +39,9 @@
 #ifndef IDX_TOPK_RADIX
 #define IDX_TOPK_RADIX 1           // one-wave kernel: 1 finds its threshold by 8-bit digits over LDS
 #endif                             // histograms; 0: bit by bit, one wave-wide count a bit
+#ifndef IDX_TOPK_BALLOT_SCHED
+#define IDX_TOPK_BALLOT_SCHED 1  // one-wave kernel: slot and length loads issue before the score loads
+#endif
 #ifndef IDX_TOPK_BALLOT_ROWS
 #define IDX_TOPK_BALLOT_ROWS 1024  // rows from which rows of <= 1,024 blocks take one wave each
 #endif
@@ -47,7 +50,10 @@ namespace idx {
 
 constexpr int kTopkThreads = 512;        // the workgroup kernel: one row a workgroup
 constexpr int kTopkThreadsNarrow = 256;  // its threads for rows of at most 2,048 blocks
-constexpr int kBallotThreads = 256;  // the one-wave kernel: four rows a workgroup
+#ifndef IDX_TOPK_BALLOT_THREADS
+#define IDX_TOPK_BALLOT_THREADS 256  // the one-wave kernel's workgroup: a row a wave
+#endif
+constexpr int kBallotThreads = IDX_TOPK_BALLOT_THREADS;
 constexpr int kBallotWaves = kBallotThreads / 64;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -333,8 +339,21 @@ __device__ __forceinline__ void ballot_row(const StepArgs& a, int64_t o, int row
   const int r = (int)(o / rows), i = (int)(o - (int64_t)r * rows);
   const float* bs = a.block_scores + o * MB;
   const int slot = a.req_slot[r];
+  const int len_raw = a.row_len[r * a.P + i / a.H];
+#if IDX_TOPK_BALLOT_SCHED
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+  // the row's scores are loaded up to max_blocks without waiting for the
+  // slot and the length (every column of the row is written), so the two
+  // loads overlap instead of following each other
+  float sv[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const int b = 64 * j + lane;
+    sv[j] = b < MB ? bs[b] : -INFINITY;
+  }
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
-  const int nb = pad ? 0 : blocks_of(clamp_len(a.row_len[r * a.P + i / a.H], MB));
+  const int nb = pad ? 0 : blocks_of(clamp_len(len_raw, MB));
   int32_t* ids = a.topk_ids + o * K;
   float* sc = a.topk_scores + o * K;
   if (nb <= K) {
@@ -346,14 +365,12 @@ __device__ __forceinline__ void ballot_row(const StepArgs& a, int64_t o, int row
   }
 
   const int init = a.init_blocks, local_from = nb - a.local_blocks;
-  float sv[S];
   uint32_t key[S], ckey[S];  // ckey: the key where the block competes, else 0
   uint32_t cand = 0, forced = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const int b = 64 * j + lane;
     const bool in = b < nb;
-    sv[j] = in ? bs[b] : -INFINITY;
     key[j] = order_key(sv[j]);
     const bool f = in && (b < init || b >= local_from);
     const bool c = in && !f;

@@ -25,11 +25,13 @@
 // wave use DPP; waves meet through LDS.
 //
 // Many short rows (at least 1,024 rows of at most 1,024 blocks, as prefill
-// gives, or rows of at most 64 blocks) take one wave a row and no LDS instead: lane l holds blocks l,
-// l + 64, ...; T is found bit by bit, each candidate threshold counted with
-// one ballot per 64 blocks, stopping once exactly the wanted number reach
-// it; ties and output positions come from the same ballot masks.  An LDS-histogram version of that one-wave kernel measured
-// 20 % slower on 32,768 rows of 272 blocks.
+// gives, or rows of at most 64 blocks) take one wave a row and no workgroup
+// barrier instead: lane l holds blocks l, l + 64, ...; T is found by a radix
+// select over 8-bit digits with a 256-bin LDS histogram of the wave's own
+// (IDX_TOPK_RADIX 1; bit by bit with one wave-wide count a bit measured
+// slower, 33.3 against 28.4 us on 32,768 rows of 272 blocks), stopping once
+// the chosen bin holds exactly the keys still needed; ties and output
+// positions come from ballot masks.
 #include "device.h"
 
 

@@ -25,6 +25,12 @@ namespace idx {
 #ifndef IDX_STORE_WIDE_LANES
 #define IDX_STORE_WIDE_LANES 4  // lanes a key of the large-store kernel (4 or 2)
 #endif
+#ifndef IDX_STORE_GRID_CAP
+#define IDX_STORE_GRID_CAP 32768  // most workgroups a store launches (threads then stride over the keys)
+#endif
+#ifndef IDX_STORE_WIDE_UNROLL
+#define IDX_STORE_WIDE_UNROLL 2  // large-store kernel: keys a thread loads before it quantizes any
+#endif
 #ifndef IDX_STORE_NT
 #define IDX_STORE_NT 0      // 1: non-temporal staging loads and payload / scale stores
 #endif
@@ -110,44 +116,62 @@ __device__ __forceinline__ void quantize_group(u32x4 w0, u32x4 w1, int64_t slot,
 // pieces; lane 0 of the key stores the 8 scale bytes.  For large stores:
 // fewer, wider accesses a key.  The whole 150K NVFP4 pool (9.87 M keys)
 // stored in 692 us with four lanes a key, 727 with eight (the other kernel)
-// and 769 with two (medians of 36 interleaved calls, one box).  A small store
-// (a step's 256 new keys) keeps eight lanes a key: with one group a lane its
-// chain is shortest, and a small grid has no bandwidth to win.
+// and 769 with two (medians of 36 interleaved calls, one box); a thread
+// loading two keys before it quantizes either, on at most 32,768
+// workgroups, then took it from 687 to 667 us (one key a thread on 65,536:
+// the former; 16,384 or 8,192 workgroups, or three keys a thread, were no
+// better).  A small store (a step's 256 new keys) keeps eight lanes a key:
+// with one group a lane its chain is shortest, and a small grid has no
+// bandwidth to win.
 template <int KL>
 __global__ __launch_bounds__(kStoreThreads) void fp4_store_wide_kernel(
     const uint16_t* __restrict__ staging, int64_t n_tokens, int64_t stride,
     const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ payload,
     uint8_t* __restrict__ scales, int64_t n_slots) {
   constexpr int NG = 8 / KL;  // groups a lane
+  constexpr int U = IDX_STORE_WIDE_UNROLL;
   const int64_t n_items = n_tokens * KL;
   const int64_t step = (int64_t)gridDim.x * kStoreThreads;
-  for (int64_t item = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x; item < n_items; item += step) {
-    const int64_t t = item / KL;
-    const int q = (int)(item % KL);
-    const u32x4* src = reinterpret_cast<const u32x4*>(staging + t * stride + 16 * NG * q);
-    u32x4 w[2 * NG];
+  for (int64_t item0 = (int64_t)blockIdx.x * kStoreThreads + threadIdx.x; item0 < n_items; item0 += step * U) {
+    u32x4 w[U][2 * NG];
+    int64_t slot[U];
 #pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) w[i] = src[i];
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0 || slot >= n_slots) continue;  // the key's lanes skip it together
-    uint32_t p[2 * NG], sw = 0;
+    for (int u = 0; u < U; ++u) {
+      const int64_t item = item0 + u * step;
+      slot[u] = -1;
+      if (item < n_items) {  // a key's KL items are all in range or all out (n_items is a multiple of KL)
+        const int64_t t = item / KL;
+        const int q = (int)(item % KL);
+        const u32x4* src = reinterpret_cast<const u32x4*>(staging + t * stride + 16 * NG * q);
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) sw |= quantize16(w[2 * gi], w[2 * gi + 1], &p[2 * gi]) << (8 * (gi & 3));
-#pragma unroll
-    for (int i = 0; i < NG / 2; ++i)
-      *reinterpret_cast<u32x4*>(payload + slot * 64 + 16 * (NG / 2) * q + 16 * i) =
-          u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
-    uint32_t lo, hi;
-    if constexpr (KL == 4) {  // lanes 0, 1 of the quad make bytes 0..3, lanes 2, 3 bytes 4..7
-      uint32_t word = sw << (16 * (q & 1));
-      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-      lo = word;
-      hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-    } else {  // lane 0 bytes 0..3, lane 1 bytes 4..7
-      lo = sw;
-      hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sw, 0xB1, 0xF, 0xF, false);
+        for (int i = 0; i < 2 * NG; ++i) w[u][i] = src[i];
+        slot[u] = slot_mapping[t];
+      }
     }
-    if (q == 0) *reinterpret_cast<u32x2*>(scales + slot * 8) = u32x2{lo, hi};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t item = item0 + u * step;
+      if (item >= n_items || slot[u] < 0 || slot[u] >= n_slots) continue;  // the key's lanes skip it together
+      const int q = (int)(item % KL);
+      uint32_t p[2 * NG], sw = 0;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) sw |= quantize16(w[u][2 * gi], w[u][2 * gi + 1], &p[2 * gi]) << (8 * (gi & 3));
+#pragma unroll
+      for (int i = 0; i < NG / 2; ++i)
+        *reinterpret_cast<u32x4*>(payload + slot[u] * 64 + 16 * (NG / 2) * q + 16 * i) =
+            u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+      uint32_t lo, hi;
+      if constexpr (KL == 4) {  // lanes 0, 1 of the quad make bytes 0..3, lanes 2, 3 bytes 4..7
+        uint32_t word = sw << (16 * (q & 1));
+        word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        lo = word;
+        hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+      } else {  // lane 0 bytes 0..3, lane 1 bytes 4..7
+        lo = sw;
+        hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sw, 0xB1, 0xF, 0xF, false);
+      }
+      if (q == 0) *reinterpret_cast<u32x2*>(scales + slot[u] * 8) = u32x2{lo, hi};
+    }
   }
 }
 
@@ -198,15 +222,16 @@ hipError_t launch_fp4_store(const uint16_t* staging, int64_t n_tokens, int64_t s
   if (n_tokens == 0) return hipSuccess;
   if (n_tokens >= IDX_STORE_WIDE_MIN) {
     constexpr int KL = IDX_STORE_WIDE_LANES;
-    const int64_t want = (n_tokens * KL + kStoreThreads - 1) / kStoreThreads;
-    const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+    const int64_t want = (n_tokens * KL + (int64_t)kStoreThreads * IDX_STORE_WIDE_UNROLL - 1) /
+                         ((int64_t)kStoreThreads * IDX_STORE_WIDE_UNROLL);
+    const unsigned grid = (unsigned)(want < IDX_STORE_GRID_CAP ? want : IDX_STORE_GRID_CAP);
     hipLaunchKernelGGL(fp4_store_wide_kernel<KL>, dim3(grid), dim3(kStoreThreads), 0, stream, staging,
                        n_tokens, stride, slot_mapping, payload, scales, n_slots);
     return hipGetLastError();
   }
   const int64_t want = (n_tokens * 8 + (int64_t)kStoreThreads * IDX_STORE_UNROLL - 1) /
                        ((int64_t)kStoreThreads * IDX_STORE_UNROLL);
-  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  const unsigned grid = (unsigned)(want < IDX_STORE_GRID_CAP ? want : IDX_STORE_GRID_CAP);
   hipLaunchKernelGGL(fp4_store_kernel, dim3(grid), dim3(kStoreThreads), 0, stream, staging,
                      n_tokens, stride, slot_mapping, payload, scales, n_slots);
   return hipGetLastError();

@@ -41,6 +41,9 @@
 #ifndef IDX_TOPK_RADIX
 #define IDX_TOPK_RADIX 1           // one-wave kernel: 1 finds its threshold by 8-bit digits over LDS
 #endif                             // histograms; 0: bit by bit, one wave-wide count a bit
+#ifndef IDX_TOPK_BALLOT_BUFLOAD
+#define IDX_TOPK_BALLOT_BUFLOAD 1  // one-wave kernel: score loads through a row descriptor (no branches)
+#endif
 #ifndef IDX_TOPK_BALLOT_SCHED
 #define IDX_TOPK_BALLOT_SCHED 1  // one-wave kernel: slot and length loads issue before the score loads
 #endif
@@ -58,11 +61,22 @@ constexpr int kTopkThreadsNarrow = 256;  // its threads for rows of at most 2,04
 constexpr int kBallotThreads = IDX_TOPK_BALLOT_THREADS;
 constexpr int kBallotWaves = kBallotThreads / 64;
 
+#ifndef IDX_TOPK_KEY_ADD0
+#define IDX_TOPK_KEY_ADD0 1  // order keys: -0 made +0 by adding +0 (fewer vector instructions)
+#endif
 __device__ __forceinline__ uint32_t order_key(float f) {
+#if IDX_TOPK_KEY_ADD0
+  // f + 0 is f except that -0 becomes +0 (round to nearest); negative
+  // values flip every bit, others set the sign bit; NaN ranks lowest
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return (f == f) ? k : 0u;
+#else
   if (f != f) return 0u;  // NaN
   uint32_t u = __float_as_uint(f);
   if (f == 0.0f) u = 0u;  // -0 ranks with +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+#endif
 }
 
 template <int CTRL, int ROW_MASK = 0xF>
@@ -349,11 +363,21 @@ __device__ __forceinline__ void ballot_row(const StepArgs& a, int64_t o, int row
   // slot and the length (every column of the row is written), so the two
   // loads overlap instead of following each other
   float sv[S];
+#if IDX_TOPK_BALLOT_BUFLOAD
+  // through a descriptor of the row (max_blocks floats): past it a load
+  // returns 0, and those blocks are past nb too, so nothing reads them
+  const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(bs), (short)0, 4 * MB,
+                                                                        0x00020000);
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    sv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rrow, 4 * (64 * j + lane), 0, 0));
+#else
 #pragma unroll
   for (int j = 0; j < S; ++j) {
     const int b = 64 * j + lane;
     sv[j] = b < MB ? bs[b] : -INFINITY;
   }
+#endif
   const bool pad = slot < 0 || slot >= a.n_slot_rows;
   const int nb = pad ? 0 : blocks_of(clamp_len(len_raw, MB));
   int32_t* ids = a.topk_ids + o * K;

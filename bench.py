@@ -86,6 +86,7 @@ KERNEL_SOURCES = {
     "score_kernel": ("device.h", "tile.h", "score.hip"),
     "rows_kernel": ("device.h", "tile.h", "score_rows.hip"),
     "attn_partial_kernel": ("device.h", "attn.hip"),
+    "fp4_store_wide_kernel": ("device.h", "fp4_store.hip"),
 }
 
 
@@ -307,7 +308,9 @@ class Step:
                 n_pool = w.staging.shape[0]
                 pool_us = float(np.median(pool_ms)) * 1e3
                 self.pool_store = {"tokens": n_pool, "us": round(pool_us, 2), "calls": 5,
-                                   "GBps": round(n_pool * (256 + 72 + 8) / (pool_us / 1e6) / 1e9, 1)}
+                                   "GBps": round(n_pool * (256 + 72 + 8) / (pool_us / 1e6) / 1e9, 1),
+                                   "algorithmic_bytes": n_pool * (256 + 72 + 8),
+                                   "traffic": traffic_from_profiles("fp4_store_wide_kernel", "nvfp4", w.name)}
             ends = np.cumsum(w.group_len()[: w.n_real].astype(np.int64))
             new_rows = np.concatenate([np.arange(e - w.packed_queries, e) for e in ends])
             sel = torch.as_tensor(new_rows, device=dev)

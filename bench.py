@@ -13,9 +13,10 @@ Prints one JSON line: the metric (us per index step, wall clock over the
 timed steps), the dominant kernel's roofline against the 8 TB/s HBM peak
 (algorithmic bytes over its mean duration, from HIP events on its launch
 stream in a separate pass of at least 20 steps), the rate at which the part
-reads the same K pages with nothing else to do (``idx_probe_read``), and the
+reads the same K pages with nothing else to do (``idx_probe_read``), the
 CPU oracle timed on the host as a reported baseline (all cores, and one
-thread on a sixteenth of that sample).
+thread on a sixteenth of that sample), and, in the default run, every other
+workload's step, kernels and score roofline under ``other_workloads``.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 3] [--k-format fp8]
 """

@@ -969,7 +969,7 @@ def _random_case(seed: int) -> dict:
                 lse=bool(rng.random() < 0.4), scale=float(rng.choice([0.02, 1 / np.sqrt(128), 0.5])))
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(256))
 def test_random_shapes(oracle, seed):
     c = _random_case(seed)
     say("random", seed, c)

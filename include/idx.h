@@ -191,6 +191,39 @@ int idx_block_topk(const idx_params* p, void* stream);
 /* idx_score_packed then idx_block_topk on the same stream. */
 int idx_step(const idx_params* p, void* stream);
 
+/* The step's new NVFP4 keys [P3] (Summary: the store writes each new key into
+ * the index cache before the decode scorer reads it): bf16 staging rows and
+ * their slots, as the arguments of idx_fp4_store. */
+typedef struct idx_fp4_new_keys {
+  const void* staging_bf16;    /* [n_tokens][staging_row_stride] bf16, 16-byte aligned */
+  int64_t n_tokens;            /* >= 0                                                 */
+  int64_t staging_row_stride;  /* >= 128, a multiple of 8                              */
+  const int64_t* slot_mapping; /* [n_tokens]: slot = page * 128 + offset               */
+} idx_fp4_new_keys;
+
+/* Keys the score launch stores itself; more take a store launch of their own. */
+#define IDX_FP4_FUSED_MAX_KEYS 1024
+
+/*
+ * idx_fp4_store of `keys` into p->k (payload) and p->k_scale (scales), with
+ * n_slots = p->n_pages * 128, followed by idx_score_packed(p), on `stream`:
+ * the pool bytes and the block scores are exactly those two calls'.  For
+ * NVFP4 keys (p->k_format == IDX_K_NVFP4) only.  When keys->n_tokens <=
+ * IDX_FP4_FUSED_MAX_KEYS and the requests hold at most 16 rows each
+ * (packed_queries * gqa <= 16), the score launch writes the keys itself (one
+ * launch in all: every key is written by one workgroup early in the launch
+ * and again, with the same bytes, by every workgroup whose pages hold it
+ * before that workgroup reads them); otherwise a store launch precedes the
+ * score launch.  p->k and p->k_scale are written, so they must be writable
+ * device memory; k_scale 8-byte aligned.  Two keys with one slot leave
+ * either key's bytes there, as for idx_fp4_store.  Refusals: those of both
+ * calls, IDX_E_FORMAT for another k_format, IDX_E_NULL for a NULL `keys`.
+ */
+int idx_score_packed_fp4(const idx_params* p, const idx_fp4_new_keys* keys, void* stream);
+
+/* idx_score_packed_fp4 then idx_block_topk on the same stream. */
+int idx_step_fp4(const idx_params* p, const idx_fp4_new_keys* keys, void* stream);
+
 /* Message describing the last refusal on the calling thread ("" if none). */
 const char* idx_last_error(void);
 

@@ -242,6 +242,75 @@ int idx_step(const idx_params* p, void* stream) {
   return launched(idx::launch_topk(a, (hipStream_t)stream), "top-k");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The checks of idx_fp4_store for the new keys of an NVFP4 step.
+int check_new_keys(const idx_params* p, const idx_fp4_new_keys* nk) {
+  if (!nk) return fail(IDX_E_NULL, "keys is NULL");
+  if (p->k_format != IDX_K_NVFP4)
+    return fail(IDX_E_FORMAT, "the fused store is for NVFP4 keys (k_format %d)", p->k_format);
+  if (nk->n_tokens < 0) return fail(IDX_E_SHAPE, "negative n_tokens %lld", (long long)nk->n_tokens);
+  if (nk->staging_row_stride < 128 || (nk->staging_row_stride & 7))
+    return fail(IDX_E_SHAPE, "staging_row_stride %lld must be >= 128 and a multiple of 8",
+                (long long)nk->staging_row_stride);
+  if (nk->n_tokens > ((int64_t)1 << 40)) return fail(IDX_E_SHAPE, "n_tokens too large");
+  if (nk->n_tokens == 0) return IDX_OK;
+  if (!nk->staging_bf16 || !nk->slot_mapping || (p->n_pages > 0 && (!p->k || !p->k_scale)))
+    return fail(IDX_E_NULL, "staging, slot_mapping, k and k_scale are required");
+  if (!aligned16(nk->staging_bf16) || !aligned16(p->k))
+    return fail(IDX_E_ALIGN, "staging and k must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(p->k_scale) & 7u) != 0)
+    return fail(IDX_E_ALIGN, "k_scale must be 8-byte aligned for the store");
+  return IDX_OK;
+}
+
+// The store and the scoring of an NVFP4 step: one launch when the score
+// kernel can take the keys, else a store launch first.
+int score_with_keys(const idx_params* p, const idx_fp4_new_keys* nk, hipStream_t stream) {
+  idx::StepArgs a = args_of(p);
+  const int64_t n = nk->n_tokens;
+  const bool fused = n > 0 && n <= IDX_FP4_FUSED_MAX_KEYS && (int64_t)p->packed_queries * p->gqa <= 16 &&
+                     p->n_req > 0 && p->max_blocks > 0;
+  if (fused) {
+    a.st_staging = static_cast<const uint16_t*>(nk->staging_bf16);
+    a.st_slots = nk->slot_mapping;
+    a.st_n = n;
+    a.st_stride = nk->staging_row_stride;
+  } else if (n > 0) {
+    const int r = launched(idx::launch_fp4_store(static_cast<const uint16_t*>(nk->staging_bf16), n,
+                                                 nk->staging_row_stride, nk->slot_mapping,
+                                                 static_cast<uint8_t*>(const_cast<void*>(p->k)),
+                                                 const_cast<uint8_t*>(p->k_scale), p->n_pages * 128, stream),
+                           "fp4 store");
+    if (r) return r;
+  }
+  return launched(idx::launch_score(a, stream), "score");
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_score_packed_fp4(const idx_params* p, const idx_fp4_new_keys* keys, void* stream) {
+  int rc = check(p, kScore);
+  if (!rc) rc = check_new_keys(p, keys);
+  if (rc) return rc;
+  clear_stale_error();
+  return score_with_keys(p, keys, (hipStream_t)stream);
+}
+
+int idx_step_fp4(const idx_params* p, const idx_fp4_new_keys* keys, void* stream) {
+  int rc = check(p, kScore | kTopk);
+  if (!rc) rc = check_new_keys(p, keys);
+  if (rc) return rc;
+  clear_stale_error();
+  const int r1 = score_with_keys(p, keys, (hipStream_t)stream);
+  if (r1) return r1;
+  return launched(idx::launch_topk(args_of(p), (hipStream_t)stream), "top-k");
+}
+
 int idx_step_noalloc(const idx_params* p, void* stream) {
   if (p && p->block_scores)
     return fail(IDX_E_SHAPE, "idx_step_noalloc keeps the block scores itself: block_scores must be NULL");

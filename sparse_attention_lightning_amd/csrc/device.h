@@ -36,6 +36,11 @@ struct StepArgs {
   int32_t n_req, n_slot_rows, P, H, max_blocks, topk, init_blocks, local_blocks;
   int32_t score_mode;  // IDX_SCORE_MAX or IDX_SCORE_LSE
   float sm_scale;      // lse only
+  // NVFP4 only: new keys the score kernel quantizes into the pool (k, k_scale)
+  // before it reads them (st_n = 0: none); see the fused store in score.hip
+  const uint16_t* st_staging;  // bf16 [st_n][st_stride]
+  const int64_t* st_slots;     // [st_n]
+  int64_t st_n, st_stride;
 };
 
 // Sparse attention over the selected blocks (one launch of partials, one of

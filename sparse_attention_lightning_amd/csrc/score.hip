@@ -36,6 +36,7 @@
 #include <climits>
 #include <cstddef>
 
+#include "fp4_quant.h"
 #include "tile.h"
 
 namespace idx {
@@ -65,6 +66,8 @@ constexpr int kQPiecesPerThread = (8 * 16 * 16) / kThreads;       // query-tile 
 constexpr int kRoundPages = 768;   // pages a workgroup stages at once
 constexpr int kRoundReqs = 8;      // requests a round may touch
 constexpr int kQStride = 136;      // 16-bit values per query row in LDS (272 B: rows change banks)
+constexpr uint32_t kSkNewKeys = 0x2000u;  // sk bit: the page holds new NVFP4 keys (fused store)
+constexpr int kKeysPerThread = (IDX_FP4_FUSED_MAX_KEYS + kThreads - 1) / kThreads;  // fused store: slots a thread holds
 
 // ---------------------------------------------------------------------------
 // Rounds.  A workgroup's range of the step's pages is handled in rounds of at
@@ -82,12 +85,18 @@ struct RoundLds {
   float stage[kTileRows][kRoundPages];            // block scores of the round
   int32_t pid[kRoundPages];                       // page ids, in hand-out order
   uint16_t sk[kRoundPages];                       // in hand-out order: round page | request in the round << 10
+                                                  // | kSkNewKeys
   uint8_t ridx[kRoundPages];                      // each round page's request within the round
   uint16_t q[kRoundReqs][kTileRows][kQStride];    // query tiles (bf16, or f16 scaled by 2^sigma)
   RoundReq req[kRoundReqs];
   uint32_t amax[kRoundReqs];                      // NVFP4: largest |q| of each tile (float bits)
   uint32_t next;                                  // pages handed out
   uint32_t wave_tot[kWaves];                      // scan scratch
+  // NVFP4 with new keys (the fused store): the keys whose page this round
+  // reads (their pages carry kSkNewKeys in sk), and whether wave 0 has
+  // stored them
+  uint16_t own[IDX_FP4_FUSED_MAX_KEYS];
+  uint32_t n_own, keys_ready;
 };
 static_assert(offsetof(RoundLds, q) % 16 == 0 && offsetof(RoundLds, req) % 16 == 0, "16-byte LDS rows");
 // with the per-request arrays for the largest request count, one workgroup
@@ -243,12 +252,86 @@ __device__ void setup_round(const StepArgs& a, RoundLds& L, const uint32_t* pre,
   if (tid == 0) L.next = 0;
 }
 
+// Fused store of a step's new NVFP4 keys (st_n of them, at most
+// IDX_FP4_FUSED_MAX_KEYS): the same bytes idx_fp4_store writes, eight lanes a
+// key.  Every key is written twice over: by workgroup t mod G (wave 1, while
+// the other waves stream), so that keys in pages no workgroup reads reach the
+// pool too, and by wave 0 of each workgroup whose round holds the key's page,
+// before any wave of that workgroup reads the page.  Both write identical
+// bytes, so their order does not matter; the reading wave sees wave 0's
+// write through its own CU's caches once wave 0's stores are complete, which
+// wave 0 publishes in LDS.  No workgroup waits for another.
+__device__ __forceinline__ void store_new_key(const StepArgs& a, int64_t t, int grp, int64_t n_slots) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.st_staging + t * a.st_stride + 16 * grp);
+  const u32x4 w0 = src[0], w1 = src[1];
+  const int64_t slot = a.st_slots[t];
+  if (slot < 0 || slot >= n_slots) return;  // the key's eight lanes skip it together
+  quantize_group(w0, w1, slot, grp, const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.k)),
+                 const_cast<uint8_t*>(a.k_scale));
+}
+
+// The keys whose page this round reads (np pages in L.pid; when the round
+// was sorted, the first NB words of the stage hold each bucket's first
+// position), found per key in its bucket's range from the slots each thread
+// loaded at the start: listed for wave 0 to store, and their pages marked in
+// sk, so that a wave handed such a page waits until wave 0 has stored them.
+__device__ void mark_round_keys(const StepArgs& a, RoundLds& L, int np, int tid, const int64_t* kslot) {
+  constexpr int NB = IDX_SCORE_SORT_BUCKETS;
+  const uint32_t* starts = reinterpret_cast<const uint32_t*>(&L.stage[0][0]);
+  const int64_t n_slots = a.n_pages * kBlock;
+  const bool sorted = NB > 0 && np >= IDX_SCORE_SORT_MIN;
+  if (tid == 0) {
+    L.n_own = 0u;
+    L.keys_ready = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    const int64_t slot = kslot[i];
+    if (slot < 0 || slot >= n_slots) continue;  // past the keys, or a slot the store skips
+    const int page = (int)(slot / kBlock);
+    int k0 = 0, k1 = np;
+    if (sorted) {
+      const int bk = (int)((uint64_t)page * (uint64_t)(NB > 0 ? NB : 1) / (uint64_t)a.n_pages);
+      k0 = (int)starts[bk];
+      k1 = bk + 1 < NB ? (int)starts[bk + 1] : np;
+    }
+    bool found = false;
+    for (int k = k0; k < k1; ++k)
+      if (L.pid[k] == page) {
+        // keys of one page set the same bit: concurrent writes agree
+        L.sk[k] = (uint16_t)(L.sk[k] | kSkNewKeys);
+        found = true;
+      }
+    if (found) L.own[atomicAdd(&L.n_own, 1u)] = (uint16_t)(tid + kThreads * i);
+  }
+  __syncthreads();
+}
+
+// A wave handed a round page that holds new keys waits until wave 0 has
+// stored them (wave 0 stores them before it takes any page, so it never
+// waits itself; the bound only keeps the loop finite).
+__device__ __forceinline__ void wait_round_keys(RoundLds& L) {
+  for (int it = 0; it < (1 << 24); ++it) {
+    if (__hip_atomic_load(&L.keys_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Keys b, b + G, ... (this workgroup's share of the writes that also cover
+// keys in pages no workgroup reads), eight lanes a key, from `lanes` lanes.
+__device__ __forceinline__ void store_cyclic_keys(const StepArgs& a, int lane, int lanes) {
+  const int64_t n_slots = a.n_pages * kBlock;
+  for (int64_t t = blockIdx.x + (int64_t)gridDim.x * (lane >> 3); t < a.st_n; t += (int64_t)gridDim.x * (lanes >> 3))
+    store_new_key(a, t, lane & 7, n_slots);
+}
+
 // One wave's part of a round: pages from the round's counter until none is
 // left.  Wave page p (two units) is described by lane p % 64 of vm_tag (round
 // page | request << 16, or -1) and vm_pid.
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool KEYS>
 __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uint32_t lo, int np, int lane,
-                                             int n, int g) {
+                                             int n, int g, int wave, bool first) {
   typedef typename Fmt<FMT>::Op Op;
   constexpr int kRing = Fmt<FMT>::kRing;
   static_assert(kRing >= 2, "at least one half page in flight");
@@ -272,6 +355,22 @@ __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uin
   float st0[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float st1[4] = {0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (KEYS) {
+    // the fused store: wave 0 writes the keys of this round's pages before it
+    // takes a page, wave 1 its share of all keys in the first round
+    {
+      if (wave == 0) {
+        const int64_t n_slots = a.n_pages * kBlock;
+        const int no = (int)uniform(L.n_own);
+        for (int i = lane >> 3; i < no; i += 8) store_new_key(a, L.own[i], lane & 7, n_slots);
+        __builtin_amdgcn_s_waitcnt(0);  // wave 0's stores are complete
+        if (lane == 0) __hip_atomic_store(&L.keys_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else if (wave == 1 && first) {
+        store_cyclic_keys(a, lane, 64);
+      }
+    }
+  }
+
   auto issue = [&](Half<FMT>& h, int V) {
     const int p = V >> 1;
     if ((V & 1) == 0) {
@@ -283,7 +382,10 @@ __device__ __forceinline__ void stream_round(const StepArgs& a, RoundLds& L, uin
         if (k < (uint32_t)np) {
           pid = (int)uniform((uint32_t)L.pid[k]);
           const uint32_t skv = uniform((uint32_t)L.sk[k]);
-          tag = (int)((skv & 1023u) | ((skv >> 10) << 16));
+          if constexpr (KEYS) {
+            if (skv & kSkNewKeys) wait_round_keys(L);  // the page holds new keys
+          }
+          tag = (int)((skv & 1023u) | (((skv >> 10) & 7u) << 16));
           last = p;
         } else {
           done = true;
@@ -406,8 +508,9 @@ __device__ __forceinline__ int request_of(const uint32_t* pre, int R, uint32_t x
 // result.
 __device__ uint32_t g_wg_rate[1024];
 
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool KEYS>
 __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
+  static_assert(!KEYS || FMT == IDX_K_NVFP4, "the fused store is for NVFP4 keys");
   extern __shared__ uint32_t pre[];  // n_req + 1 prefix sums of per-request block counts, then n_req slots
   __shared__ RoundLds L;
   __shared__ uint32_t wave_tot[kWaves];
@@ -416,6 +519,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int P = a.P, rows = P * a.H, MB = a.max_blocks, R = a.n_req;
   int32_t* slot_of = reinterpret_cast<int32_t*>(pre + R + 1);
+
+  // 0. NVFP4 with new keys: their slots, loaded now for the rounds' lookups
+  int64_t kslot[kKeysPerThread];
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) kslot[i] = -1;
+  if constexpr (KEYS) {
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i)
+      if (tid + kThreads * i < a.st_n) kslot[i] = a.st_slots[tid + kThreads * i];
+  }
 
   // 1. pages each request's group reads (0 for graph pads) and their prefix
   // sums; the slots stay in LDS for the rounds
@@ -508,12 +621,17 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const StepArgs a) {
       const int np = (int)(rh - rl);
       setup_round<FMT>(a, L, pre, slot_of, r0, nreq, rl, np, tid);
       __syncthreads();
-      stream_round<FMT, MODE>(a, L, rl, np, lane, n, g);
+      if constexpr (KEYS) mark_round_keys(a, L, np, tid, kslot);
+      stream_round<FMT, MODE, KEYS>(a, L, rl, np, lane, n, g, wave, rl == lo);
       __syncthreads();
       write_round(a, L, rl, np, tid);
       __syncthreads();
       rl = rh;
     }
+  }
+  if constexpr (KEYS) {
+    // a workgroup that streamed nothing still writes its share of the keys
+    if (lo >= hi || a.n_pages == 0) store_cyclic_keys(a, tid, kThreads);
   }
 
   if (adapt) {
@@ -543,28 +661,28 @@ size_t dyn_bytes(int n_req) { return (size_t)(2 * n_req + 1) * sizeof(uint32_t);
 
 // Workgroups that fit on the device at once (cached per device), with the
 // dynamic LDS limit raised to what the largest request count needs.
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool KEYS>
 int resident_workgroups() {
   static std::atomic<int> cache[64];  // zero-initialised; calls from several threads store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (const int n = cache[dev].load(std::memory_order_relaxed); n > 0) return n;
   const size_t smem = dyn_bytes(IDX_MAX_REQ);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_kernel<FMT, MODE>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_kernel<FMT, MODE, KEYS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(score_kernel<FMT, MODE>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(score_kernel<FMT, MODE, KEYS>),
                                                    kThreads, smem) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   cache[dev].store(cus * per_cu, std::memory_order_relaxed);
   return cus * per_cu;
 }
 
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool KEYS = false>
 void launch(const StepArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((score_kernel<FMT, MODE>), dim3(resident_workgroups<FMT, MODE>()), dim3(kThreads),
+  hipLaunchKernelGGL((score_kernel<FMT, MODE, KEYS>), dim3(resident_workgroups<FMT, MODE, KEYS>()), dim3(kThreads),
                      dyn_bytes(a.n_req), stream, a);
 }
 
@@ -573,7 +691,12 @@ void launch_mode(const StepArgs& a, hipStream_t stream) {
   switch (a.k_format) {
     case IDX_K_BF16: launch<IDX_K_BF16, MODE>(a, stream); break;
     case IDX_K_FP8_E4M3: launch<IDX_K_FP8_E4M3, MODE>(a, stream); break;
-    default: launch<IDX_K_NVFP4, MODE>(a, stream); break;
+    default:  // NVFP4: the kernel with the fused store only when there are new keys
+      if (a.st_n > 0)
+        launch<IDX_K_NVFP4, MODE, true>(a, stream);
+      else
+        launch<IDX_K_NVFP4, MODE>(a, stream);
+      break;
   }
 }
 }  // namespace

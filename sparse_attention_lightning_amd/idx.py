@@ -30,8 +30,10 @@ IDX_ATTN_MAX_ROWS = 64
 IDX_ATTN_MAX_DRAFT = 16
 IDX_ATTN_MAX_IDS = 1024
 IDX_ATTN_MAX_SPLITS = 64
+IDX_FP4_FUSED_MAX_KEYS = 1024
 EXPORTS = ("idx_fp4_store", "idx_score_packed", "idx_block_topk", "idx_step", "idx_last_error",
-           "idx_step_noalloc", "idx_probe_read", "idx_sparse_attn", "idx_sparse_attn_workspace")
+           "idx_step_noalloc", "idx_probe_read", "idx_sparse_attn", "idx_sparse_attn_workspace",
+           "idx_score_packed_fp4", "idx_step_fp4")
 
 
 class IdxError(RuntimeError):
@@ -53,6 +55,12 @@ class IdxParams(C.Structure):
         ("req_slot", C.c_void_p), ("block_table", C.c_void_p), ("row_len", C.c_void_p),
         ("block_scores", C.c_void_p), ("topk_ids", C.c_void_p), ("topk_scores", C.c_void_p),
     ]
+
+
+class IdxFp4NewKeys(C.Structure):
+    """Mirror of ``idx_fp4_new_keys``."""
+    _fields_ = [("staging_bf16", C.c_void_p), ("n_tokens", C.c_int64), ("staging_row_stride", C.c_int64),
+                ("slot_mapping", C.c_void_p)]
 
 
 class IdxAttnParams(C.Structure):
@@ -84,6 +92,10 @@ def load(path: Path | str | None = None) -> C.CDLL:
     for name in ("idx_score_packed", "idx_block_topk", "idx_step", "idx_step_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = [C.POINTER(IdxParams), C.c_void_p]
+        fn.restype = C.c_int
+    for name in ("idx_score_packed_fp4", "idx_step_fp4"):
+        fn = getattr(lib, name)
+        fn.argtypes = [C.POINTER(IdxParams), C.POINTER(IdxFp4NewKeys), C.c_void_p]
         fn.restype = C.c_int
     lib.idx_fp4_store.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_int64, C.c_void_p]
@@ -220,6 +232,34 @@ def idx_block_topk(p: IdxParams, stream=None) -> None:
 def idx_step(p: IdxParams, stream=None) -> None:
     lib = load()
     _check(lib.idx_step(C.byref(p), _stream(stream)), lib)
+
+
+def make_new_keys(staging: torch.Tensor, slot_mapping: torch.Tensor) -> IdxFp4NewKeys:
+    """The step's new NVFP4 keys: ``staging`` bf16 [n_tokens, >=128] (row
+    stride from the tensor) and ``slot_mapping`` int64 [n_tokens]."""
+    if staging.dim() != 2 or staging.shape[1] < 128 or staging.stride(1) != 1:
+        raise ValueError("staging must be [n_tokens, >=128] with unit element stride")
+    if staging.device.type != "cuda" or staging.dtype != torch.bfloat16:
+        raise TypeError("staging must be a bf16 GPU tensor")
+    _dev(slot_mapping, "slot_mapping", (torch.int64,))
+    if slot_mapping.numel() != staging.shape[0]:
+        raise ValueError("slot_mapping needs one entry per staging row")
+    nk = IdxFp4NewKeys(staging.data_ptr(), staging.shape[0], staging.stride(0), slot_mapping.data_ptr())
+    nk._keep = (staging, slot_mapping)
+    return nk
+
+
+def idx_score_packed_fp4(p: IdxParams, keys: IdxFp4NewKeys, stream=None) -> None:
+    """idx_fp4_store of ``keys`` into p's NVFP4 planes, then idx_score_packed
+    (one launch when the score kernel takes the keys)."""
+    lib = load()
+    _check(lib.idx_score_packed_fp4(C.byref(p), C.byref(keys), _stream(stream)), lib)
+
+
+def idx_step_fp4(p: IdxParams, keys: IdxFp4NewKeys, stream=None) -> None:
+    """idx_score_packed_fp4 then idx_block_topk."""
+    lib = load()
+    _check(lib.idx_step_fp4(C.byref(p), C.byref(keys), _stream(stream)), lib)
 
 
 def idx_step_noalloc(p: IdxParams, stream=None) -> None:

@@ -351,3 +351,55 @@ def test_last_error_is_per_thread(lib):
     u.join()
     assert seen["rc"] == I.IDX_E_SHAPE and "head_dim" in seen["msg"]
     assert seen["other"] == ""
+
+
+def test_new_keys_layout_matches_header(tmp_path):
+    names = [f for f, _ in I.IdxFp4NewKeys._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "idx.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(idx_fp4_new_keys));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(idx_fp4_new_keys, {n}));\n' for n in names)
+                   + '  printf("%d\\n", IDX_FP4_FUSED_MAX_KEYS);\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", f"-I{ROOT / 'include'}", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == C.sizeof(I.IdxFp4NewKeys)
+    assert got[1:-1] == [getattr(I.IdxFp4NewKeys, n).offset for n in names]
+    assert got[-1] == I.IDX_FP4_FUSED_MAX_KEYS
+
+
+def good_fp4_step() -> tuple:
+    p = good_params()
+    p.k_format = I.IDX_K_NVFP4
+    nk = I.IdxFp4NewKeys(0x900000, 256, 128, 0xA00000)
+    return p, nk
+
+
+FP4_STEP_REFUSALS = [
+    ("p", "k_format", I.IDX_K_FP8_E4M3, I.IDX_E_FORMAT),
+    ("p", "k_format", I.IDX_K_BF16, I.IDX_E_FORMAT),
+    ("p", "k_scale", 0x100004, I.IDX_E_ALIGN),     # 8-byte alignment for the store's scale words
+    ("p", "topk", 0, I.IDX_E_TOPK),                 # the step's own checks still apply
+    ("k", "n_tokens", -1, I.IDX_E_SHAPE),
+    ("k", "staging_row_stride", 100, I.IDX_E_SHAPE),
+    ("k", "staging_row_stride", 130, I.IDX_E_SHAPE),
+    ("k", "staging_bf16", None, I.IDX_E_NULL),
+    ("k", "slot_mapping", None, I.IDX_E_NULL),
+    ("k", "staging_bf16", 0x900008, I.IDX_E_ALIGN),
+]
+
+
+@pytest.mark.parametrize("which,field,value,code", FP4_STEP_REFUSALS,
+                         ids=[f"{w}.{f}={v}" for w, f, v, _ in FP4_STEP_REFUSALS])
+def test_fp4_step_refusals(lib, which, field, value, code):
+    p, nk = good_fp4_step()
+    setattr(p if which == "p" else nk, field, value)
+    assert lib.idx_step_fp4(C.byref(p), C.byref(nk), None) == code
+    assert lib.idx_last_error().decode() != ""
+    assert lib.idx_score_packed_fp4(C.byref(p), C.byref(nk), None) == code
+
+
+def test_fp4_step_needs_keys(lib):
+    p, _ = good_fp4_step()
+    assert lib.idx_step_fp4(C.byref(p), None, None) == I.IDX_E_NULL
+    assert lib.idx_score_packed_fp4(C.byref(p), None, None) == I.IDX_E_NULL

@@ -6,10 +6,13 @@
 // nb are always taken and the remaining topk - |forced| slots go to the
 // highest block scores, ties to the lower block id.  Selection is exact.
 //
-// One workgroup of NT threads per (row, head): 256 for rows of at most 2,048
-// blocks, else 512 (1,024 rows of 1,184 blocks: 7.5 against 9.4 us; 560 rows
-// of 4,096: 9.8 against 9.2 us).  Thread t owns the contiguous blocks
-// [t*C, t*C + C), C = ceil(max_blocks / NT) <= 8 or 16 (rounded up to
+// One workgroup of NT threads per (row, head): for rows of at most 2,048
+// blocks, 512 threads of up to 4 blocks when there are at most 512 rows (the
+// launch is then one row's latency, which more threads shorten: 256 rows of
+// 1,024 blocks 7.3 against 7.9 us), else 256 (1,024 rows of 1,184 blocks: 7.5
+// against 9.4 us with 512); wider rows 512 (560 rows of 4,096: 9.8 against
+// 9.2 us with 256).  Thread t owns the contiguous blocks
+// [t*C, t*C + C), C = ceil(max_blocks / NT) <= 4, 8 or 16 (rounded up to
 // a multiple of 4 when rows are 16-byte aligned), and loads their scores into
 // registers first thing; the row's slot and length are fetched before them and
 // the score loads do not wait for them.  Keys are 32-bit integers whose
@@ -47,6 +50,9 @@
 #ifndef IDX_TOPK_BALLOT_SCHED
 #define IDX_TOPK_BALLOT_SCHED 1  // one-wave kernel: slot and length loads issue before the score loads
 #endif
+#ifndef IDX_TOPK_WIDE_ROWS
+#define IDX_TOPK_WIDE_ROWS 512  // up to this many rows of <= 2,048 blocks: 512 threads of 4 blocks a row
+#endif                          // (256 rows of 1,024: 7.9 -> 7.3 us); more rows keep 256 threads of 8
 #ifndef IDX_TOPK_BALLOT_ROWS
 #define IDX_TOPK_BALLOT_ROWS 1024  // rows from which rows of <= 1,024 blocks take one wave each
 #endif
@@ -565,6 +571,8 @@ hipError_t launch_topk(const StepArgs& a, hipStream_t stream) {
   // rows of 12)
   if (a.max_blocks <= 16 * 64 && (grid >= IDX_TOPK_BALLOT_ROWS || a.max_blocks <= 64))
     launch_ballot<1>(a, grid, stream);
+  else if (a.max_blocks <= 4 * kTopkThreads && grid <= IDX_TOPK_WIDE_ROWS)
+    hipLaunchKernelGGL((topk_kernel<4, kTopkThreads>), dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, a);
   else if (a.max_blocks <= 8 * kTopkThreadsNarrow)
     hipLaunchKernelGGL((topk_kernel<8, kTopkThreadsNarrow>), dim3((unsigned)grid), dim3(kTopkThreadsNarrow), 0, stream,
                        a);

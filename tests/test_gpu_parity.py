@@ -243,9 +243,10 @@ def test_exact_tie_lower_id():
 def test_topk_synthetic_scores_exact(oracle, R):
     """Selection alone on the same fp32 scores (many exact ties, NaN, -0):
     ids and scores identical to the oracle's.  1,100 rows of at most 1,024
-    blocks take the one-wave-per-row kernel, 48 rows the workgroup kernel
-    (256 threads up to 2,048 blocks, 512 beyond, 16 blocks a thread past
-    4,096)."""
+    blocks take the one-wave-per-row kernel and 1,100 rows of 1,025 to 2,048
+    blocks the workgroup kernel with 256 threads; 48 rows the workgroup kernel
+    with 512 threads (4 blocks a thread up to 2,048 blocks, 8 up to 4,096, 16
+    beyond)."""
     rng = np.random.default_rng(9)
     for MB, topk, init, local in [(40, 8, 1, 2), (300, 64, 1, 2), (1000, 64, 0, 0), (8192, 64, 3, 5),
                                   (700, 1, 1, 0), (50, 50, 2, 2), (1024, 64, 1, 2), (2048, 64, 1, 2),

@@ -193,3 +193,46 @@ def test_workload_4_fused_store(oracle, mode):
     assert np.array_equal(w.k_scale.cpu().numpy(), scales), "scale bytes differ"
     a = dict(w.oracle_args(payload, scales), **m)
     Hn.assert_parity(g, oracle.step(**a), a)
+
+
+def test_fp4_step_graph_replays():
+    """idx_step_fp4 captured once in a HIP graph and replayed after new key
+    values are written into the captured staging buffer equals, on every
+    replay, the store then the step run eagerly on a copy of the pool."""
+    say("fp4 step graph replays")
+    w = W.make(name="fs_graph", R=5, P=4, H=4, k_format=W.K_NVFP4, req_len=[4000, 900, 15000, 60, 2100],
+               topk=8, init_blocks=1, local_blocks=2, seed=1260, pads=1, pad_len=800, device="cuda")
+    rows = new_key_rows(w)
+    setup_pool(w, rows)
+    st, sl = keys_of(w, rows)
+    outs = Hn.gpu_outputs(w)
+    p = Hn.gpu_params(w, outs)
+    nk = I.make_new_keys(st, sl)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        I.idx_step_fp4(p, nk)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        I.idx_step_fp4(p, nk)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1261)
+    for rep in range(4):
+        st.copy_(torch.randn(st.shape, generator=gen, device="cuda").to(torch.bfloat16) * (1 + rep))
+        k0, ks0 = w.k.clone(), w.k_scale.clone()
+        for v in outs.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {key: v.cpu().numpy() for key, v in outs.items()}
+        got["payload"], got["scales"] = w.k.cpu().numpy(), w.k_scale.cpu().numpy()
+        ref_outs = Hn.gpu_outputs(w)
+        I.idx_fp4_store(st, sl, k0, ks0)
+        I.idx_step(Hn.gpu_params(w, ref_outs, k=k0, k_scale=ks0))
+        torch.cuda.synchronize()
+        ref = {key: v.cpu().numpy() for key, v in ref_outs.items()}
+        ref["payload"], ref["scales"] = k0.cpu().numpy(), ks0.cpu().numpy()
+        assert_identical(ref, got, f"replay {rep}")
